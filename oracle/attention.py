@@ -1,0 +1,124 @@
+"""Ragged scaled-dot-product attention over a paged KV cache (TEST
+INFRASTRUCTURE).
+
+Definitions followed:
+
+* NumKong matrix-kernels page, "Attention with a Pre-Packed KV-Cache" and
+  ``attention_packed``: segments are addressed by cumulative offsets; queries
+  align to the end of their segment's keys, so row r of q query rows over k
+  keys sits at position r + k - q and sees keys from that position minus
+  ``keys_before`` through that position plus ``keys_after``; ``keys_after=0``
+  is causal; ``keys_before = w - 1`` is a window of w keys; rows that see no
+  key come back as zeros; the forward also fills a (tokens, heads)
+  log-sum-exp.
+* Algenta "Attention variant kernels", "A scalar reference, not a buffer
+  kernel": the score is q.k / sqrt(d) (here an explicit ``softmax_scale``
+  replaces 1/sqrt(d), as the aria_kernel ``attention_with_scale`` entry
+  allows), the causal mask admits key position <= query position, and the
+  softmax subtracts the row maximum before exponentiating.
+* Algenta, "Flash attention's running state ...":
+  ``grouped_query_attention_scale(32, 8) = 4`` -- each KV head serves
+  Hq / Hkv query heads.
+
+Readings taken where the pages leave a step open: query head h reads KV head
+floor(h / G) with G = Hq / Hkv; only the causal band (keys_after = 0) is
+computed; ``window_left`` = keys_before (-1 = unbounded); the log-sum-exp is
+the natural log of sum_j exp(scale * q.k_j); an empty row has lse = -inf.
+
+This is the plain definition: full score rows, one max, one exponent, one
+sum, one division -- no tiling, no online softmax, no split.
+"""
+
+import numpy as np
+
+
+def visible_range(row, q_len, kv_len, window_left):
+    """Inclusive key range [lo, hi] visible to query row ``row`` of a segment
+    with ``q_len`` query rows over ``kv_len`` keys (empty when lo > hi)."""
+    p = row + kv_len - q_len                    # end-aligned query position
+    hi = min(p, kv_len - 1)
+    lo = 0 if window_left < 0 else max(0, p - window_left)
+    return lo, hi
+
+
+def attend_rows(q_rows, K, V, row_ids, q_len, kv_len, softmax_scale, window_left):
+    """Attention for selected query rows of one segment and one KV head.
+
+    q_rows [n, D] float64, K/V [kv_len, D] float64, row_ids [n] local rows.
+    Returns out [n, D], lse [n].
+    """
+    n, d = q_rows.shape
+    out = np.zeros((n, d))
+    lse = np.full(n, -np.inf)
+    scores = softmax_scale * (q_rows @ K.T)     # [n, kv_len]
+    for r in range(n):
+        lo, hi = visible_range(int(row_ids[r]), q_len, kv_len, window_left)
+        if lo > hi:
+            continue
+        s = scores[r, lo:hi + 1]
+        m = np.max(s)
+        e = np.exp(s - m)
+        l = np.sum(e)
+        out[r] = (e @ V[lo:hi + 1]) / l
+        lse[r] = m + np.log(l)
+    return out, lse
+
+
+def ragged_paged_attention(q, q_offsets, kv_lens, cache, page_table, softmax_scale,
+                           window_left=-1, rows=None):
+    """Attention of every (or the selected) query row of a ragged batch.
+
+    q [T, Hq, D]: float64 values of the stored queries.  ``cache`` is an
+    ``oracle.paged.PagedCache``.  ``rows`` optionally restricts the
+    computation to a list of global token indices (outputs of other rows are
+    left zero / -inf).  Returns out [T, Hq, D] float64, lse [T, Hq] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    q_offsets = np.asarray(q_offsets, dtype=np.int64)
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    T, hq, d = q.shape
+    hkv = cache.num_kv_heads
+    if hq % hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = hq // hkv
+    out = np.zeros((T, hq, d))
+    lse = np.full((T, hq), -np.inf)
+    wanted = None if rows is None else np.zeros(T, dtype=bool)
+    if wanted is not None:
+        wanted[np.asarray(rows, dtype=np.int64)] = True
+    for s in range(len(kv_lens)):
+        a, b = int(q_offsets[s]), int(q_offsets[s + 1])
+        q_len, kv_len = b - a, int(kv_lens[s])
+        local = np.arange(q_len)
+        if wanted is not None:
+            local = local[wanted[a:b]]
+        if q_len == 0 or local.size == 0:
+            continue
+        K, V = cache.gather(page_table, s, kv_len)
+        for h in range(hq):
+            g = h // group
+            o, l = attend_rows(q[a + local, h, :], K[:, g, :], V[:, g, :], local,
+                               q_len, kv_len, softmax_scale, window_left)
+            out[a + local, h, :] = o
+            lse[a + local, h] = l
+    return out, lse
+
+
+def dense_attention(q, k, v, softmax_scale, window_left=-1):
+    """Single-segment attention on contiguous arrays (no pages).
+
+    q [n_q, Hq, D], k/v [n_kv, Hkv, D] float64; end-aligned causal band.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_q, hq, d = q.shape
+    n_kv, hkv, _ = k.shape
+    group = hq // hkv
+    out = np.zeros((n_q, hq, d))
+    lse = np.full((n_q, hq), -np.inf)
+    for h in range(hq):
+        g = h // group
+        o, l = attend_rows(q[:, h, :], k[:, g, :], v[:, g, :], np.arange(n_q),
+                           n_q, n_kv, softmax_scale, window_left)
+        out[:, h, :] = o
+        lse[:, h] = l
+    return out, lse

@@ -1,0 +1,127 @@
+"""The paged KV cache of ``include/nk.h``, addressed element by element
+(TEST INFRASTRUCTURE).
+
+Layout (one layer):
+
+* K pages  ``[num_pages][num_kv_heads][page_size][head_dim]``
+* V pages  ``[num_pages][num_kv_heads][head_dim][page_size]`` -- within a page,
+  for one head, values are stored dimension-major (the page's tokens are
+  contiguous for each dimension).
+* fp8 scales (K and V separately) ``[num_pages][num_kv_heads][page_size]``.
+* ``page_table[s][p]`` is the physical page holding logical slots
+  ``p*page_size .. p*page_size + page_size - 1`` of sequence ``s``.
+
+The pages define a cache whose pages a caller packs once and reads many times
+(NumKong matrix-kernels page, "Attention with a Pre-Packed KV-Cache"), updated
+in place by the fused RoPE step (Mojo page,
+``generic_fused_qk_rope_bshd_paged_ragged_kernel_api``, ``kv_collection``).
+The physical layout is not fixed by the pages; the one above is this
+library's.
+
+The oracle keeps the cache as float64 *stored values*: for ``f32`` and
+``bf16`` the element values, for ``e4m3`` the values of the codes (unscaled)
+plus the per-slot scales.  ``from_storage`` / ``to_storage`` convert to and
+from raw bytes.
+"""
+
+import numpy as np
+
+from . import formats
+
+DTYPES = ("f32", "bf16", "e4m3")
+
+
+class PagedCache:
+    def __init__(self, dtype, num_pages, num_kv_heads, page_size, head_dim):
+        if dtype not in DTYPES:
+            raise ValueError(dtype)
+        self.dtype = dtype
+        self.num_pages = num_pages
+        self.num_kv_heads = num_kv_heads
+        self.page_size = page_size
+        self.head_dim = head_dim
+        self.k = np.full((num_pages, num_kv_heads, page_size, head_dim), np.nan)
+        self.v = np.full((num_pages, num_kv_heads, head_dim, page_size), np.nan)
+        if dtype == "e4m3":
+            self.k_scale = np.full((num_pages, num_kv_heads, page_size), np.nan)
+            self.v_scale = np.full((num_pages, num_kv_heads, page_size), np.nan)
+        else:
+            self.k_scale = self.v_scale = None
+
+    def copy(self):
+        c = PagedCache(self.dtype, self.num_pages, self.num_kv_heads,
+                       self.page_size, self.head_dim)
+        c.k, c.v = self.k.copy(), self.v.copy()
+        if self.k_scale is not None:
+            c.k_scale, c.v_scale = self.k_scale.copy(), self.v_scale.copy()
+        return c
+
+    # -- raw storage <-> stored values ------------------------------------
+    @classmethod
+    def from_storage(cls, dtype, k_pages, v_pages, k_scales=None, v_scales=None):
+        """Build from raw arrays: float32 (f32), uint16 bit patterns (bf16)
+        or uint8 codes (e4m3), shaped as the layout above."""
+        n, h, p, d = k_pages.shape
+        c = cls(dtype, n, h, p, d)
+        if v_pages.shape != (n, h, d, p):
+            raise ValueError("V pages must be [num_pages][heads][head_dim][page_size]")
+        c.k = _decode(dtype, k_pages)
+        c.v = _decode(dtype, v_pages)
+        if dtype == "e4m3":
+            c.k_scale = np.asarray(k_scales, dtype=np.float32).astype(np.float64)
+            c.v_scale = np.asarray(v_scales, dtype=np.float32).astype(np.float64)
+        return c
+
+    def to_storage(self):
+        """Raw arrays (k_pages, v_pages, k_scales, v_scales); unwritten slots
+        (NaN) become the dtype's NaN pattern, scales NaN."""
+        k = _encode(self.dtype, self.k)
+        v = _encode(self.dtype, self.v)
+        if self.dtype == "e4m3":
+            return k, v, self.k_scale.astype(np.float32), self.v_scale.astype(np.float32)
+        return k, v, None, None
+
+    # -- logical slot access -------------------------------------------------
+    def locate(self, page_table, seq, slot):
+        """Logical slot of a sequence -> (physical page, offset in page)."""
+        page = int(page_table[seq][slot // self.page_size])
+        return page, slot % self.page_size
+
+    def store(self, page_table, seq, slot, head, k_vals, v_vals, k_scale=None, v_scale=None):
+        """Store one (token, kv head) row of stored values into its slot."""
+        page, off = self.locate(page_table, seq, slot)
+        self.k[page, head, off, :] = k_vals
+        self.v[page, head, :, off] = v_vals
+        if self.dtype == "e4m3":
+            self.k_scale[page, head, off] = k_scale
+            self.v_scale[page, head, off] = v_scale
+
+    def gather(self, page_table, seq, length):
+        """Dequantised K and V of slots 0..length-1 of a sequence, as float64
+        arrays [length, num_kv_heads, head_dim]."""
+        slots = np.arange(length)
+        pages = np.asarray(page_table[seq])[slots // self.page_size].astype(np.int64)
+        offs = slots % self.page_size
+        K = self.k[pages, :, offs, :]            # [length, heads, head_dim]
+        V = self.v[pages, :, :, offs]            # [length, heads, head_dim]
+        if self.dtype == "e4m3":
+            K = K * self.k_scale[pages, :, offs][:, :, None]
+            V = V * self.v_scale[pages, :, offs][:, :, None]
+        return K, V
+
+
+def _decode(dtype, raw):
+    raw = np.asarray(raw)
+    if dtype == "f32":
+        return raw.astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return formats.bf16_value(raw.view(np.uint16) if raw.dtype != np.uint16 else raw)
+    return formats.e4m3_value(raw.view(np.uint8) if raw.dtype != np.uint8 else raw)
+
+
+def _encode(dtype, vals):
+    if dtype == "f32":
+        return vals.astype(np.float32)
+    if dtype == "bf16":
+        return formats.bf16_bits(vals)
+    return formats.e4m3_code(vals)
