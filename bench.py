@@ -1,0 +1,317 @@
+"""Benchmark: one step = the whole hot path (fused RoPE + KV append, then
+ragged paged attention with its split-KV merge) over one batch of synthetic
+input, inputs resident in HBM.
+
+Headline (the JSON line's `value`): decode KV GB/s on the batched-decode
+workload (32 sequences, KV lengths 512..4096, 32 query / 8 KV heads, D 128,
+bf16, 16-token pages).  The same line carries the prefill TFLOP/s of the
+ragged causal prefill workload (8192 tokens, bf16), the float8 long-context
+decode and the sliding-window mixed batch, each with its dominant kernel's
+roofline fraction, and the float64 oracle timed on the host as a CPU
+baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode_bf16,...]
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+
+Timing: W untimed warm-up steps, then K timed steps, the whole loop
+bracketed by torch.cuda.synchronize().  Before every step a 1 GiB buffer is
+overwritten (outside the step's events) so that the 256 MB Infinity Cache
+holds none of the step's inputs; each step is timed with HIP events on the
+step's stream and ms_per_step is the median.  Per-kernel durations come from
+the library's own event pairs around each launch (nk_profile_*).
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+FLUSH_BYTES = 1 << 30
+
+METRIC = "decode KV GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)"
+DESCR = {
+    "decode_bf16": "batched decode, bf16: 32 seqs x 1 token, KV 512-4096, Hq32/Hkv8, D128, page16 permuted",
+    "prefill_bf16": "ragged causal prefill, bf16: 8 segments 128..2176, 8192 tokens, Hq32/Hkv8, D128, page16",
+    "decode_fp8": "long-context decode, e4m3 KV + f32 scales: 128 seqs, KV 4096-32768 log-uniform, Hq64/Hkv8, D128, split 512",
+    "mixed_window_bf16": "sliding-window mixed batch, bf16: 4 prefill 1024-4096 + 60 decode 2048-8192, Hq16/Hkv8, D256, window 1024",
+    "tiny_prefill_f32": "tiny ragged prefill, fp32: segments 5 and 12, Hq4/Hkv2, D64",
+}
+KERNEL_SOURCES = ["attn_decode.hip", "attn_prefill.hip", "rope_write.hip", "lse_merge.hip", "common.h"]
+
+
+def source_hash(files=KERNEL_SOURCES):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "ragged_paged_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ GPU part
+def run_workload(name, steps, warmup, flush):
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import work
+    from ragged_paged_kv_amd import nk
+
+    w = synth.make(name)
+    t0 = time.time()
+    raw = synth.build_cache(w)
+    nt = synth.new_tokens(w)
+    dev = "cuda"
+
+    def t(x, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    if w.in_dtype == "bf16":
+        q, k, v = (t(nt[n].view(np.int16), torch.bfloat16) for n in ("q", "k", "v"))
+    else:
+        q, k, v = (t(nt[n]) for n in ("q", "k", "v"))
+    if w.cache_dtype == "bf16":
+        kp, vp = t(raw["k_pages"].view(np.int16), torch.bfloat16), t(raw["v_pages"].view(np.int16), torch.bfloat16)
+    else:
+        kp, vp = t(raw["k_pages"]), t(raw["v_pages"])
+    ks = None if raw["k_scales"] is None else t(raw["k_scales"])
+    vs = None if raw["v_scales"] is None else t(raw["v_scales"])
+    del raw
+    cache = nk.PagedKVCache(kp, vp, t(w.page_table.astype(np.int32)), ks, vs)
+    q_offsets, kv_lens = t(w.q_offsets.astype(np.int32)), t(w.kv_lens.astype(np.int32))
+    pos = None if w.position_ids is None else t(w.position_ids.astype(np.int32))
+    freqs = t(synth.freqs_table(w))
+    q_out = torch.empty_like(q)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.total_q, w.num_q_heads, dtype=torch.float32, device=dev)
+    ws_bytes = nk.workspace_size(q.dtype, cache, w.num_seqs, w.total_q, w.max_q_len, w.max_kv_len,
+                                 w.num_q_heads, w.window_left, w.split_tokens)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    split = nk.split_tokens(cache, w.num_seqs, w.max_kv_len, w.num_q_heads, w.window_left, w.split_tokens)
+    log(f"{name}: inputs ready in {time.time() - t0:.1f}s (cache {kp.numel() * kp.element_size() / 1e9:.2f} GB, "
+        f"split {split}, workspace {ws_bytes / 1e6:.1f} MB)")
+
+    def step():
+        nk.rope_qk_write_paged(q, k, v, q_offsets, kv_lens, freqs, cache, w.rotary_dim, w.rope_layout,
+                               position_ids=pos, q_out=q_out)
+        nk.ragged_paged_attention(q_out, q_offsets, kv_lens, cache, w.softmax_scale, w.max_q_len, w.max_kv_len,
+                                  w.window_left, out=out, lse=lse, kv_split_tokens=w.split_tokens, workspace=ws)
+
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    nk.profile_reset()
+    nk.profile_enable(True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        if scratch is not None:
+            scratch.fill_(float(i))
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    nk.profile_enable(False)
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    ms = times[len(times) // 2]
+    kern = {}
+    for fam in ("rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge"):
+        tot, n = nk.profile_read(fam)
+        if n:
+            kern[fam] = {"avg_ms": tot / n, "launches": n}
+    res = {
+        "workload": name, "descr": DESCR[name], "ms_per_step": ms, "ms_min": times[0], "ms_max": times[-1],
+        "wall_s_incl_flush": wall, "kernels": kern, "split_tokens": split,
+        "decode_bytes": work.decode_bytes(w), "prefill_flops": work.prefill_flops(w), "rope_bytes": work.rope_bytes(w),
+    }
+    if res["decode_bytes"]:
+        res["decode_GBps_step"] = res["decode_bytes"] / ms / 1e6
+        if "attn_decode" in kern:
+            res["decode_GBps_kernel"] = res["decode_bytes"] / kern["attn_decode"]["avg_ms"] / 1e6
+    if res["prefill_flops"]:
+        res["prefill_TFLOPs_step"] = res["prefill_flops"] / ms / 1e9
+        if "attn_prefill" in kern:
+            res["prefill_TFLOPs_kernel"] = res["prefill_flops"] / kern["attn_prefill"]["avg_ms"] / 1e9
+    if "rope_write" in kern:
+        res["rope_GBps_kernel"] = res["rope_bytes"] / kern["rope_write"]["avg_ms"] / 1e6
+    del cache, kp, vp, ks, vs, scratch, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(name):
+    """The oracle as it stands, on the host: RoPE + append + attention over
+    the whole workload (decode) or over its five shortest segments (prefill)."""
+    import numpy as np
+    import threadpoolctl
+
+    import synth
+    from synth import work
+    from tests import gpu_util as gu
+
+    w = synth.make(name)
+    sample = "whole batch"
+    if name == "prefill_bf16":
+        w = w.subset(np.arange(5))
+        sample = "segments 128..1024 (2688 of 8192 tokens)"
+    raw = synth.build_cache(w)
+    t0 = time.perf_counter()
+    gu.oracle_run(w, raw)
+    dt = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    if name == "prefill_bf16":
+        return {"value": work.prefill_flops(w) / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": sample, "seconds": dt}
+    return {"value": work.decode_bytes(w) / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": dt}
+
+
+# ------------------------------------------------------------------ counters
+def load_traffic(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _pmc_rows(d):
+    import csv
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
+        with open(p) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, kernel_match, key):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the kernel, scaled
+    by the same counters on a plain copy of known size; writes
+    profiles/traffic_<key>.json and prints the summary."""
+    def avg(rows, match, counter):
+        vals = [float(r.get("Counter_Value", r.get("counter_value", 0))) for r in rows
+                if match in r.get("Kernel_Name", r.get("kernel_name", "")) and
+                r.get("Counter_Name", r.get("counter_name", "")) == counter]
+        return sum(vals) / len(vals) if vals else None
+    kf = avg(_pmc_rows(fetch_dir), kernel_match, "FETCH_SIZE")
+    kw = avg(_pmc_rows(write_dir), kernel_match, "WRITE_SIZE")
+    cf = avg(_pmc_rows(copy_fetch_dir), "copy", "FETCH_SIZE") or avg(_pmc_rows(copy_fetch_dir), "elementwise", "FETCH_SIZE")
+    cw = avg(_pmc_rows(copy_write_dir), "copy", "WRITE_SIZE") or avg(_pmc_rows(copy_write_dir), "elementwise", "WRITE_SIZE")
+    fs = copy_bytes / (cf * 1024.0) if cf else None
+    wsf = copy_bytes / (cw * 1024.0) if cw else None
+    rec = {"kernel": kernel_match, "fetch_kib": kf, "write_kib": kw, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "copy_bytes": copy_bytes, "fetch_scale": fs, "write_scale": wsf,
+           "bytes_per_launch": (kf * 1024 * fs + kw * 1024 * wsf) if None not in (kf, kw, fs, wsf) else None,
+           "source_hash": source_hash()}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="decode_bf16,prefill_bf16,decode_fp8,mixed_window_bf16")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--pmc-kernel", default="attn_decode_kernel")
+    ap.add_argument("--pmc-key", default="decode_bf16")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--copy-only", action="store_true", help="run one plain 1 GiB copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, args.copy_bytes, args.pmc_kernel, args.pmc_key)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(each GPU would run the same kernels on its own share of sequences or KV heads).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    assert torch.cuda.is_available(), "no GPU"
+    if args.copy_only:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        return 0
+
+    names = [n for n in args.only.split(",") if n]
+    results = {}
+    for n in names:
+        log(f"running {n}")
+        results[n] = run_workload(n, args.steps, args.warmup, not args.no_flush)
+        log(json.dumps(results[n]))
+
+    head = results.get("decode_bf16") or next(iter(results.values()))
+    cpu = None
+    if not args.no_cpu and head["workload"] in ("decode_bf16", "prefill_bf16"):
+        log("timing the oracle on the host")
+        cpu = cpu_baseline(head["workload"])
+        log(json.dumps(cpu))
+
+    dec_k = head.get("kernels", {}).get("attn_decode")
+    roof = None
+    if dec_k:
+        achieved = head["decode_bytes"] / dec_k["avg_ms"] / 1e6
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic("decode_bf16"),
+                "kernel": "attn_decode_kernel<128,16,bf16>", "avg_kernel_ms": dec_k["avg_ms"],
+                "bytes_per_launch": head["decode_bytes"]}
+    value = head.get("decode_GBps_step", 0.0)
+    line = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": head["workload"] + ": " + head["descr"], "global_batch": 32, "seq_len": "512-4096 KV",
+                   "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    extra = {}
+    for n, r in results.items():
+        e = {"ms_per_step": r["ms_per_step"], "kernels": r["kernels"], "split_tokens": r["split_tokens"]}
+        if r.get("decode_GBps_kernel"):
+            e["decode_GBps_kernel"] = r["decode_GBps_kernel"]
+            e["decode_hbm_frac"] = r["decode_GBps_kernel"] / HBM_PEAK_GBS
+        if r.get("prefill_TFLOPs_kernel"):
+            e["prefill_TFLOPs_kernel"] = r["prefill_TFLOPs_kernel"]
+            e["prefill_mfma_frac"] = r["prefill_TFLOPs_kernel"] / BF16_PEAK_TFLOPS
+        if r.get("rope_GBps_kernel"):
+            e["rope_GBps_kernel"] = r["rope_GBps_kernel"]
+        extra[n] = e
+    line["workloads"] = extra
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,234 @@
+/*
+ * nk.h -- ragged paged attention with fused RoPE + KV append, for AMD
+ * Instinct MI355X (gfx950).  C ABI of libnk.so.
+ *
+ * Three operations:
+ *
+ *   nk_rope_qk_write_paged     rotate Q and K with a (cos, sin) table, write
+ *                              the rotated Q out and append rotated K and
+ *                              plain V to a paged cache (Mojo docs,
+ *                              generic_fused_qk_rope_bshd_paged_ragged_kernel_api,
+ *                              "Args"; NumKong for Python, matrix-kernels page,
+ *                              attention_rope);
+ *   nk_ragged_paged_attention  ragged causal (optionally windowed) grouped-query
+ *                              scaled-dot-product attention over that cache,
+ *                              with a per-row log-sum-exp (NumKong matrix-kernels
+ *                              page, "Attention with a Pre-Packed KV-Cache" and
+ *                              attention_packed);
+ *   nk_attention_lse_merge     merge of partial attention states by their
+ *                              log-sum-exp (Algenta "Attention variant kernels",
+ *                              "Flash attention's running state reproduces the
+ *                              same softmax").
+ *
+ * Conventions for every call (after the NumKong python page, "GPU Tensors
+ * through DLPack": no verb allocates, each GPU call queues its launches on
+ * the given stream and returns before they finish):
+ *
+ *   - Pointers are DEVICE pointers unless the parameter is named *_host or
+ *     is the cache descriptor itself (a host struct holding device pointers).
+ *     Integer arrays are int32.
+ *   - The caller owns every buffer, the workspace and the cache.  The library
+ *     never allocates device memory, keeps no state between calls (apart from
+ *     the optional profiling events below) and may be called from several
+ *     host threads at once.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work; they never synchronise.
+ *   - Errors are returned as nk_status_t values, detected on the host before
+ *     anything is launched.  There is no CPU fallback: an unsupported
+ *     combination returns NK_ERR_UNSUPPORTED.  A failed launch returns
+ *     NK_ERR_DEVICE.  Contents of device arrays are preconditions, not
+ *     checked (see each call).
+ *
+ * Paged cache layout (one layer), nk_paged_kv_t:
+ *
+ *   K pages   [num_pages][num_kv_heads][page_size][head_dim]
+ *   V pages   [num_pages][num_kv_heads][head_dim][page_size]
+ *             (within one page and head, V is stored dimension-major: the
+ *             page's tokens are contiguous for each dimension)
+ *   scales    [num_pages][num_kv_heads][page_size] float32, K and V apart,
+ *             only for NK_E4M3 caches: the stored code times its scale is the
+ *             value
+ *   page_table[s][p] (device, [num_seqs][page_table_stride]) is the physical
+ *             page of logical slots p*page_size .. p*page_size+page_size-1 of
+ *             sequence s.
+ *
+ * Supported: head_dim 64, 128 or 256; page_size 16 or 32; query heads a
+ * multiple of KV heads.  Element types: f32 inputs with an f32 cache; bf16
+ * inputs with a bf16 or e4m3 (OCP e4m3fn: bias 7, max 448, no Inf) cache.
+ */
+#ifndef NK_H_
+#define NK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { NK_F32 = 0, NK_BF16 = 1, NK_E4M3 = 2 } nk_dtype_t;
+
+/* NK_ROPE_HALF pairs dim i with dim i + rotary_dim/2 (rotate-half);
+ * NK_ROPE_INTERLEAVED pairs dims 2i and 2i+1 (Mojo `interleaved`;
+ * aria_kernel `rope` / `rope_half`). */
+typedef enum { NK_ROPE_HALF = 0, NK_ROPE_INTERLEAVED = 1 } nk_rope_layout_t;
+
+typedef enum {
+  NK_OK = 0,
+  NK_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shape */
+  NK_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim, page size, dtypes */
+  NK_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  NK_ERR_DEVICE = 4         /* a HIP launch or query failed */
+} nk_status_t;
+
+typedef struct nk_paged_kv {
+  void *k_pages;               /* see layout above, element type `dtype` */
+  void *v_pages;
+  float *k_scales;             /* NK_E4M3 only, else NULL */
+  float *v_scales;
+  int32_t dtype;               /* nk_dtype_t of the stored elements */
+  int32_t num_pages;
+  int32_t page_size;           /* 16 or 32 */
+  int32_t num_kv_heads;
+  int32_t head_dim;            /* 64, 128 or 256 */
+  const int32_t *page_table;   /* [num_seqs][page_table_stride] */
+  int32_t page_table_stride;
+} nk_paged_kv_t;
+
+/*
+ * nk_rope_qk_write_paged -- fused RoPE on Q and K plus append of K/V.
+ *
+ * Defined by the Mojo docs page generic_fused_qk_rope_bshd_paged_ragged_
+ * kernel_api ("Applies fused rotary position embedding to Q and K, updating
+ * keys in the paged KV cache"; Args input_row_offsets, freqs_cis,
+ * position_ids, output; parameter `interleaved`), extended to append V.
+ *
+ * For token t = q_offsets[s] + i (i < q_len(s) = q_offsets[s+1]-q_offsets[s]):
+ *   slot  j   = kv_lens[s] - q_len(s) + i      (kv_lens counts keys AFTER
+ *                                               this append)
+ *   pos       = position_ids ? position_ids[t] : j
+ *   each Q head and K head: the pairs of the first rotary_dim dims rotate by
+ *   (c, s) = (freqs[pos][p][0], freqs[pos][p][1]):  x' = x c - y s,
+ *   y' = x s + y c; dims >= rotary_dim are copied.  V is not rotated.
+ *   q_out[t] = rotated Q (input dtype; may alias q).
+ *   K and V rows go to page page_table[s][j / page_size], offset
+ *   j % page_size, of every KV head.  For an NK_E4M3 cache each (token, kv
+ *   head) row gets scale = absmax/448 and codes e4m3(x / scale), rounded to
+ *   nearest even (an all-zero row stores scale 0 and zero codes).
+ *
+ * q      [total_tokens][num_q_heads][head_dim]   in_dtype (NK_F32 / NK_BF16)
+ * k, v   [total_tokens][num_kv_heads][head_dim]  in_dtype
+ * q_out  [total_tokens][num_q_heads][head_dim]   in_dtype
+ * q_offsets [num_seqs+1], kv_lens [num_seqs], position_ids [total_tokens] or NULL
+ * freqs  [max_pos][rotary_dim/2][2] float32 (cos, sin)
+ * rotary_dim: multiple of 16, 16 <= rotary_dim <= head_dim.
+ * Preconditions (not checked): q_offsets non-decreasing with
+ * q_offsets[num_seqs] == total_tokens, q_len(s) <= kv_lens[s], the page
+ * table covers ceil(kv_lens[s]/page_size) pages, 0 <= pos < max_pos.
+ * Slots outside the appended ones are not touched.
+ */
+int nk_rope_qk_write_paged(const void *q, const void *k, const void *v, int32_t in_dtype,
+                           void *q_out, const int32_t *q_offsets, const int32_t *kv_lens,
+                           const int32_t *position_ids, const float *freqs, int32_t max_pos,
+                           int32_t rotary_dim, int32_t layout, int32_t num_seqs,
+                           int32_t total_tokens, int32_t num_q_heads,
+                           const nk_paged_kv_t *cache, void *stream);
+
+/*
+ * nk_ragged_paged_attention -- causal (optionally windowed) GQA attention.
+ *
+ * NumKong matrix-kernels page, attention_packed: query row i of a segment
+ * with q_len rows over kv_len keys sits at position p = i + kv_len - q_len
+ * and sees keys lo..hi with hi = min(p, kv_len-1), lo = 0 if window_left < 0
+ * else max(0, p - window_left) (window_left = w - 1 for a window of w keys);
+ * rows that see no key return zeros and lse = -inf.  Query head h reads KV
+ * head h / (num_q_heads / num_kv_heads).  With scores
+ * s_j = softmax_scale * <q, K_j> (e4m3: K_j = code * scale):
+ *   out[t][h] = sum_j exp(s_j - m) V_j / sum_j exp(s_j - m),  m = max_j s_j
+ *   lse[t][h] = m + ln(sum_j exp(s_j - m))          (natural log, float32)
+ *
+ * q    [total_q][num_q_heads][head_dim] q_dtype; out the same, q_dtype.
+ * lse  [total_q][num_q_heads] float32, or NULL.
+ * q_offsets [num_seqs+1], kv_lens [num_seqs] (device).
+ * max_q_len / max_kv_len: host upper bounds of q_len(s) / kv_lens[s]; they
+ *   size the launch grids (rows beyond them are not computed).
+ * kv_split_tokens: keys per split-KV chunk of a single-token (decode) row,
+ *   a multiple of 32; 0 lets the library choose.  Rows of longer segments
+ *   (prefill) are not split.
+ * workspace: device scratch of at least nk_ragged_paged_attention_workspace_
+ *   size(...) bytes with the same scalars (may be NULL when that is 0);
+ *   contents need no initialisation and are garbage afterwards.
+ * Supported: q_dtype NK_F32 with an NK_F32 cache, NK_BF16 with an NK_BF16
+ *   or NK_E4M3 cache.
+ */
+int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_offsets,
+                              const int32_t *kv_lens, const nk_paged_kv_t *cache,
+                              float softmax_scale, int32_t window_left, void *out, float *lse,
+                              int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                              int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace nk_ragged_paged_attention needs for these scalars
+ * (0 if none).  Pure host computation. */
+size_t nk_ragged_paged_attention_workspace_size(int32_t q_dtype, int32_t cache_dtype,
+                                                int32_t num_seqs, int32_t total_q,
+                                                int32_t max_q_len, int32_t max_kv_len,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t window_left,
+                                                int32_t kv_split_tokens);
+
+/* The keys per split-KV chunk nk_ragged_paged_attention uses for these
+ * scalars (resolves kv_split_tokens = 0).  Pure host computation. */
+int32_t nk_ragged_paged_attention_split_tokens(int32_t num_seqs, int32_t max_kv_len,
+                                               int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t window_left,
+                                               int32_t kv_split_tokens);
+
+/*
+ * nk_attention_lse_merge -- merge partial attention states.
+ *
+ * Algenta "Attention variant kernels", "Flash attention's running state
+ * reproduces the same softmax" (running max, rescale by exp(old - new),
+ * final divide), applied to whole chunks: for row r and head h, with
+ * partials i in merge_offsets[r] .. merge_offsets[r+1]-1,
+ *   M = max_i lse_i, w_i = exp(lse_i - M),
+ *   out[r][h] = sum_i w_i partial_out[i][h] / sum_i w_i,
+ *   lse_out[r][h] = M + ln(sum_i w_i);
+ * a row whose partials are all -inf (or that has none) gets zeros and -inf.
+ *
+ * partial_out [n_part][num_heads][head_dim] float32 (normalised chunk outputs)
+ * partial_lse [n_part][num_heads] float32, natural log, -inf = empty chunk
+ * merge_offsets [num_rows+1] (device, non-decreasing)
+ * out [num_rows][num_heads][head_dim] in out_dtype (NK_F32 or NK_BF16)
+ * lse_out [num_rows][num_heads] float32 or NULL
+ * head_dim: any multiple of 2 up to 512.
+ */
+int nk_attention_lse_merge(const float *partial_out, const float *partial_lse,
+                           const int32_t *merge_offsets, int32_t num_rows, int32_t num_heads,
+                           int32_t head_dim, void *out, int32_t out_dtype, float *lse_out,
+                           void *stream);
+
+/* Static description of a status code. */
+const char *nk_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int nk_version(void);
+
+/*
+ * Kernel timing (diagnostics).  When enabled, every launch the entry points
+ * make is bracketed by two HIP events recorded on the call's stream, kept per
+ * kernel family ("rope_write", "attn_decode", "attn_prefill", "attn_f32",
+ * "lse_merge").  nk_profile_read waits for the recorded events and returns
+ * the summed milliseconds and the launch count of one family since the last
+ * reset.  Events are created on first use and reused; this is the only state
+ * the library keeps.  Not for concurrent use from several threads.
+ */
+int nk_profile_enable(int enable);
+int nk_profile_reset(void);
+int nk_profile_read(const char *kernel, double *total_ms_host, int64_t *launches_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NK_H_ */

@@ -1,0 +1,297 @@
+// C ABI of libnk.so: argument validation, launch planning, dispatch.
+//
+// Every check here is a host-side check of scalars and pointer nullness, made
+// before anything is launched; device-array contents are preconditions
+// (include/nk.h).  Planning uses host scalars only: the split-KV chunk size,
+// the grid bounds and the workspace carve-up.  Which rows are single-token
+// decode rows and which are prefill rows is decided inside the kernels from
+// the device offsets, so a call never reads device memory on the host and
+// never synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "internal.h"
+
+using namespace nk;
+
+namespace {
+
+constexpr int kVersion = 10000;   // 1.0.0
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool page_size_ok(int p) { return p == 16 || p == 32; }
+
+int check_cache(const nk_paged_kv_t *c) {
+  if (!c || !c->k_pages || !c->v_pages || !c->page_table) return NK_ERR_INVALID_ARG;
+  if (c->num_pages < 0 || c->num_kv_heads <= 0 || c->page_table_stride < 0) return NK_ERR_INVALID_ARG;
+  if (c->dtype != NK_F32 && c->dtype != NK_BF16 && c->dtype != NK_E4M3) return NK_ERR_UNSUPPORTED;
+  if (c->dtype == NK_E4M3 && (!c->k_scales || !c->v_scales)) return NK_ERR_INVALID_ARG;
+  if (!head_dim_ok(c->head_dim) || !page_size_ok(c->page_size)) return NK_ERR_UNSUPPORTED;
+  return NK_OK;
+}
+
+// Keys per split-KV chunk of a decode row.
+int split_tokens(int num_seqs, int max_kv_len, int hq, int hkv, int head_dim, int window_left,
+                 int requested) {
+  if (requested > 0) return requested;
+  int span = window_left < 0 ? max_kv_len : std::min(max_kv_len, window_left + 32);
+  if (span <= 0) return 512;
+  // aim for about 4 chunk work-groups per CU over the batch, in 256..2048-key
+  // chunks (a multiple of 32 keys)
+  const long long target = 4LL * 256;
+  long long per_row = (target + (long long)num_seqs * hkv - 1) / std::max(1LL, (long long)num_seqs * hkv);
+  long long s = (span + per_row - 1) / std::max(1LL, per_row);
+  s = std::max(256LL, std::min(2048LL, s));
+  s = (s + 31) / 32 * 32;
+  (void)hq;
+  (void)head_dim;
+  return (int)s;
+}
+
+int max_chunks(int max_kv_len, int window_left, int split) {
+  long long span = window_left < 0 ? max_kv_len : std::min<long long>(max_kv_len, (long long)window_left + 32);
+  if (span <= 0) return 1;
+  return (int)((span + split - 1) / split);
+}
+
+bool uses_split(int q_dtype, int cache_dtype) { return q_dtype == NK_BF16 && cache_dtype != NK_F32; }
+
+size_t workspace_bytes(int q_dtype, int cache_dtype, int num_seqs, int max_kv_len, int hq, int hkv,
+                       int head_dim, int window_left, int requested_split, int *split_out,
+                       int *chunks_out) {
+  const int split = split_tokens(num_seqs, max_kv_len, hq, hkv, head_dim, window_left, requested_split);
+  const int chunks = max_chunks(max_kv_len, window_left, split);
+  if (split_out) *split_out = split;
+  if (chunks_out) *chunks_out = chunks;
+  if (!uses_split(q_dtype, cache_dtype) || chunks <= 1) return 0;
+  const size_t slots = (size_t)num_seqs * chunks;
+  size_t bytes = slots * hq * head_dim * sizeof(float);       // partial outputs
+  bytes = (bytes + 255) / 256 * 256;
+  bytes += slots * hq * sizeof(float);                           // partial lse
+  return (bytes + 255) / 256 * 256;
+}
+
+// ------------------------------------------------------------------ profiling
+struct ProfileState {
+  std::mutex mu;
+  bool enabled = false;
+  struct Rec { const char *family; hipEvent_t a, b; bool pending; };
+  std::vector<Rec> recs;
+  std::vector<std::pair<std::string, std::pair<double, int64_t>>> totals;
+};
+ProfileState &prof() {
+  static ProfileState p;
+  return p;
+}
+
+void flush_pending(ProfileState &p) {
+  for (auto &r : p.recs) {
+    if (!r.pending) continue;
+    hipEventSynchronize(r.b);
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, r.a, r.b);
+    bool found = false;
+    for (auto &t : p.totals)
+      if (t.first == r.family) { t.second.first += ms; t.second.second += 1; found = true; }
+    if (!found) p.totals.push_back({r.family, {ms, 1}});
+    r.pending = false;
+  }
+}
+
+}  // namespace
+
+namespace nk {
+
+ProfileScope::ProfileScope(const char *family, hipStream_t s) : slot(-1), stream(s) {
+  ProfileState &p = prof();
+  if (!p.enabled) return;
+  std::lock_guard<std::mutex> lock(p.mu);
+  int idx = -1;
+  for (size_t i = 0; i < p.recs.size(); ++i)
+    if (!p.recs[i].pending) { idx = (int)i; break; }
+  if (idx < 0) {
+    if (p.recs.size() >= 4096) flush_pending(p), idx = 0;
+    else {
+      ProfileState::Rec r{family, nullptr, nullptr, false};
+      if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
+      p.recs.push_back(r);
+      idx = (int)p.recs.size() - 1;
+    }
+  }
+  p.recs[idx].family = family;
+  p.recs[idx].pending = true;
+  hipEventRecord(p.recs[idx].a, stream);
+  slot = idx;
+}
+
+ProfileScope::~ProfileScope() {
+  if (slot < 0) return;
+  ProfileState &p = prof();
+  std::lock_guard<std::mutex> lock(p.mu);
+  hipEventRecord(p.recs[slot].b, stream);
+}
+
+}  // namespace nk
+
+extern "C" {
+
+const char *nk_status_string(int status) {
+  switch (status) {
+    case NK_OK: return "ok";
+    case NK_ERR_INVALID_ARG: return "invalid argument";
+    case NK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NK_ERR_WORKSPACE: return "workspace missing or too small";
+    case NK_ERR_DEVICE: return "device launch failed";
+    default: return "unknown status";
+  }
+}
+
+int nk_version(void) { return kVersion; }
+
+int nk_rope_qk_write_paged(const void *q, const void *k, const void *v, int32_t in_dtype,
+                           void *q_out, const int32_t *q_offsets, const int32_t *kv_lens,
+                           const int32_t *position_ids, const float *freqs, int32_t max_pos,
+                           int32_t rotary_dim, int32_t layout, int32_t num_seqs,
+                           int32_t total_tokens, int32_t num_q_heads,
+                           const nk_paged_kv_t *cache, void *stream) {
+  if (num_seqs < 0 || total_tokens < 0 || num_q_heads <= 0 || max_pos <= 0) return NK_ERR_INVALID_ARG;
+  int st = check_cache(cache);
+  if (st != NK_OK) return st;
+  if (num_q_heads % cache->num_kv_heads) return NK_ERR_INVALID_ARG;
+  if (layout != NK_ROPE_HALF && layout != NK_ROPE_INTERLEAVED) return NK_ERR_INVALID_ARG;
+  if (rotary_dim <= 0 || rotary_dim > cache->head_dim || rotary_dim % 16) return NK_ERR_UNSUPPORTED;
+  const bool ok_types = (in_dtype == NK_F32 && cache->dtype == NK_F32) ||
+                        (in_dtype == NK_BF16 && (cache->dtype == NK_BF16 || cache->dtype == NK_E4M3));
+  if (!ok_types) return NK_ERR_UNSUPPORTED;
+  if (total_tokens == 0) return NK_OK;
+  if (num_seqs == 0) return NK_ERR_INVALID_ARG;
+  if (!q || !k || !v || !q_out || !q_offsets || !kv_lens || !freqs) return NK_ERR_INVALID_ARG;
+  RopeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.q_out = q_out;
+  a.q_offsets = q_offsets; a.kv_lens = kv_lens; a.position_ids = position_ids;
+  a.freqs = freqs; a.rotary_dim = rotary_dim; a.layout = layout; a.in_dtype = in_dtype;
+  a.max_pos = max_pos;
+  a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.hq = num_q_heads;
+  a.cache = *cache;
+  return launch_rope_write(a, (hipStream_t)stream) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
+}
+
+size_t nk_ragged_paged_attention_workspace_size(int32_t q_dtype, int32_t cache_dtype,
+                                                int32_t num_seqs, int32_t total_q,
+                                                int32_t max_q_len, int32_t max_kv_len,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t window_left,
+                                                int32_t kv_split_tokens) {
+  (void)total_q; (void)max_q_len;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len <= 0) return 0;
+  return workspace_bytes(q_dtype, cache_dtype, num_seqs, max_kv_len, num_q_heads, num_kv_heads,
+                         head_dim, window_left, kv_split_tokens, nullptr, nullptr);
+}
+
+int32_t nk_ragged_paged_attention_split_tokens(int32_t num_seqs, int32_t max_kv_len,
+                                               int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t window_left,
+                                               int32_t kv_split_tokens) {
+  return split_tokens(num_seqs, max_kv_len, num_q_heads, num_kv_heads, head_dim, window_left,
+                      kv_split_tokens);
+}
+
+int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_offsets,
+                              const int32_t *kv_lens, const nk_paged_kv_t *cache,
+                              float softmax_scale, int32_t window_left, void *out, float *lse,
+                              int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                              int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens,
+                              void *workspace, size_t workspace_bytes_given, void *stream) {
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0 || num_q_heads <= 0)
+    return NK_ERR_INVALID_ARG;
+  if (window_left < -1) return NK_ERR_INVALID_ARG;
+  if (kv_split_tokens < 0 || kv_split_tokens % 32) return NK_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return NK_ERR_INVALID_ARG;
+  int st = check_cache(cache);
+  if (st != NK_OK) return st;
+  if (num_q_heads % cache->num_kv_heads) return NK_ERR_INVALID_ARG;
+  const bool ok_types = (q_dtype == NK_F32 && cache->dtype == NK_F32) ||
+                        (q_dtype == NK_BF16 && (cache->dtype == NK_BF16 || cache->dtype == NK_E4M3));
+  if (!ok_types) return NK_ERR_UNSUPPORTED;
+  if (q_dtype == NK_BF16 && num_q_heads / cache->num_kv_heads > 64) return NK_ERR_UNSUPPORTED;
+  if (total_q == 0) return NK_OK;
+  if (num_seqs == 0) return NK_ERR_INVALID_ARG;
+  if (!q || !q_offsets || !kv_lens || !out) return NK_ERR_INVALID_ARG;
+
+  AttnArgs a{};
+  a.q = q; a.q_dtype = q_dtype; a.q_offsets = q_offsets; a.kv_lens = kv_lens;
+  a.cache = *cache; a.softmax_scale = softmax_scale; a.window_left = window_left;
+  a.out = out; a.lse = lse;
+  a.num_seqs = num_seqs; a.total_q = total_q; a.max_q_len = max_q_len; a.max_kv_len = max_kv_len;
+  a.hq = num_q_heads;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (q_dtype == NK_F32) return launch_attn_f32(a, s) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
+
+  int split = 0, chunks = 1;
+  const size_t need = workspace_bytes(q_dtype, cache->dtype, num_seqs, max_kv_len, num_q_heads,
+                                      cache->num_kv_heads, cache->head_dim, window_left,
+                                      kv_split_tokens, &split, &chunks);
+  if (need > 0 && (!workspace || workspace_bytes_given < need)) return NK_ERR_WORKSPACE;
+  a.split_tokens = split;
+  a.max_chunks = chunks;
+  if (need > 0) {
+    const size_t slots = (size_t)num_seqs * chunks;
+    size_t off = slots * num_q_heads * cache->head_dim * sizeof(float);
+    off = (off + 255) / 256 * 256;
+    a.part_out = (float *)workspace;
+    a.part_lse = (float *)((char *)workspace + off);
+  }
+  // prefill rows (q_len > 1) and decode rows (q_len == 1) run as two launches
+  // on the same stream; each kernel skips the rows of the other kind
+  if (max_q_len > 1 && launch_attn_prefill(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  if (launch_attn_decode(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  if (chunks > 1 && launch_decode_merge(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  return NK_OK;
+}
+
+int nk_attention_lse_merge(const float *partial_out, const float *partial_lse,
+                           const int32_t *merge_offsets, int32_t num_rows, int32_t num_heads,
+                           int32_t head_dim, void *out, int32_t out_dtype, float *lse_out,
+                           void *stream) {
+  if (num_rows < 0 || num_heads <= 0 || head_dim <= 0 || head_dim % 2 || head_dim > 512)
+    return NK_ERR_INVALID_ARG;
+  if (out_dtype != NK_F32 && out_dtype != NK_BF16) return NK_ERR_UNSUPPORTED;
+  if (num_rows == 0) return NK_OK;
+  if (!partial_out || !partial_lse || !merge_offsets || !out) return NK_ERR_INVALID_ARG;
+  return launch_lse_merge(partial_out, partial_lse, merge_offsets, num_rows, num_heads, head_dim,
+                          out, out_dtype, lse_out, (hipStream_t)stream) == hipSuccess
+             ? NK_OK : NK_ERR_DEVICE;
+}
+
+int nk_profile_enable(int enable) {
+  prof().enabled = enable != 0;
+  return NK_OK;
+}
+
+int nk_profile_reset(void) {
+  ProfileState &p = prof();
+  std::lock_guard<std::mutex> lock(p.mu);
+  flush_pending(p);
+  p.totals.clear();
+  return NK_OK;
+}
+
+int nk_profile_read(const char *kernel, double *total_ms_host, int64_t *launches_host) {
+  if (!kernel || !total_ms_host || !launches_host) return NK_ERR_INVALID_ARG;
+  ProfileState &p = prof();
+  std::lock_guard<std::mutex> lock(p.mu);
+  flush_pending(p);
+  *total_ms_host = 0.0;
+  *launches_host = 0;
+  for (auto &t : p.totals)
+    if (t.first == kernel) { *total_ms_host = t.second.first; *launches_host = t.second.second; }
+  return NK_OK;
+}
+
+}  // extern "C"

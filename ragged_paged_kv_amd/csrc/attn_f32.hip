@@ -1,0 +1,103 @@
+// Ragged paged attention for float32 queries and a float32 cache (VALU).
+//
+// What it computes: NumKong matrix-kernels page, attention_packed -- query
+// row i of a segment sits at i + kv_len - q_len and sees the causal band
+// (optionally windowed: window_left keys before it); rows with no key give
+// zeros; the log-sum-exp is filled alongside.  Scores are
+// softmax_scale * q.k (Algenta "A scalar reference, not a buffer kernel";
+// explicit scale as in aria_kernel `attention_with_scale`).
+//
+// Design: float32 parity path.  One wave per (query row, query head); lanes
+// take 64 keys at a time, each lane computing a full dot product, followed by
+// an online-softmax update (running max / sum, rescale on a new max, as on
+// the Algenta page's flash-attention walkthrough) and the P.V accumulation
+// with lanes over head dimensions.  Throughput is not the goal here: the
+// float32 workloads are small; the bf16 / fp8 paths use MFMA kernels.
+
+#include "common.h"
+#include "internal.h"
+
+namespace nk {
+namespace {
+
+__global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int D = a.cache.head_dim;
+  const int P = a.cache.page_size;
+  const int hkv = a.cache.num_kv_heads;
+  const int g = h / (a.hq / hkv);
+  __shared__ float qs[256];
+
+  const int s = find_segment(a.q_offsets, a.num_seqs, t);
+  const int q0 = a.q_offsets[s];
+  const int q_len = a.q_offsets[s + 1] - q0;
+  const int L = a.kv_lens[s];
+  const int p = (t - q0) + L - q_len;
+  const int hi = min(p, L - 1);
+  const int lo = a.window_left < 0 ? 0 : max(0, p - a.window_left);
+
+  const float *q = (const float *)a.q + ((size_t)t * a.hq + h) * D;
+  for (int d = lane; d < D; d += kWave) qs[d] = q[d];
+  __syncthreads();
+
+  const float *kp = (const float *)a.cache.k_pages;
+  const float *vp = (const float *)a.cache.v_pages;
+  const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
+
+  float m = -INFINITY, l = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};     // dims lane, lane+64, lane+128, lane+192
+  for (int base = lo; base <= hi; base += kWave) {
+    const int key = base + lane;
+    float sc = -INFINITY;
+    if (key <= hi) {
+      const int page = pt[key / P];
+      const float *krow = kp + (((size_t)page * hkv + g) * P + key % P) * D;
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = fmaf(qs[d], krow[d], acc);
+      sc = a.softmax_scale * acc;
+    }
+    const float cm = wave_max(sc);
+    const float nm = fmaxf(m, cm);
+    const float corr = expf(m - nm);                 // 0 when m = -inf
+    const float pj = key <= hi ? expf(sc - nm) : 0.f;
+    l = l * corr + wave_sum(pj);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= corr;
+    const int nk = min(kWave, hi - base + 1);
+    for (int i = 0; i < nk; ++i) {
+      const float pi = __shfl(pj, i, kWave);
+      const int kk = base + i;
+      const int page = pt[kk / P];
+      const float *vcol = vp + ((size_t)page * hkv + g) * D * P + kk % P;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = lane + r * kWave;
+        if (d < D) o[r] = fmaf(pi, vcol[(size_t)d * P], o[r]);
+      }
+    }
+    m = nm;
+  }
+
+  float *out = (float *)a.out + ((size_t)t * a.hq + h) * D;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int d = lane + r * kWave;
+    if (d < D) out[d] = o[r] * inv;
+  }
+  if (a.lse && lane == 0) a.lse[(size_t)t * a.hq + h] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream) {
+  if (a.total_q == 0) return hipSuccess;
+  ProfileScope prof("attn_f32", stream);
+  dim3 grid((unsigned)a.total_q, (unsigned)a.hq);
+  attn_f32_kernel<<<grid, kWave, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace nk

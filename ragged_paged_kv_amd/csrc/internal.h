@@ -1,0 +1,59 @@
+// Launch descriptors shared between the C-ABI layer (api.hip) and the
+// kernel files.  Host-side only types plus the launcher prototypes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nk.h"
+
+namespace nk {
+
+struct RopeArgs {
+  const void *q, *k, *v;
+  void *q_out;
+  const int32_t *q_offsets, *kv_lens, *position_ids;
+  const float *freqs;
+  int32_t rotary_dim, layout, in_dtype, max_pos;
+  int32_t num_seqs, total_tokens, hq;
+  nk_paged_kv_t cache;
+};
+
+struct AttnArgs {
+  const void *q;
+  int32_t q_dtype;
+  const int32_t *q_offsets, *kv_lens;
+  nk_paged_kv_t cache;
+  float softmax_scale;
+  int32_t window_left;
+  void *out;
+  float *lse;
+  int32_t num_seqs, total_q, max_q_len, max_kv_len, hq;
+  // split-KV decode
+  int32_t split_tokens;     // keys per chunk
+  int32_t max_chunks;       // chunks per decode row (upper bound)
+  float *part_out;          // [num_seqs * max_chunks][hq][D]
+  float *part_lse;          // [num_seqs * max_chunks][hq]
+};
+
+// Each launcher enqueues its kernel(s) on `stream` and returns a
+// hipError_t (hipSuccess when the launch was accepted).
+hipError_t launch_rope_write(const RopeArgs &a, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_decode_merge(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_lse_merge(const float *po, const float *pl, const int32_t *offsets,
+                            int32_t rows, int32_t heads, int32_t head_dim, void *out,
+                            int32_t out_dtype, float *lse_out, hipStream_t stream);
+
+// Kernel timing (diagnostics): bracket a launch with events when enabled.
+struct ProfileScope {
+  ProfileScope(const char *family, hipStream_t stream);
+  ~ProfileScope();
+  int slot;
+  hipStream_t stream;
+};
+
+}  // namespace nk

@@ -1,0 +1,252 @@
+"""Python binding of libnk.so (ctypes): argument marshalling only.
+
+Every function here checks devices, dtypes, shapes and contiguity of torch
+tensors, passes raw device pointers and the current HIP stream to the C ABI
+declared in ``include/nk.h``, and raises ``NKError`` on a non-zero status.
+All computation happens in the library's HIP kernels; if the library is not
+built, importing works but every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnk.so")
+
+NK_F32, NK_BF16, NK_E4M3 = 0, 1, 2
+NK_ROPE_HALF, NK_ROPE_INTERLEAVED = 0, 1
+NK_OK, NK_ERR_INVALID_ARG, NK_ERR_UNSUPPORTED, NK_ERR_WORKSPACE, NK_ERR_DEVICE = 0, 1, 2, 3, 4
+
+EXPORTS = ("nk_rope_qk_write_paged", "nk_ragged_paged_attention",
+           "nk_ragged_paged_attention_workspace_size", "nk_ragged_paged_attention_split_tokens",
+           "nk_attention_lse_merge", "nk_status_string", "nk_version", "nk_profile_enable",
+           "nk_profile_reset", "nk_profile_read")
+
+
+class NKError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class nk_paged_kv_t(ctypes.Structure):
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+                ("dtype", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_table", ctypes.c_void_p),
+                ("page_table_stride", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m ragged_paged_kv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, vp, sz, f32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+        cache_p = ctypes.POINTER(nk_paged_kv_t)
+        L.nk_rope_qk_write_paged.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                             i32, i32, i32, cache_p, vp]
+        L.nk_rope_qk_write_paged.restype = ctypes.c_int
+        L.nk_ragged_paged_attention.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, vp, vp, i32,
+                                                i32, i32, i32, i32, i32, vp, sz, vp]
+        L.nk_ragged_paged_attention.restype = ctypes.c_int
+        L.nk_ragged_paged_attention_workspace_size.argtypes = [i32] * 11
+        L.nk_ragged_paged_attention_workspace_size.restype = sz
+        L.nk_ragged_paged_attention_split_tokens.argtypes = [i32] * 7
+        L.nk_ragged_paged_attention_split_tokens.restype = i32
+        L.nk_attention_lse_merge.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, vp, vp]
+        L.nk_attention_lse_merge.restype = ctypes.c_int
+        L.nk_status_string.argtypes = [ctypes.c_int]
+        L.nk_status_string.restype = ctypes.c_char_p
+        L.nk_version.restype = ctypes.c_int
+        L.nk_profile_enable.argtypes = [ctypes.c_int]
+        L.nk_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64)]
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().nk_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != NK_OK:
+        raise NKError(status, where)
+
+
+def _dtype_code(t):
+    if t == torch.float32:
+        return NK_F32
+    if t == torch.bfloat16:
+        return NK_BF16
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return NK_E4M3
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(*tensors):
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"tensors must share one device, got {devs}")
+    d = devs.pop()
+    if d.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    for t in tensors:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return d
+
+
+def _i32(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+class PagedKVCache:
+    """One layer's paged cache (device tensors in the layout of nk.h).
+
+    k_pages [num_pages, Hkv, P, D], v_pages [num_pages, Hkv, D, P] (float32,
+    bfloat16 or uint8 e4m3 codes), k_scales/v_scales [num_pages, Hkv, P]
+    float32 for e4m3, page_table [num_seqs, stride] int32.
+    """
+
+    def __init__(self, k_pages, v_pages, page_table, k_scales=None, v_scales=None):
+        n, h, p, d = k_pages.shape
+        if tuple(v_pages.shape) != (n, h, d, p):
+            raise ValueError("v_pages must be [num_pages, heads, head_dim, page_size]")
+        if k_pages.dtype != v_pages.dtype:
+            raise TypeError("K and V pages must share a dtype")
+        self.dtype = _dtype_code(k_pages.dtype)
+        if self.dtype == NK_E4M3 and (k_scales is None or v_scales is None):
+            raise ValueError("e4m3 caches need k_scales and v_scales")
+        _i32(page_table, "page_table")
+        _dev(k_pages, v_pages, page_table, k_scales, v_scales)
+        self.k_pages, self.v_pages, self.page_table = k_pages, v_pages, page_table
+        self.k_scales, self.v_scales = k_scales, v_scales
+        self.num_pages, self.num_kv_heads, self.page_size, self.head_dim = n, h, p, d
+
+    def struct(self):
+        return nk_paged_kv_t(self.k_pages.data_ptr(), self.v_pages.data_ptr(),
+                             None if self.k_scales is None else self.k_scales.data_ptr(),
+                             None if self.v_scales is None else self.v_scales.data_ptr(),
+                             self.dtype, self.num_pages, self.page_size, self.num_kv_heads,
+                             self.head_dim, self.page_table.data_ptr(),
+                             self.page_table.shape[1] if self.page_table.dim() == 2 else 0)
+
+
+def rope_qk_write_paged(q, k, v, q_offsets, kv_lens, freqs, cache, rotary_dim, layout="half",
+                        position_ids=None, q_out=None, stream=None):
+    """Rotate q and k by ``freqs`` [max_pos, R/2, 2] and append k/v to the
+    cache; returns q_out ([T, Hq, D], may be q itself)."""
+    T, hq, d = q.shape
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k.shape != (T, cache.num_kv_heads, d) or v.shape != k.shape or q_out.shape != q.shape:
+        raise ValueError("q/k/v shapes disagree with the cache")
+    if not (q.dtype == k.dtype == v.dtype == q_out.dtype):
+        raise TypeError("q, k, v, q_out must share a dtype")
+    if freqs.dtype != torch.float32 or freqs.dim() != 3:
+        raise TypeError("freqs must be float32 [max_pos, R/2, 2]")
+    _i32(q_offsets, "q_offsets"), _i32(kv_lens, "kv_lens")
+    if position_ids is not None:
+        _i32(position_ids, "position_ids")
+    _dev(q, k, v, q_out, q_offsets, kv_lens, position_ids, freqs, cache.k_pages)
+    lay = {"half": NK_ROPE_HALF, "interleaved": NK_ROPE_INTERLEAVED}[layout]
+    c = cache.struct()
+    st = lib().nk_rope_qk_write_paged(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(q_out),
+                                      _ptr(q_offsets), _ptr(kv_lens), _ptr(position_ids), _ptr(freqs),
+                                      freqs.shape[0], rotary_dim, lay, kv_lens.shape[0], T, hq,
+                                      ctypes.byref(c), _stream(stream))
+    _check(st, "nk_rope_qk_write_paged")
+    return q_out
+
+
+def workspace_size(q_dtype, cache, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads,
+                   window_left=-1, kv_split_tokens=0):
+    return int(lib().nk_ragged_paged_attention_workspace_size(
+        _dtype_code(q_dtype), cache.dtype, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads,
+        cache.num_kv_heads, cache.head_dim, window_left, kv_split_tokens))
+
+
+def split_tokens(cache, num_seqs, max_kv_len, num_q_heads, window_left=-1, kv_split_tokens=0):
+    return int(lib().nk_ragged_paged_attention_split_tokens(
+        num_seqs, max_kv_len, num_q_heads, cache.num_kv_heads, cache.head_dim, window_left,
+        kv_split_tokens))
+
+
+def ragged_paged_attention(q, q_offsets, kv_lens, cache, softmax_scale, max_q_len, max_kv_len,
+                           window_left=-1, out=None, lse=None, kv_split_tokens=0, workspace=None,
+                           stream=None):
+    """Causal (optionally windowed) GQA attention of q [T, Hq, D] over the
+    cache; returns (out, lse).  ``lse`` is filled when given (float32
+    [T, Hq]); ``workspace`` is allocated here when not given."""
+    T, hq, d = q.shape
+    B = kv_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    _i32(q_offsets, "q_offsets"), _i32(kv_lens, "kv_lens")
+    _dev(q, q_offsets, kv_lens, out, lse, cache.k_pages, workspace)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is not None and (lse.shape != (T, hq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [T, Hq]")
+    need = workspace_size(q.dtype, cache, B, T, max_q_len, max_kv_len, hq, window_left, kv_split_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = cache.struct()
+    st = lib().nk_ragged_paged_attention(_ptr(q), _dtype_code(q.dtype), _ptr(q_offsets), _ptr(kv_lens),
+                                         ctypes.byref(c), float(softmax_scale), int(window_left),
+                                         _ptr(out), _ptr(lse), B, T, int(max_q_len), int(max_kv_len), hq,
+                                         int(kv_split_tokens), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "nk_ragged_paged_attention")
+    return out, lse
+
+
+def attention_lse_merge(partial_out, partial_lse, merge_offsets, out, lse_out=None, stream=None):
+    """Merge partial states [n, H, D] / [n, H] into rows given by
+    merge_offsets [R+1]; writes out [R, H, D] (float32 or bf16)."""
+    n, h, d = partial_out.shape
+    R = merge_offsets.shape[0] - 1
+    if partial_out.dtype != torch.float32 or partial_lse.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    _i32(merge_offsets, "merge_offsets")
+    _dev(partial_out, partial_lse, merge_offsets, out, lse_out)
+    st = lib().nk_attention_lse_merge(_ptr(partial_out), _ptr(partial_lse), _ptr(merge_offsets), R, h, d,
+                                      _ptr(out), _dtype_code(out.dtype), _ptr(lse_out), _stream(stream))
+    _check(st, "nk_attention_lse_merge")
+    return out, lse_out
+
+
+def profile_enable(on=True):
+    lib().nk_profile_enable(1 if on else 0)
+
+
+def profile_reset():
+    lib().nk_profile_reset()
+
+
+def profile_read(kernel):
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().nk_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)), "nk_profile_read")
+    return ms.value, n.value

@@ -25,6 +25,6 @@ Recipe (per workload, seed = workload number - 1):
 See ``synth.configs`` for the five workloads.
 """
 
-from .configs import (Workload, make, names, new_tokens, freqs_table,  # noqa: F401
+from .configs import (Workload, make, names, new_tokens, freqs_table, custom,  # noqa: F401
                       prior_rows, build_cache, sentinel_cache)
 from . import work  # noqa: F401

@@ -299,3 +299,24 @@ def build_cache(w, threads=8):
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(fill, range(w.num_seqs)))
     return c
+
+
+def custom(q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, *, rotary_dim=None,
+           rope_layout="half", rope_theta=1e4, page_size=16, in_dtype="bf16", cache_dtype="bf16",
+           softmax_scale=None, window_left=-1, qk_norm=False, explicit_positions=True,
+           page_order="permuted", seed=1000, split_tokens=0, name="custom"):
+    """A workload of given shapes (for tests); pages drawn from
+    ``default_rng(seed)``, values from the same per-token/per-sequence streams
+    as the named workloads."""
+    rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    kv_lens = np.asarray(kv_lens, dtype=np.int32)
+    table, npages = _pages(rng, kv_lens, page_size, page_order)
+    w = Workload(name, seed, q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim,
+                 head_dim if rotary_dim is None else rotary_dim, rope_layout, rope_theta, page_size,
+                 in_dtype, cache_dtype, 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale,
+                 window_left, qk_norm, explicit_positions, table, npages, split_tokens)
+    w.seq_ids = np.arange(w.num_seqs)
+    w.token_ids = np.arange(w.total_q)
+    w.full_total_q = w.total_q
+    return w

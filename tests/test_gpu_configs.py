@@ -1,0 +1,133 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times, against the oracle on sampled sequences (the oracle
+regenerates exactly those sequences' inputs from their own random streams).
+
+For each workload: RoPE + append then attention run over the whole batch on
+the GPU; for the sampled sequences the oracle computes q_out, the appended
+cache rows and out/lse.  Checked: stored q_out and appended K/V rows equal
+the oracle's or one rounding step away (e4m3 codes: equal or adjacent, scales
+within one float32 step); every other cache byte unchanged; out and lse
+within the workload's tolerance.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = {
+    1: None,                     # everything
+    2: "ends+4",
+    3: None,
+    4: "mixed",
+    5: "ends+2",
+}
+
+
+def _sample(w, how):
+    if how is None:
+        return np.arange(w.num_seqs)
+    order = np.argsort(w.kv_lens, kind="stable")
+    if how == "mixed":
+        pre = np.nonzero(w.q_lens > 1)[0]
+        dec = np.nonzero(w.q_lens == 1)[0]
+        dec_sorted = dec[np.argsort(w.kv_lens[dec], kind="stable")]
+        return np.unique(np.concatenate([pre[[0, -1]], dec_sorted[[0, -1]], dec[[3, 17]]]))
+    n = int(how.split("+")[1])
+    rng = np.random.default_rng(99)
+    mid = rng.choice(order[1:-1], size=n, replace=False)
+    return np.unique(np.concatenate([order[[0, -1]], mid]))
+
+
+def _written_mask(w):
+    m = np.zeros((w.num_pages, w.num_kv_heads, w.page_size), bool)
+    for s in range(w.num_seqs):
+        L, ql = int(w.kv_lens[s]), int(w.q_lens[s])
+        for j in range(L - ql, L):
+            m[int(w.page_table[s][j // w.page_size]), :, j % w.page_size] = True
+    return m
+
+
+def _cache_rows(w, k_pages, v_pages, seq, slots, page_table):
+    pages = page_table[seq][slots // w.page_size].astype(np.int64)
+    offs = slots % w.page_size
+    return k_pages[pages, :, offs, :], v_pages[pages, :, :, offs]
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_workload_full_size(k):
+    w = synth.make(k)
+    gu.say(f"workload {k} {w.name}: B={w.num_seqs} T={w.total_q} max_kv={w.max_kv_len}")
+    d = gu.to_device(w)
+    q_out, out, lse = gu.run_hip(w, d)
+    torch.cuda.synchronize()
+    gu.say(f"workload {k}: GPU done")
+
+    seqs = _sample(w, SAMPLES[k])
+    ws = w.subset(seqs)
+    raw_sub = synth.build_cache(ws)
+    q_o, cache_o, out_o, lse_o = gu.oracle_run(ws, raw_sub)
+    tok = ws.token_ids
+
+    # --- q_out
+    qg = gu.host_values(q_out, w.in_dtype)[tok]
+    frac = gu.compare_storage(qg, q_o, w.in_dtype, "q_out")
+    gu.say(f"workload {k}: q_out differing fraction {frac:.2e}")
+
+    # --- appended cache rows of the sampled sequences
+    c = d["cache"]
+    kg_all = c.k_pages.cpu()
+    vg_all = c.v_pages.cpu()
+    kg_vals = gu.host_values(kg_all, w.cache_dtype)
+    vg_vals = gu.host_values(vg_all, w.cache_dtype)
+    ok_adj = 0
+    for i, s in enumerate(seqs):
+        L, ql = int(w.kv_lens[s]), int(w.q_lens[s])
+        slots = np.arange(L - ql, L)
+        kg, vg = _cache_rows(w, kg_vals, vg_vals, s, slots, w.page_table)
+        ko, vo = _cache_rows(w, cache_o.k, cache_o.v, i, slots, ws.page_table)
+        if w.cache_dtype == "e4m3":
+            kcg, vcg = _cache_rows(w, kg_all.view(torch.uint8).numpy(), vg_all.view(torch.uint8).numpy(),
+                                   s, slots, w.page_table)
+            kco, vco = formats.e4m3_code(ko), formats.e4m3_code(vo)
+            for a, b, what in ((kcg, kco, "K codes"), (vcg, vco, "V codes")):
+                ia = np.where(a & 0x80, -(a & 0x7F).astype(int), (a & 0x7F).astype(int))
+                ib = np.where(b & 0x80, -(b & 0x7F).astype(int), (b & 0x7F).astype(int))
+                assert np.abs(ia - ib).max() <= 1, f"{what} not adjacent"
+                ok_adj += int(np.sum(ia != ib))
+            pages = w.page_table[s][slots // w.page_size]
+            opages = ws.page_table[i][slots // w.page_size]
+            for sc_g, sc_o in ((c.k_scales.cpu().numpy(), cache_o.k_scale), (c.v_scales.cpu().numpy(), cache_o.v_scale)):
+                g_ = sc_g[pages, :, slots % w.page_size].astype(np.float64)
+                o_ = sc_o[opages, :, slots % w.page_size]
+                assert np.all(np.abs(g_ - o_) <= 2.0 ** -23 * np.abs(o_)), "scales differ by more than one step"
+        else:
+            gu.compare_storage(kg, ko, w.cache_dtype, "K rows")
+            gu.compare_storage(vg, vo, w.cache_dtype, "V rows")
+    gu.say(f"workload {k}: appended rows ok (adjacent fp8 codes {ok_adj})")
+
+    # --- nothing else in the cache changed
+    raw = d["raw_cache"]
+    mask = _written_mask(w)
+    kb = kg_all.view(torch.uint8).numpy().reshape(w.num_pages, w.num_kv_heads, w.page_size, -1)
+    kr = raw["k_pages"].view(np.uint8).reshape(kb.shape)
+    assert np.array_equal(kb[~mask], kr[~mask]), "K bytes outside the appended slots changed"
+    vb = vg_all.view(torch.uint8).numpy()
+    vr = raw["v_pages"].view(np.uint8).reshape(vb.shape)
+    vmask = np.repeat(np.transpose(mask, (0, 1, 2))[:, :, None, :], w.head_dim, axis=2)
+    vmask = np.repeat(vmask, vb.shape[-1] // w.page_size, axis=3) if vb.shape[-1] != w.page_size else vmask
+    assert np.array_equal(vb[~vmask], vr[~vmask]), "V bytes outside the appended slots changed"
+    gu.say(f"workload {k}: untouched bytes ok")
+
+    # --- attention output
+    tol = gu.tol_for(w)
+    og = gu.host_values(out, w.in_dtype)[tok]
+    lg = lse.cpu().numpy().astype(np.float64)[tok]
+    e_out = gu.check_close(og, out_o, tol, "out")
+    e_lse = gu.check_close(lg, lse_o, tol, "lse")
+    gu.say(f"workload {k}: out max err {e_out:.3g}, lse max err {e_lse:.3g} (tol {tol})")
