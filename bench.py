@@ -15,9 +15,10 @@ baseline.
 
 Timing: W untimed warm-up steps, then K timed steps, the whole loop
 bracketed by torch.cuda.synchronize().  Before every step a 1 GiB buffer is
-overwritten (outside the step's events) so that the 256 MB Infinity Cache
-holds none of the step's inputs; each step is timed with HIP events on the
-step's stream and ms_per_step is the median.  Per-kernel durations come from
+read (outside the step's events) so that the 256 MB Infinity Cache and the
+L2s hold none of the step's inputs -- a read, not a write, so that the step
+does not pay for writing back someone else's dirty lines; each step is timed
+with HIP events on the step's stream and ms_per_step is the median.  Per-kernel durations come from
 the library's own event pairs around each launch (nk_profile_*).
 """
 
@@ -60,12 +61,15 @@ def log(*a):
 
 
 # ------------------------------------------------------------------ GPU part
-def run_workload(name, steps, warmup, flush):
+class Prepared:
+    """One workload's inputs resident on the GPU."""
+
+
+def prepare(name):
     import numpy as np
     import torch
 
     import synth
-    from synth import work
     from ragged_paged_kv_amd import nk
 
     w = synth.make(name)
@@ -78,10 +82,12 @@ def run_workload(name, steps, warmup, flush):
         x = torch.from_numpy(np.ascontiguousarray(x))
         return (x.view(dt) if dt is not None else x).to(dev)
 
+    st = Prepared()
+    st.w = w
     if w.in_dtype == "bf16":
-        q, k, v = (t(nt[n].view(np.int16), torch.bfloat16) for n in ("q", "k", "v"))
+        st.q, st.k, st.v = (t(nt[n].view(np.int16), torch.bfloat16) for n in ("q", "k", "v"))
     else:
-        q, k, v = (t(nt[n]) for n in ("q", "k", "v"))
+        st.q, st.k, st.v = (t(nt[n]) for n in ("q", "k", "v"))
     if w.cache_dtype == "bf16":
         kp, vp = t(raw["k_pages"].view(np.int16), torch.bfloat16), t(raw["v_pages"].view(np.int16), torch.bfloat16)
     else:
@@ -89,27 +95,40 @@ def run_workload(name, steps, warmup, flush):
     ks = None if raw["k_scales"] is None else t(raw["k_scales"])
     vs = None if raw["v_scales"] is None else t(raw["v_scales"])
     del raw
-    cache = nk.PagedKVCache(kp, vp, t(w.page_table.astype(np.int32)), ks, vs)
-    q_offsets, kv_lens = t(w.q_offsets.astype(np.int32)), t(w.kv_lens.astype(np.int32))
-    pos = None if w.position_ids is None else t(w.position_ids.astype(np.int32))
-    freqs = t(synth.freqs_table(w))
-    q_out = torch.empty_like(q)
-    out = torch.empty_like(q)
-    lse = torch.empty(w.total_q, w.num_q_heads, dtype=torch.float32, device=dev)
-    ws_bytes = nk.workspace_size(q.dtype, cache, w.num_seqs, w.total_q, w.max_q_len, w.max_kv_len,
-                                 w.num_q_heads, w.window_left, w.split_tokens)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    split = nk.split_tokens(cache, w.num_seqs, w.max_kv_len, w.num_q_heads, w.window_left, w.split_tokens)
-    log(f"{name}: inputs ready in {time.time() - t0:.1f}s (cache {kp.numel() * kp.element_size() / 1e9:.2f} GB, "
-        f"split {split}, workspace {ws_bytes / 1e6:.1f} MB)")
+    st.cache = nk.PagedKVCache(kp, vp, t(w.page_table.astype(np.int32)), ks, vs)
+    st.q_offsets, st.kv_lens = t(w.q_offsets.astype(np.int32)), t(w.kv_lens.astype(np.int32))
+    st.pos = None if w.position_ids is None else t(w.position_ids.astype(np.int32))
+    st.freqs = t(synth.freqs_table(w))
+    st.q_out = torch.empty_like(st.q)
+    st.out = torch.empty_like(st.q)
+    st.lse = torch.empty(w.total_q, w.num_q_heads, dtype=torch.float32, device=dev)
+    log(f"{name}: inputs ready in {time.time() - t0:.1f}s (cache {kp.numel() * kp.element_size() / 1e9:.2f} GB)")
+    return st
+
+
+def measure(st, steps, warmup, flush, split=None):
+    """Time `steps` hot-path steps on prepared inputs (see module doc)."""
+    import torch
+
+    from synth import work
+    from ragged_paged_kv_amd import nk
+
+    w = st.w
+    split_req = w.split_tokens if split is None else split
+    ws_bytes = nk.workspace_size(st.q.dtype, st.cache, w.num_seqs, w.total_q, w.max_q_len, w.max_kv_len,
+                                 w.num_q_heads, w.window_left, split_req)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    split_used = nk.split_tokens(st.cache, w.num_seqs, w.max_kv_len, w.num_q_heads, w.window_left, split_req)
 
     def step():
-        nk.rope_qk_write_paged(q, k, v, q_offsets, kv_lens, freqs, cache, w.rotary_dim, w.rope_layout,
-                               position_ids=pos, q_out=q_out)
-        nk.ragged_paged_attention(q_out, q_offsets, kv_lens, cache, w.softmax_scale, w.max_q_len, w.max_kv_len,
-                                  w.window_left, out=out, lse=lse, kv_split_tokens=w.split_tokens, workspace=ws)
+        nk.rope_qk_write_paged(st.q, st.k, st.v, st.q_offsets, st.kv_lens, st.freqs, st.cache, w.rotary_dim,
+                               w.rope_layout, position_ids=st.pos, q_out=st.q_out)
+        nk.ragged_paged_attention(st.q_out, st.q_offsets, st.kv_lens, st.cache, w.softmax_scale, w.max_q_len,
+                                  w.max_kv_len, w.window_left, out=st.out, lse=st.lse, kv_split_tokens=split_req,
+                                  workspace=ws)
 
-    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -120,7 +139,7 @@ def run_workload(name, steps, warmup, flush):
     wall0 = time.perf_counter()
     for i in range(steps):
         if scratch is not None:
-            scratch.fill_(float(i))
+            torch.sum(scratch, dim=0, out=sink)
         evs[i][0].record()
         step()
         evs[i][1].record()
@@ -135,8 +154,8 @@ def run_workload(name, steps, warmup, flush):
         if n:
             kern[fam] = {"avg_ms": tot / n, "launches": n}
     res = {
-        "workload": name, "descr": DESCR[name], "ms_per_step": ms, "ms_min": times[0], "ms_max": times[-1],
-        "wall_s_incl_flush": wall, "kernels": kern, "split_tokens": split,
+        "workload": w.name, "descr": DESCR[w.name], "ms_per_step": ms, "ms_min": times[0], "ms_max": times[-1],
+        "wall_s_incl_flush": wall, "kernels": kern, "split_tokens": split_used,
         "decode_bytes": work.decode_bytes(w), "prefill_flops": work.prefill_flops(w), "rope_bytes": work.rope_bytes(w),
     }
     if res["decode_bytes"]:
@@ -149,7 +168,15 @@ def run_workload(name, steps, warmup, flush):
             res["prefill_TFLOPs_kernel"] = res["prefill_flops"] / kern["attn_prefill"]["avg_ms"] / 1e9
     if "rope_write" in kern:
         res["rope_GBps_kernel"] = res["rope_bytes"] / kern["rope_write"]["avg_ms"] / 1e6
-    del cache, kp, vp, ks, vs, scratch, ws
+    del scratch, ws
+    return res
+
+
+def run_workload(name, steps, warmup, flush):
+    import torch
+    st = prepare(name)
+    res = measure(st, steps, warmup, flush)
+    del st
     torch.cuda.empty_cache()
     return res
 

@@ -41,7 +41,10 @@
  *
  * Paged cache layout (one layer), nk_paged_kv_t:
  *
- *   K pages   [num_pages][num_kv_heads][page_size][head_dim]
+ *   K pages   [num_pages][num_kv_heads][head_dim/32][page_size][32]
+ *             (within one page and head, K is stored in blocks of 32
+ *             dimensions: block b holds dims 32b..32b+31 of every token of the
+ *             page, token after token)
  *   V pages   [num_pages][num_kv_heads][head_dim][page_size]
  *             (within one page and head, V is stored dimension-major: the
  *             page's tokens are contiguous for each dimension)

@@ -3,7 +3,9 @@
 
 Layout (one layer):
 
-* K pages  ``[num_pages][num_kv_heads][page_size][head_dim]``
+* K pages  ``[num_pages][num_kv_heads][head_dim/32][page_size][32]`` -- within
+  a page, for one head, K is stored in blocks of 32 dimensions: block b holds
+  dims 32b..32b+31 of every token of the page, token after token.
 * V pages  ``[num_pages][num_kv_heads][head_dim][page_size]`` -- within a page,
   for one head, values are stored dimension-major (the page's tokens are
   contiguous for each dimension).
@@ -20,8 +22,9 @@ library's.
 
 The oracle keeps the cache as float64 *stored values*: for ``f32`` and
 ``bf16`` the element values, for ``e4m3`` the values of the codes (unscaled)
-plus the per-slot scales.  ``from_storage`` / ``to_storage`` convert to and
-from raw bytes.
+plus the per-slot scales, with K held token-major ([page][head][slot][dim]);
+``from_storage`` / ``to_storage`` convert to and from the raw bytes of the
+layout above.
 """
 
 import numpy as np
@@ -61,11 +64,15 @@ class PagedCache:
     def from_storage(cls, dtype, k_pages, v_pages, k_scales=None, v_scales=None):
         """Build from raw arrays: float32 (f32), uint16 bit patterns (bf16)
         or uint8 codes (e4m3), shaped as the layout above."""
-        n, h, p, d = k_pages.shape
+        n, h, nb, p, blk = k_pages.shape
+        if blk != 32:
+            raise ValueError("K pages must be [num_pages][heads][head_dim/32][page_size][32]")
+        d = nb * 32
         c = cls(dtype, n, h, p, d)
         if v_pages.shape != (n, h, d, p):
             raise ValueError("V pages must be [num_pages][heads][head_dim][page_size]")
-        c.k = _decode(dtype, k_pages)
+        # [n][h][d/32][p][32] -> token-major [n][h][p][d]
+        c.k = _decode(dtype, np.transpose(k_pages, (0, 1, 3, 2, 4)).reshape(n, h, p, d))
         c.v = _decode(dtype, v_pages)
         if dtype == "e4m3":
             c.k_scale = np.asarray(k_scales, dtype=np.float32).astype(np.float64)
@@ -75,7 +82,9 @@ class PagedCache:
     def to_storage(self):
         """Raw arrays (k_pages, v_pages, k_scales, v_scales); unwritten slots
         (NaN) become the dtype's NaN pattern, scales NaN."""
+        n, h, p, d = self.k.shape
         k = _encode(self.dtype, self.k)
+        k = np.ascontiguousarray(np.transpose(k.reshape(n, h, p, d // 32, 32), (0, 1, 3, 2, 4)))
         v = _encode(self.dtype, self.v)
         if self.dtype == "e4m3":
             return k, v, self.k_scale.astype(np.float32), self.v_scale.astype(np.float32)

@@ -15,6 +15,9 @@ LIB = os.path.join(HERE, "libnk.so")
 SOURCES = ["api.hip", "rope_write.hip", "attn_decode.hip", "attn_prefill.hip", "attn_f32.hip",
            "lse_merge.hip"]
 ARCH = "gfx950"
+# per-file extra flags: the decode kernel keeps its MFMA accumulators in
+# ordinary VGPRs (its VALU rescales them every step)
+FILE_FLAGS = {"attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU ops are left out of the generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -28,16 +31,16 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=False, jobs=None):
+def build(verbose=False, jobs=None, extra_flags=(), out_path=None, objdir=None):
     cc = hipcc()
-    objdir = os.path.join(HERE, "_build")
+    objdir = objdir or os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *FLAGS, *FILE_FLAGS.get(src, []), *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -54,13 +57,14 @@ def build(verbose=False, jobs=None):
         for src, text in failed:
             sys.stderr.write(f"---- {src}\n{text}\n")
         raise RuntimeError("HIP compilation failed: " + ", ".join(s for s, _ in failed))
-    tmp = LIB + ".tmp"
+    lib = out_path or LIB
+    tmp = lib + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

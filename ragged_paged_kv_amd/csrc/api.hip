@@ -35,22 +35,20 @@ int check_cache(const nk_paged_kv_t *c) {
   return NK_OK;
 }
 
-// Keys per split-KV chunk of a decode row.
+// Keys per split-KV chunk of a decode row: about 4096 single-wave work items
+// over the batch (four per SIMD of a 256-CU part, all resident at once),
+// chunks of 128..4096 keys, a multiple of 32.
 int split_tokens(int num_seqs, int max_kv_len, int hq, int hkv, int head_dim, int window_left,
                  int requested) {
-  if (requested > 0) return requested;
-  int span = window_left < 0 ? max_kv_len : std::min(max_kv_len, window_left + 32);
-  if (span <= 0) return 512;
-  // aim for about 4 chunk work-groups per CU over the batch, in 256..2048-key
-  // chunks (a multiple of 32 keys)
-  const long long target = 4LL * 256;
-  long long per_row = (target + (long long)num_seqs * hkv - 1) / std::max(1LL, (long long)num_seqs * hkv);
-  long long s = (span + per_row - 1) / std::max(1LL, per_row);
-  s = std::max(256LL, std::min(2048LL, s));
-  s = (s + 31) / 32 * 32;
-  (void)hq;
   (void)head_dim;
-  return (int)s;
+  if (requested > 0) return requested;
+  const long long span = window_left < 0 ? max_kv_len : std::min<long long>(max_kv_len, (long long)window_left + 32);
+  if (span <= 0) return 128;
+  const long long rows = (long long)std::max(num_seqs, 1) * hkv * ((hq / hkv + 15) / 16);
+  const long long per_row = std::max(1LL, 4096 / std::max(1LL, rows));
+  long long s = (span + per_row - 1) / per_row;
+  s = std::max(128LL, std::min(4096LL, s));
+  return (int)((s + 31) / 32 * 32);
 }
 
 int max_chunks(int max_kv_len, int window_left, int split) {

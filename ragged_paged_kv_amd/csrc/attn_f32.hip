@@ -53,9 +53,10 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
     float sc = -INFINITY;
     if (key <= hi) {
       const int page = pt[key / P];
-      const float *krow = kp + (((size_t)page * hkv + g) * P + key % P) * D;
+      // K page-head: [dim/32][slot][32]
+      const float *kph = kp + ((size_t)page * hkv + g) * P * D + (key % P) * 32;
       float acc = 0.f;
-      for (int d = 0; d < D; ++d) acc = fmaf(qs[d], krow[d], acc);
+      for (int d = 0; d < D; ++d) acc = fmaf(qs[d], kph[(d >> 5) * P * 32 + (d & 31)], acc);
       sc = a.softmax_scale * acc;
     }
     const float cm = wave_max(sc);

@@ -15,10 +15,11 @@
 //     KV head (GW * BM/32 = waves; each wave owns 32 rows of one head), so
 //     every K/V tile staged in LDS serves all GW heads;
 //   * KV tiles of 64 keys (four 16-token or two 32-token pages) are gathered
-//     through the page table into LDS: K as [key][dim], V as [dim][key] (the
-//     cache already stores V dimension-major per page), 16-byte chunks XOR-
-//     swizzled against bank conflicts; e4m3 codes are widened to bf16 on the
-//     way in, their scales kept beside the tile;
+//     through the page table into LDS with contiguous 16-byte reads: K as
+//     [key][dim] (from the cache's 32-dim blocks), V as [dim][key] (the cache
+//     already stores V dimension-major per page), 16-byte chunks XOR-swizzled
+//     against bank conflicts; e4m3 codes are widened to bf16 on the way in,
+//     their scales kept beside the tile;
 //   * per wave: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 rows),
 //     with K rows read in a permuted key order that makes the score tile's
 //     lane layout the P^T operand layout of the second product
@@ -73,13 +74,16 @@ struct Loader {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
-      // K: chunk c -> key c / (D/8), dims 8*(c % (D/8)) ..
+      // K: chunk c -> (page of the tile, 32-dim block, key in page, 8 dims);
+      // consecutive chunks are consecutive in the page's [dim/32][key][32]
       {
-        const int key = c / (D / 8), slot = c % (D / 8);
-        const int kk = tile_base + key;
+        const int e8 = c & 3, rest = c >> 2;
+        const int kip = rest % P, rest2 = rest / P;
+        const int blk = rest2 % (D / 32), pit = rest2 / (D / 32);
+        const int kk = tile_base + pit * P + kip;
         const int page = pt[min(kk / P, last_page)];
-        const size_t row = ((size_t)page * hkv + g) * P + (kk % P);
-        k[i] = *(const Raw *)(kb + (row * D + 8 * slot) * esz);
+        const size_t ph = (size_t)page * hkv + g;
+        k[i] = *(const Raw *)(kb + (ph * P * D + ((size_t)blk * P + kip) * 32 + 8 * e8) * esz);
       }
       // V: chunk c -> dim c / 8, keys 8*(c % 8) ..
       {
@@ -104,7 +108,10 @@ struct Loader {
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
       {
-        const int key = c / (D / 8), slot = c % (D / 8);
+        const int e8 = c & 3, rest = c >> 2;
+        const int kip = rest % P, rest2 = rest / P;
+        const int blk = rest2 % (D / 32), pit = rest2 / (D / 32);
+        const int key = pit * P + kip, slot = blk * 4 + e8;
         bf16x8_t x;
         if constexpr (FP8) x = fp8x8_to_bf16x8(k[i]); else x = k[i];
         if (tile_base + key >= L) x = bf16x8_t{};
@@ -288,11 +295,10 @@ __global__ void __launch_bounds__(NWAVES * 64) attn_prefill_kernel(AttnArgs a, i
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float p[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      p[i] = fast_exp2(x[i] - m_use);
-      l_run += p[i];
-    }
+    for (int i = 0; i < 32; ++i) p[i] = fast_exp2(x[i] - m_use);
     if (FP8) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) l_run += p[i];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -300,6 +306,15 @@ __global__ void __launch_bounds__(NWAVES * 64) attn_prefill_kernel(AttnArgs a, i
           const int key = 32 * st + perm_key(8 * (v >> 2) + 4 * half + (v & 3));
           p[16 * st + v] *= svs[key];
         }
+    } else {
+      // the normaliser sums the probabilities as the P.V product sees them
+      // (rounded to bf16), so the weights stay self-consistent: a dominant
+      // key reproduces its value row exactly even when p is up to 2^8
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        p[i] = (float)(bf16_t)p[i];
+        l_run += p[i];
+      }
     }
     // ---- O^T += V^T P^T over four 16-key chunks
 #pragma unroll

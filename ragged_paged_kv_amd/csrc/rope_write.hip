@@ -8,6 +8,10 @@
 // `rope_half_partial`: only the first rotary_dim dims).  float8 caches store
 // one scale per (token, kv head), absmax / 448.
 //
+// Rounding: the rotation runs in float64 and every stored element is rounded
+// once from it (see round_odd_f32), so q_out and the appended cache rows are
+// exactly the float64 definition rounded to the storage type.
+//
 // Design: a streaming pass, HBM-bound.  One thread owns a "unit" of 16
 // elements of one head of one token: for the rotate-half layout the 8
 // elements [8j, 8j+8) and their partners [R/2+8j, R/2+8j+8); for the
@@ -26,110 +30,90 @@ namespace {
 
 enum CacheKind { kCacheF32 = 0, kCacheBF16 = 1, kCacheE4M3 = 2 };
 
+// ---------------------------------------------------------------- rounding
+// The rotation is computed in float64: an input (bf16 or float32) times a
+// float32 table entry is exact in float64, so x*c - y*s is the float64
+// nearest to the exact value, as the float64 definition computes it.  Each
+// stored element is then rounded ONCE from that float64: to float32 directly,
+// to bf16 / e4m3 through a float32 rounded to odd (truncate, then set the last
+// bit if anything was dropped) -- with at least two spare bits, the final
+// round-to-nearest-even of a round-to-odd intermediate equals the direct
+// rounding of the float64.
+
+NK_DEVICE float round_odd_f32(double d) {
+  float f = __double2float_rz(d);
+  if ((double)f != d) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return f;
+}
+
 template <typename T> struct InTraits;
 template <> struct InTraits<float> {
-  static NK_DEVICE void load8(const float *p, float *x) {
+  static NK_DEVICE void load8(const float *p, double *x) {
     f32x4_t a = *(const f32x4_t *)p, b = *(const f32x4_t *)(p + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
   }
-  static NK_DEVICE void store8(float *p, const float *x) {
+  static NK_DEVICE void store8(float *p, const double *x) {
     f32x4_t a, b;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { a[i] = x[i]; b[i] = x[4 + i]; }
+    for (int i = 0; i < 4; ++i) { a[i] = (float)x[i]; b[i] = (float)x[4 + i]; }
     *(f32x4_t *)p = a;
     *(f32x4_t *)(p + 4) = b;
   }
 };
 template <> struct InTraits<bf16_t> {
-  static NK_DEVICE void load8(const bf16_t *p, float *x) {
+  static NK_DEVICE void load8(const bf16_t *p, double *x) {
     bf16x8_t a = *(const bf16x8_t *)p;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (float)a[i];
+    for (int i = 0; i < 8; ++i) x[i] = (double)(float)a[i];
   }
-  static NK_DEVICE void store8(bf16_t *p, const float *x) {
+  static NK_DEVICE void store8(bf16_t *p, const double *x) {
     bf16x8_t a;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = (bf16_t)x[i];
+    for (int i = 0; i < 8; ++i) a[i] = (bf16_t)round_odd_f32(x[i]);
     *(bf16x8_t *)p = a;
   }
 };
 
-// Store 8 consecutive K elements of a cache row (same element order).
-template <int CACHE> NK_DEVICE void store_k8(void *row, int d0, const float *x, float inv_scale);
-template <> NK_DEVICE void store_k8<kCacheF32>(void *row, int d0, const float *x, float) {
+// e4m3 code pair from two float64 quotients x/scale (already in range or
+// saturated at +-448 here).
+NK_DEVICE uint32_t fp8x2(double a, double b) {
+  return f32x2_to_fp8x2(round_odd_f32(fmin(fmax(a, -448.0), 448.0)),
+                        round_odd_f32(fmin(fmax(b, -448.0), 448.0)));
+}
+
+// Store 8 consecutive K elements (within one 32-dim block of a token).
+template <int CACHE> NK_DEVICE void store_k8(void *row, int d0, const double *x);
+template <> NK_DEVICE void store_k8<kCacheF32>(void *row, int d0, const double *x) {
   InTraits<float>::store8((float *)row + d0, x);
 }
-template <> NK_DEVICE void store_k8<kCacheBF16>(void *row, int d0, const float *x, float) {
+template <> NK_DEVICE void store_k8<kCacheBF16>(void *row, int d0, const double *x) {
   InTraits<bf16_t>::store8((bf16_t *)row + d0, x);
 }
-template <> NK_DEVICE void store_k8<kCacheE4M3>(void *row, int d0, const float *x, float inv) {
+template <> NK_DEVICE void store_k8<kCacheE4M3>(void *row, int d0, const double *x) {
   u32x2_t w;
-  w[0] = f32x2_to_fp8x2(x[0] * inv, x[1] * inv) | (f32x2_to_fp8x2(x[2] * inv, x[3] * inv) << 16);
-  w[1] = f32x2_to_fp8x2(x[4] * inv, x[5] * inv) | (f32x2_to_fp8x2(x[6] * inv, x[7] * inv) << 16);
+  w[0] = fp8x2(x[0], x[1]) | (fp8x2(x[2], x[3]) << 16);
+  w[1] = fp8x2(x[4], x[5]) | (fp8x2(x[6], x[7]) << 16);
   *(u32x2_t *)((uint8_t *)row + d0) = w;
 }
 
 // Store 8 V elements d0..d0+7 into a dimension-major page (stride P).
-template <int CACHE> NK_DEVICE void store_v8(void *col, int d0, int P, const float *x, float inv);
-template <> NK_DEVICE void store_v8<kCacheF32>(void *col, int d0, int P, const float *x, float) {
+template <int CACHE> NK_DEVICE void store_v8(void *col, int d0, int P, const double *x);
+template <> NK_DEVICE void store_v8<kCacheF32>(void *col, int d0, int P, const double *x) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ((float *)col)[(size_t)(d0 + e) * P] = x[e];
+  for (int e = 0; e < 8; ++e) ((float *)col)[(size_t)(d0 + e) * P] = (float)x[e];
 }
-template <> NK_DEVICE void store_v8<kCacheBF16>(void *col, int d0, int P, const float *x, float) {
+template <> NK_DEVICE void store_v8<kCacheBF16>(void *col, int d0, int P, const double *x) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ((bf16_t *)col)[(size_t)(d0 + e) * P] = (bf16_t)x[e];
+  for (int e = 0; e < 8; ++e) ((bf16_t *)col)[(size_t)(d0 + e) * P] = (bf16_t)round_odd_f32(x[e]);
 }
-template <> NK_DEVICE void store_v8<kCacheE4M3>(void *col, int d0, int P, const float *x, float inv) {
+template <> NK_DEVICE void store_v8<kCacheE4M3>(void *col, int d0, int P, const double *x) {
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
-    uint32_t c = f32x2_to_fp8x2(x[e] * inv, x[e + 1] * inv);
+    uint32_t c = fp8x2(x[e], x[e + 1]);
     ((uint8_t *)col)[(size_t)(d0 + e) * P] = (uint8_t)(c & 0xff);
     ((uint8_t *)col)[(size_t)(d0 + e + 1) * P] = (uint8_t)(c >> 8);
   }
-}
-
-// x / scale for the float8 quantiser, returned so that rounding it to e4m3
-// (nearest, ties to even) gives the rounding of the EXACT quotient.  The
-// float32 quotient is correctly rounded, so it can only be on the wrong side
-// of an e4m3 rounding midpoint by landing exactly on that midpoint; then the
-// sign of the exact remainder x - q*scale (one fma, exactly signed) says which
-// way the exact quotient lies, and q moves one float32 step that way.  With
-// bf16 inputs such near-ties are common (x*448/absmax is often a midpoint).
-NK_DEVICE float fp8_quotient(float x, float scale) {
-  float q = x / scale;
-  const float aq = fabsf(q);
-  if (!(aq < kFp8Max) || aq == 0.f) return q;
-  const int e = (int)((__float_as_uint(aq) >> 23) & 0xff) - 127;   // aq in [2^e, 2^(e+1))
-  if (e < -126) return q;
-  const int step = max(e, -6) - 3;                  // e4m3 spacing 2^step around aq
-  const float t = ldexpf(aq, 1 - step);             // exact: power-of-two scaling
-  if (t == truncf(t) && (((int)t) & 1)) {           // aq is a midpoint
-    const float r = fmaf(-q, scale, x);
-    if (r != 0.f) q = nextafterf(q, r > 0.f ? INFINITY : -INFINITY);
-  }
-  return q;
-}
-
-struct Fp8Div {
-  float scale;
-  NK_DEVICE void apply(float *x) const {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = scale > 0.f ? fp8_quotient(x[e], scale) : 0.f;
-  }
-};
-
-// a*d - b*c to within 1.5 float32 ulps of the exact value (Kahan's 2x2
-// determinant: the product b*c is split into its float32 value and its exact
-// rounding error by an fma).  A plain float32 x*c - y*s can lose every digit
-// to cancellation; this keeps the stored rotation within one storage
-// rounding of the exact one.
-NK_DEVICE float det2(float a, float d, float b, float c) {
-#pragma clang fp contract(off)
-  const float w = b * c;
-  const float e = fmaf(-b, c, w);       // w - b*c, exactly
-  const float f = fmaf(a, d, -w);
-  return f + e;
 }
 
 template <typename TIn, int CACHE, bool INTERLEAVED>
@@ -165,7 +149,7 @@ __global__ void __launch_bounds__(256) rope_write_kernel(RopeArgs a) {
   } else {
     a0 = R + 16 * (j - (R >> 4)); b0 = a0 + 8;
   }
-  float xa[8], xb[8];
+  double xa[8], xb[8];
   InTraits<TIn>::load8(src + a0, xa);
   InTraits<TIn>::load8(src + b0, xb);
 
@@ -179,7 +163,7 @@ __global__ void __launch_bounds__(256) rope_write_kernel(RopeArgs a) {
     // the table read stays inside the table
     const int pos = min(max(a.position_ids ? a.position_ids[t] : slot, 0), a.max_pos - 1);
     const f32x4_t *cs = (const f32x4_t *)(a.freqs + ((size_t)pos * (R >> 1) + 8 * j) * 2);
-    float c[8], sn[8];
+    double c[8], sn[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x4_t v = cs[i];
@@ -188,19 +172,19 @@ __global__ void __launch_bounds__(256) rope_write_kernel(RopeArgs a) {
     if (INTERLEAVED) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x = xa[2 * e], y = xa[2 * e + 1];
-        xa[2 * e] = det2(x, c[e], y, sn[e]);
-        xa[2 * e + 1] = det2(x, sn[e], -y, c[e]);
+        double x = xa[2 * e], y = xa[2 * e + 1];
+        xa[2 * e] = x * c[e] - y * sn[e];
+        xa[2 * e + 1] = x * sn[e] + y * c[e];
         x = xb[2 * e]; y = xb[2 * e + 1];
-        xb[2 * e] = det2(x, c[4 + e], y, sn[4 + e]);
-        xb[2 * e + 1] = det2(x, sn[4 + e], -y, c[4 + e]);
+        xb[2 * e] = x * c[4 + e] - y * sn[4 + e];
+        xb[2 * e + 1] = x * sn[4 + e] + y * c[4 + e];
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = xa[e], y = xb[e];
-        xa[e] = det2(x, c[e], y, sn[e]);
-        xb[e] = det2(x, sn[e], -y, c[e]);
+        double x = xa[e], y = xb[e];
+        xa[e] = x * c[e] - y * sn[e];
+        xb[e] = x * sn[e] + y * c[e];
       }
     }
   }
@@ -217,28 +201,32 @@ __global__ void __launch_bounds__(256) rope_write_kernel(RopeArgs a) {
   const int off = slot % P;
   const size_t ph = (size_t)page * hkv + head;
 
-  float inv = 1.f;
   if (CACHE == kCacheE4M3) {
     // absmax over the head: the D/16 units of a head are consecutive lanes
-    float m = 0.f;
+    double m = 0.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fmaxf(fabsf(xa[e]), fabsf(xb[e])));
-    for (int mask = 1; mask < units_per_head; mask <<= 1) m = fmaxf(m, shfl_xor_f32(m, mask));
-    const float scale = m / kFp8Max;
-    Fp8Div{scale}.apply(xa);
-    Fp8Div{scale}.apply(xb);
+    for (int e = 0; e < 8; ++e) m = fmax(m, fmax(fabs(xa[e]), fabs(xb[e])));
+    for (int mask = 1; mask < units_per_head; mask <<= 1) m = fmax(m, __shfl_xor(m, mask, kWave));
+    const float scale = (float)(m / 448.0);            // float32 nearest to absmax / 448
+    const double sd = scale;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xa[e] = scale > 0.f ? xa[e] / sd : 0.0;
+      xb[e] = scale > 0.f ? xb[e] / sd : 0.0;
+    }
     if (j == 0) (kind == 1 ? a.cache.k_scales : a.cache.v_scales)[ph * P + off] = scale;
   }
 
   constexpr int esz = CACHE == kCacheF32 ? 4 : (CACHE == kCacheBF16 ? 2 : 1);
   if (kind == 1) {
-    void *row = (uint8_t *)a.cache.k_pages + (ph * P + off) * (size_t)D * esz;
-    store_k8<CACHE>(row, a0, xa, inv);
-    store_k8<CACHE>(row, b0, xb, inv);
+    // K page: blocks of 32 dims, [dim/32][slot][32]
+    uint8_t *kph = (uint8_t *)a.cache.k_pages + ph * P * (size_t)D * esz;
+    store_k8<CACHE>(kph + ((size_t)(a0 >> 5) * P + off) * 32 * esz, a0 & 31, xa);
+    store_k8<CACHE>(kph + ((size_t)(b0 >> 5) * P + off) * 32 * esz, b0 & 31, xb);
   } else {
     void *col = (uint8_t *)a.cache.v_pages + (ph * D * P + off) * (size_t)esz;
-    store_v8<CACHE>(col, a0, P, xa, inv);
-    store_v8<CACHE>(col, b0, P, xb, inv);
+    store_v8<CACHE>(col, a0, P, xa);
+    store_v8<CACHE>(col, b0, P, xb);
   }
 }
 

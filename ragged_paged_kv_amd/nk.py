@@ -124,13 +124,16 @@ def _i32(t, name):
 class PagedKVCache:
     """One layer's paged cache (device tensors in the layout of nk.h).
 
-    k_pages [num_pages, Hkv, P, D], v_pages [num_pages, Hkv, D, P] (float32,
-    bfloat16 or uint8 e4m3 codes), k_scales/v_scales [num_pages, Hkv, P]
-    float32 for e4m3, page_table [num_seqs, stride] int32.
+    k_pages [num_pages, Hkv, D/32, P, 32], v_pages [num_pages, Hkv, D, P]
+    (float32, bfloat16 or uint8 e4m3 codes), k_scales/v_scales
+    [num_pages, Hkv, P] float32 for e4m3, page_table [num_seqs, stride] int32.
     """
 
     def __init__(self, k_pages, v_pages, page_table, k_scales=None, v_scales=None):
-        n, h, p, d = k_pages.shape
+        n, h, nb, p, blk = k_pages.shape
+        d = nb * 32
+        if blk != 32:
+            raise ValueError("k_pages must be [num_pages, heads, head_dim/32, page_size, 32]")
         if tuple(v_pages.shape) != (n, h, d, p):
             raise ValueError("v_pages must be [num_pages, heads, head_dim, page_size]")
         if k_pages.dtype != v_pages.dtype:

@@ -18,6 +18,7 @@
 """
 
 import math
+import threading
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 
@@ -177,25 +178,32 @@ def make(which):
 
 
 # ---------------------------------------------------------------- casting
+# torch casts run one at a time: the cache is generated from worker threads,
+# and torch is not entered concurrently from them
+_TORCH_LOCK = threading.Lock()
+
+
 def _to_storage(x32, dtype):
     """float32 array -> raw storage array (float32 / uint16 bf16 bits)."""
     if dtype == "f32":
         return np.ascontiguousarray(x32, dtype=np.float32)
     if dtype == "bf16":
-        t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
-        return t.view(torch.int16).numpy().view(np.uint16)
+        with _TORCH_LOCK:
+            t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+            return t.view(torch.int16).numpy().view(np.uint16).copy()
     raise ValueError(dtype)
 
 
 def _fp8_rows(x32):
     """Rows [..., D] float32 -> (codes uint8 [..., D], scale float32 [...])."""
-    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
-    scale = t.abs().amax(dim=-1) / 448.0
-    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
-    y = torch.clamp(t / safe[..., None], -448.0, 448.0)
-    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
-    codes = torch.where(scale[..., None] > 0, codes, torch.zeros_like(codes))
-    return codes.numpy(), scale.numpy().astype(np.float32)
+    with _TORCH_LOCK:
+        t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+        scale = t.abs().amax(dim=-1) / 448.0
+        safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+        y = torch.clamp(t / safe[..., None], -448.0, 448.0)
+        codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+        codes = torch.where(scale[..., None] > 0, codes, torch.zeros_like(codes))
+        return codes.numpy().copy(), scale.numpy().astype(np.float32)
 
 
 def _rms_normalize(x32):
@@ -260,9 +268,10 @@ _SENTINEL = {"f32": (np.float32, np.uint32(0xFFFFFFFF)), "bf16": (np.uint16, np.
 
 def sentinel_cache(w):
     """Empty cache storage: every element the dtype's all-ones NaN pattern,
-    scales NaN.  Returns dict(k_pages, v_pages, k_scales, v_scales)."""
+    scales NaN.  Returns dict(k_pages [pages, heads, D/32, P, 32], v_pages
+    [pages, heads, D, P], k_scales, v_scales [pages, heads, P])."""
     dt, pat = _SENTINEL[w.cache_dtype]
-    kshape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
+    kshape = (w.num_pages, w.num_kv_heads, w.head_dim // 32, w.page_size, 32)
     vshape = (w.num_pages, w.num_kv_heads, w.head_dim, w.page_size)
     if w.cache_dtype == "f32":
         k = np.full(kshape, pat, dtype=np.uint32).view(np.float32)
@@ -290,7 +299,8 @@ def build_cache(w, threads=8):
         slots = np.arange(n)
         pages = w.page_table[s][slots // w.page_size].astype(np.int64)
         offs = slots % w.page_size
-        c["k_pages"][pages, :, offs, :] = K
+        # K pages hold blocks of 32 dims: [page][head][dim/32][slot][32]
+        c["k_pages"][pages, :, :, offs, :] = K.reshape(n, w.num_kv_heads, w.head_dim // 32, 32)
         c["v_pages"][pages, :, :, offs] = V
         if ks is not None:
             c["k_scales"][pages, :, offs] = ks

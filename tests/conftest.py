@@ -12,6 +12,18 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+@pytest.fixture(scope="session", autouse=True)
+def _gpu_runtime_first(request):
+    """In a session that runs GPU tests, bring up the GPU runtime before any
+    test starts worker threads (the input generators use a thread pool)."""
+    if any(item.get_closest_marker("gpu") for item in request.session.items):
+        import torch
+        if torch.cuda.is_available():
+            torch.cuda.init()
+            torch.zeros(1, device="cuda")
+    yield
+
+
 @pytest.fixture(scope="session")
 def golden():
     import json

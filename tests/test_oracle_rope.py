@@ -114,13 +114,13 @@ def _tiny(k):
         order = "identity"
     elif k == 2:
         q_lens, kv_lens = np.array([1, 1, 1]), np.array([17, 3, 40])
-        kw = dict(num_q_heads=8, num_kv_heads=2, head_dim=16, rotary_dim=16, rope_layout="half",
+        kw = dict(num_q_heads=8, num_kv_heads=2, head_dim=32, rotary_dim=32, rope_layout="half",
                   rope_theta=5e5, page_size=16, in_dtype="bf16", cache_dtype="bf16",
                   softmax_scale=0.25, window_left=-1, qk_norm=False, explicit_positions=False)
         order = "permuted"
     elif k == 3:
         q_lens, kv_lens = np.array([3, 20, 9]), np.array([3, 20, 9])
-        kw = dict(num_q_heads=4, num_kv_heads=1, head_dim=16, rotary_dim=16, rope_layout="half",
+        kw = dict(num_q_heads=4, num_kv_heads=1, head_dim=32, rotary_dim=32, rope_layout="half",
                   rope_theta=5e5, page_size=16, in_dtype="bf16", cache_dtype="bf16",
                   softmax_scale=0.25, window_left=-1, qk_norm=False, explicit_positions=True)
         order = "in_order"
@@ -132,7 +132,7 @@ def _tiny(k):
         order = "permuted"
     else:
         q_lens, kv_lens = np.array([1, 1]), np.array([33, 18])
-        kw = dict(num_q_heads=8, num_kv_heads=1, head_dim=16, rotary_dim=16, rope_layout="half",
+        kw = dict(num_q_heads=8, num_kv_heads=1, head_dim=32, rotary_dim=32, rope_layout="half",
                   rope_theta=1e6, page_size=16, in_dtype="bf16", cache_dtype="e4m3",
                   softmax_scale=0.25, window_left=-1, qk_norm=False, explicit_positions=False)
         order = "permuted"
@@ -194,7 +194,7 @@ def test_brute_force_matches_oracle(k):
                         kr = formats.storage_round(np.array(kr), w.cache_dtype).tolist()
                         vr = formats.storage_round(v[t, h], w.cache_dtype).tolist()
                 else:                                            # prior rows, read raw
-                    kr = _values(w.cache_dtype, raw["k_pages"][page, h, off, :])
+                    kr = _values(w.cache_dtype, raw["k_pages"][page, h, :, off, :].reshape(-1))
                     vr = _values(w.cache_dtype, raw["v_pages"][page, h, :, off])
                     if w.cache_dtype == "e4m3":
                         kr = kr * float(raw["k_scales"][page, h, off])
