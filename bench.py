@@ -224,6 +224,41 @@ def load_traffic(kernel_key):
     return rec.get("bytes_per_launch")
 
 
+def _short(name):
+    """Kernel name without namespaces / argument lists, template arguments kept."""
+    n = name.replace("nk::(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0] if "(" in n else n
+
+
+def rocpd_summary(db_path, title, command):
+    """Per-kernel dispatch statistics of a rocprofv3 --kernel-trace database
+    (rocpd SQLite), grouped by kernel and grid; returns the text table."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    rows = con.execute("select name, grid_x, grid_y, grid_z, workgroup_x, vgpr_count, accum_vgpr_count, "
+                       "lds_size, scratch_size, duration from kernels").fetchall()
+    groups = {}
+    for name, gx, gy, gz, wx, vg, ag, lds, scr, dur in rows:
+        key = (_short(name), gx, gy, gz, wx, vg, ag, lds, scr)
+        groups.setdefault(key, []).append(dur / 1000.0)
+    lines = [f"# {title}", f"# command: {command}", "#",
+             "# kernel | grid (threads x,y,z) | block | vgpr+agpr | lds B | scratch B | calls | avg us | min us | max us"]
+    for key, ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        n, gx, gy, gz, wx, vg, ag, lds, scr = key
+        lines.append(f"{n} | {gx},{gy},{gz} | {wx} | {vg}+{ag} | {lds} | {scr} | {len(ds)} | "
+                     f"{sum(ds) / len(ds):.2f} | {min(ds):.2f} | {max(ds):.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def rocpd_counter(db_path, kernel_match, counter):
+    """Average value of a counter over the dispatches of matching kernels."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    vals = [v for name, cn, v in con.execute("select kernel_name, counter_name, value from counters_collection")
+            if kernel_match in name and cn == counter]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
 def _pmc_rows(d):
     import csv
     rows = []
@@ -271,7 +306,39 @@ def main():
     ap.add_argument("--pmc-key", default="decode_bf16")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--copy-only", action="store_true", help="run one plain 1 GiB copy (counter calibration)")
+    ap.add_argument("--rocpd-summary", nargs=3, metavar=("DB", "OUT", "COMMAND"),
+                    help="write the per-kernel table of a rocprofv3 kernel-trace database")
+    ap.add_argument("--rocpd-traffic", nargs=5, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB", "OUT"),
+                    help="HBM bytes per launch of --pmc-kernel from FETCH_SIZE / WRITE_SIZE databases")
     args = ap.parse_args()
+
+    if args.rocpd_summary:
+        db, out, cmd = args.rocpd_summary
+        text = rocpd_summary(db, "rocprofv3 --kernel-trace --stats: per-kernel dispatch durations", cmd)
+        with open(out, "w") as f:
+            f.write(text)
+        print(text)
+        return 0
+    if args.rocpd_traffic:
+        fdb, wdb, cfdb, cwdb, out = args.rocpd_traffic
+        kf, nf = rocpd_counter(fdb, args.pmc_kernel, "FETCH_SIZE")
+        kw, nw = rocpd_counter(wdb, args.pmc_kernel, "WRITE_SIZE")
+        cf, _ = rocpd_counter(cfdb, "copyBuffer", "FETCH_SIZE")
+        cw, _ = rocpd_counter(cwdb, "copyBuffer", "WRITE_SIZE")
+        if cf is None:
+            cf, _ = rocpd_counter(cfdb, "elementwise", "FETCH_SIZE")
+            cw, _ = rocpd_counter(cwdb, "elementwise", "WRITE_SIZE")
+        fs = args.copy_bytes / (cf * 1024.0) if cf else None
+        wsf = args.copy_bytes / (cw * 1024.0) if cw else None
+        rec = {"kernel": args.pmc_kernel, "dispatches": [nf, nw], "fetch_kib_per_dispatch": kf,
+               "write_kib_per_dispatch": kw, "copy_bytes": args.copy_bytes, "copy_fetch_kib": cf,
+               "copy_write_kib": cw, "fetch_scale": fs, "write_scale": wsf,
+               "bytes_per_launch": (kf * 1024 * fs + kw * 1024 * wsf) if None not in (kf, kw, fs, wsf) else None,
+               "source_hash": source_hash()}
+        with open(out, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec, indent=1))
+        return 0
 
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, args.copy_bytes, args.pmc_kernel, args.pmc_key)
