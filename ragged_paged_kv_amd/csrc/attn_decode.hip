@@ -38,13 +38,22 @@
 // Pages in flight per wave and the waves-per-SIMD the register allocation
 // aims for (compile-time; chosen by measurement on MI355X).
 #ifndef NK_DECODE_NPF_BF16
-#define NK_DECODE_NPF_BF16 4
+#define NK_DECODE_NPF_BF16 3
 #endif
 #ifndef NK_DECODE_NPF_FP8
 #define NK_DECODE_NPF_FP8 6
 #endif
 #ifndef NK_DECODE_WAVES_PER_EU
 #define NK_DECODE_WAVES_PER_EU 2
+#endif
+// K/V pages are read once per call: non-temporal loads keep them from
+// displacing other lines in the caches (measured: +8% for bf16 pages, a
+// small loss for e4m3 pages)
+#ifndef NK_DECODE_NT_BF16
+#define NK_DECODE_NT_BF16 1
+#endif
+#ifndef NK_DECODE_NT_FP8
+#define NK_DECODE_NT_FP8 0
 #endif
 
 namespace nk {
@@ -60,6 +69,17 @@ struct Page {
   VVec v[DT];
   f32x4_t ks, vs;                     // e4m3: scales of this lane's 4 keys
 };
+
+template <bool NT, typename T>
+NK_DEVICE T stream_load(const T *p) {
+  if constexpr (NT) {
+    if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, __builtin_nontemporal_load((const u32x4_t *)p));
+    else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, __builtin_nontemporal_load((const u32x2_t *)p));
+    else return __builtin_bit_cast(T, __builtin_nontemporal_load((const uint32_t *)p));
+  } else {
+    return *p;
+  }
+}
 
 // Per-lane byte offsets inside one page, fixed for the whole kernel.
 struct LaneOffsets {
@@ -89,15 +109,15 @@ NK_DEVICE void load_page(Page<D, FP8> &pg, const nk_paged_kv_t &c, int page, int
   const uint8_t *vpage = (const uint8_t *)c.v_pages + (ph * D * P + sb) * esz;
 #pragma unroll
   for (int kk = 0; kk < PG::KK; ++kk)
-    pg.k[kk] = *(const typename PG::KVec *)(kpage + lo.k + kk * P * 32 * esz);
+    pg.k[kk] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const typename PG::KVec *)(kpage + lo.k + kk * P * 32 * esz));
 #pragma unroll
   for (int dt = 0; dt < PG::DT; ++dt)
-    pg.v[dt] = *(const typename PG::VVec *)(vpage + lo.v + 16 * dt * P * esz);
+    pg.v[dt] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const typename PG::VVec *)(vpage + lo.v + 16 * dt * P * esz));
   if constexpr (FP8) {
     const uint8_t *sk = (const uint8_t *)(c.k_scales + ph * P + sb);
     const uint8_t *sv = (const uint8_t *)(c.v_scales + ph * P + sb);
-    pg.ks = *(const f32x4_t *)(sk + lo.sc);
-    pg.vs = *(const f32x4_t *)(sv + lo.sc);
+    pg.ks = stream_load<NK_DECODE_NT_FP8>((const f32x4_t *)(sk + lo.sc));
+    pg.vs = stream_load<NK_DECODE_NT_FP8>((const f32x4_t *)(sv + lo.sc));
   }
 }
 
@@ -114,11 +134,16 @@ attn_decode_kernel(AttnArgs a) {
   constexpr int KK = PG::KK, DT = PG::DT;
   constexpr int SUB = P / 16;                 // 16-key steps per page
 
+  // linear work index, KV head fastest: the KV heads of one chunk are
+  // dispatched together, so a page's heads (contiguous in memory) are
+  // fetched at the same time
   const int B = a.num_seqs;
-  const int s = blockIdx.x % B;
-  const int c = blockIdx.x / B;
-  const int g = blockIdx.y;
-  const int hb = blockIdx.z;                  // block of 16 query heads
+  const int hkv_ = a.cache.num_kv_heads;
+  const int g = blockIdx.x % hkv_;
+  const int sc = blockIdx.x / hkv_;
+  const int s = sc % B;
+  const int c = sc / B;
+  const int hb = blockIdx.y;                  // block of 16 query heads
   const int lane = threadIdx.x;
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
@@ -287,7 +312,7 @@ hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
   constexpr int NPF = FP8 ? NK_DECODE_NPF_FP8 : (D == 256 ? 2 : NK_DECODE_NPF_BF16);
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
-  dim3 grid((unsigned)(a.num_seqs * a.max_chunks), (unsigned)hkv, (unsigned)((G + 15) / 16));
+  dim3 grid((unsigned)(a.num_seqs * a.max_chunks * hkv), (unsigned)((G + 15) / 16), 1);
   // sub-chunks of 32 steps (512 keys) when the chunk size allows, else 16
   if (a.split_tokens % 512 == 0)
     attn_decode_kernel<D, P, FP8, NPF, 32><<<grid, 64, 0, stream>>>(a);

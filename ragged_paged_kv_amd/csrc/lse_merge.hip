@@ -29,33 +29,68 @@ template <> NK_DEVICE void store2<bf16_t>(bf16_t *p, float a, float b) {
 }
 
 // Merge `n` partials starting at `first` (stride `heads` between chunks) for
-// head `h`; write row `out_row`.
+// head `h`; write row `out_row`.  The chunks' lse values are read by the lanes
+// in parallel (64 at a time), the maximum and the weight sum are wave
+// reductions, and each chunk's weight is broadcast from its lane while the
+// partial outputs stream in four chunks at a time.
 template <typename TOut>
 NK_DEVICE void merge_row(const float *__restrict__ po, const float *__restrict__ pl, long long first,
                          int n, int heads, int h, int D, TOut *__restrict__ out_row,
                          float *__restrict__ lse_out) {
   const int lane = threadIdx.x;
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, pl[(first + i) * heads + h]);
-  float tot = 0.f;
-  constexpr int kMaxPairs = 4;                       // D <= 512
+  for (int b = 0; b < n; b += kWave) {
+    const int i = b + lane;
+    if (i < n) M = fmaxf(M, pl[(first + i) * heads + h]);
+  }
+  M = wave_max(M);
+  constexpr int kMaxPairs = 4;                       // D <= 512: two floats per lane per pass
   float acc[2 * kMaxPairs] = {};
+  float tot = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
-      const float li = pl[(first + i) * heads + h];
-      const float w = li == -INFINITY ? 0.f : expf(li - M);
-      tot += w;
-      const float *o = po + ((first + i) * heads + h) * (long long)D;
+    for (int b = 0; b < n; b += kWave) {
+      const int i = b + lane;
+      const float li = i < n ? pl[(first + i) * heads + h] : -INFINITY;
+      const float wl = li == -INFINITY ? 0.f : expf(li - M);     // weight of chunk b + lane
+      tot += wl;
+      const int cnt = min(kWave, n - b);
+      int k = 0;
+      for (; k + 4 <= cnt; k += 4) {
+        float w4[4];
+        f32x2_t v4[4][kMaxPairs];
 #pragma unroll
-      for (int r = 0; r < kMaxPairs; ++r) {
-        const int d = 2 * (lane + r * kWave);
-        if (d < D) {
-          f32x2_t v = *(const f32x2_t *)(o + d);
-          acc[2 * r] = fmaf(w, v[0], acc[2 * r]);
-          acc[2 * r + 1] = fmaf(w, v[1], acc[2 * r + 1]);
+        for (int u = 0; u < 4; ++u) {
+          w4[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k + u));
+          const float *o = po + ((first + b + k + u) * heads + h) * (long long)D;
+#pragma unroll
+          for (int r = 0; r < kMaxPairs; ++r) {
+            const int d = 2 * (lane + r * kWave);
+            v4[u][r] = d < D ? *(const f32x2_t *)(o + d) : f32x2_t{0.f, 0.f};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int r = 0; r < kMaxPairs; ++r) {
+            acc[2 * r] = fmaf(w4[u], v4[u][r][0], acc[2 * r]);
+            acc[2 * r + 1] = fmaf(w4[u], v4[u][r][1], acc[2 * r + 1]);
+          }
+      }
+      for (; k < cnt; ++k) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
+        const float *o = po + ((first + b + k) * heads + h) * (long long)D;
+#pragma unroll
+        for (int r = 0; r < kMaxPairs; ++r) {
+          const int d = 2 * (lane + r * kWave);
+          if (d < D) {
+            const f32x2_t v = *(const f32x2_t *)(o + d);
+            acc[2 * r] = fmaf(w, v[0], acc[2 * r]);
+            acc[2 * r + 1] = fmaf(w, v[1], acc[2 * r + 1]);
+          }
         }
       }
     }
+    tot = wave_sum(tot);
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
