@@ -59,19 +59,37 @@ int max_chunks(int max_kv_len, int window_left, int split) {
 
 bool uses_split(int q_dtype, int cache_dtype) { return q_dtype == NK_BF16 && cache_dtype != NK_F32; }
 
-size_t workspace_bytes(int q_dtype, int cache_dtype, int num_seqs, int max_kv_len, int hq, int hkv,
-                       int head_dim, int window_left, int requested_split, int *split_out,
-                       int *chunks_out) {
-  const int split = split_tokens(num_seqs, max_kv_len, hq, hkv, head_dim, window_left, requested_split);
-  const int chunks = max_chunks(max_kv_len, window_left, split);
-  if (split_out) *split_out = split;
-  if (chunks_out) *chunks_out = chunks;
-  if (!uses_split(q_dtype, cache_dtype) || chunks <= 1) return 0;
-  const size_t slots = (size_t)num_seqs * chunks;
-  size_t bytes = slots * hq * head_dim * sizeof(float);       // partial outputs
-  bytes = (bytes + 255) / 256 * 256;
-  bytes += slots * hq * sizeof(float);                           // partial lse
-  return (bytes + 255) / 256 * 256;
+// Workspace: the split-KV partials of decode rows (when a row spans several
+// chunks), then the prefill work list (when any row block may be a prefill
+// one), each 256-byte aligned.
+struct WorkspacePlan {
+  int split = 0, chunks = 1;
+  size_t part_lse = 0, sched = 0, total = 0;
+  bool partials = false, prefill = false;
+};
+
+WorkspacePlan plan_workspace(int q_dtype, int cache_dtype, int num_seqs, int total_q, int max_q_len,
+                             int max_kv_len, int hq, int hkv, int head_dim, int window_left,
+                             int requested_split) {
+  WorkspacePlan w;
+  w.split = split_tokens(num_seqs, max_kv_len, hq, hkv, head_dim, window_left, requested_split);
+  w.chunks = max_chunks(max_kv_len, window_left, w.split);
+  if (!uses_split(q_dtype, cache_dtype)) return w;
+  size_t off = 0;
+  if (w.chunks > 1) {
+    const size_t slots = (size_t)num_seqs * w.chunks;
+    off = (slots * hq * head_dim * sizeof(float) + 255) / 256 * 256;     // partial outputs
+    w.part_lse = off;
+    off = (off + slots * hq * sizeof(float) + 255) / 256 * 256;          // partial lse
+    w.partials = true;
+  }
+  if (max_q_len > 1) {
+    w.sched = off;
+    off = (off + sched_bytes(num_seqs, total_q) + 255) / 256 * 256;
+    w.prefill = true;
+  }
+  w.total = off;
+  return w;
 }
 
 // ------------------------------------------------------------------ profiling
@@ -185,10 +203,11 @@ size_t nk_ragged_paged_attention_workspace_size(int32_t q_dtype, int32_t cache_d
                                                 int32_t num_q_heads, int32_t num_kv_heads,
                                                 int32_t head_dim, int32_t window_left,
                                                 int32_t kv_split_tokens) {
-  (void)total_q; (void)max_q_len;
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len <= 0) return 0;
-  return workspace_bytes(q_dtype, cache_dtype, num_seqs, max_kv_len, num_q_heads, num_kv_heads,
-                         head_dim, window_left, kv_split_tokens, nullptr, nullptr);
+  if (num_seqs <= 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_kv_len <= 0)
+    return 0;
+  return plan_workspace(q_dtype, cache_dtype, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads,
+                        num_kv_heads, head_dim, window_left, kv_split_tokens).total;
 }
 
 int32_t nk_ragged_paged_attention_split_tokens(int32_t num_seqs, int32_t max_kv_len,
@@ -231,25 +250,25 @@ int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_o
   hipStream_t s = (hipStream_t)stream;
   if (q_dtype == NK_F32) return launch_attn_f32(a, s) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
 
-  int split = 0, chunks = 1;
-  const size_t need = workspace_bytes(q_dtype, cache->dtype, num_seqs, max_kv_len, num_q_heads,
-                                      cache->num_kv_heads, cache->head_dim, window_left,
-                                      kv_split_tokens, &split, &chunks);
-  if (need > 0 && (!workspace || workspace_bytes_given < need)) return NK_ERR_WORKSPACE;
-  a.split_tokens = split;
-  a.max_chunks = chunks;
-  if (need > 0) {
-    const size_t slots = (size_t)num_seqs * chunks;
-    size_t off = slots * num_q_heads * cache->head_dim * sizeof(float);
-    off = (off + 255) / 256 * 256;
+  const WorkspacePlan wp = plan_workspace(q_dtype, cache->dtype, num_seqs, total_q, max_q_len,
+                                         max_kv_len, num_q_heads, cache->num_kv_heads,
+                                         cache->head_dim, window_left, kv_split_tokens);
+  if (wp.total > 0 && (!workspace || workspace_bytes_given < wp.total)) return NK_ERR_WORKSPACE;
+  a.split_tokens = wp.split;
+  a.max_chunks = wp.chunks;
+  if (wp.partials) {
     a.part_out = (float *)workspace;
-    a.part_lse = (float *)((char *)workspace + off);
+    a.part_lse = (float *)((char *)workspace + wp.part_lse);
   }
-  // prefill rows (q_len > 1) and decode rows (q_len == 1) run as two launches
-  // on the same stream; each kernel skips the rows of the other kind
-  if (max_q_len > 1 && launch_attn_prefill(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  if (wp.prefill) {
+    a.sched = (int32_t *)((char *)workspace + wp.sched);
+    a.sched_items_max = sched_items_max(num_seqs, total_q);
+  }
+  // prefill rows (q_len > 1) and decode rows (q_len == 1) run as separate
+  // launches on the same stream; each kernel skips the rows of the other kind
+  if (wp.prefill && launch_attn_prefill(a, s) != hipSuccess) return NK_ERR_DEVICE;
   if (launch_attn_decode(a, s) != hipSuccess) return NK_ERR_DEVICE;
-  if (chunks > 1 && launch_decode_merge(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  if (wp.partials && launch_decode_merge(a, s) != hipSuccess) return NK_ERR_DEVICE;
   return NK_OK;
 }
 

@@ -14,164 +14,139 @@
 //   * a work-group owns BM query rows of one segment and GW query heads of one
 //     KV head (GW * BM/32 = waves; each wave owns 32 rows of one head), so
 //     every K/V tile staged in LDS serves all GW heads;
-//   * KV tiles of 64 keys (four 16-token or two 32-token pages) are gathered
-//     through the page table into LDS with contiguous 16-byte reads: K as
-//     [key][dim] (from the cache's 32-dim blocks), V as [dim][key] (the cache
-//     already stores V dimension-major per page), 16-byte chunks XOR-swizzled
-//     against bank conflicts; e4m3 codes are widened to bf16 on the way in,
-//     their scales kept beside the tile;
-//   * per wave: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 rows),
-//     with K rows read in a permuted key order that makes the score tile's
-//     lane layout the P^T operand layout of the second product
-//     O^T += V^T P^T (32 dims x 32 rows), so probabilities never leave their
-//     lanes;
-//   * online softmax in the exp2 domain with the maximum kept per row in
-//     registers, rescaling the output only when the maximum has grown by more
-//     than 2^8 (results are exact either way: each term is exp2(x - m_used));
-//   * the next tile's global loads are in flight while the current tile is
-//     computed; segments' q-blocks are dispatched heaviest-first, and
-//     consecutive work-groups take the KV heads of one q-block so that the
-//     groups of one KV head land on one XCD (round-robin dispatch) and share
-//     its L2.
+//   * KV tiles of 64 keys (four 16-token or two 32-token pages).  Each page's
+//     K or V block of one head is contiguous in the cache, so a wave's load
+//     instruction reads one contiguous 1 KiB (bf16) piece of one page, at a
+//     scalar page base plus a per-lane offset fixed for the whole kernel;
+//     e4m3 codes are widened to bf16 on the way to LDS, their scales kept
+//     beside the tile;
+//   * LDS rows are padded by 16 bytes (no swizzle): the MFMA operand reads of
+//     8 consecutive lanes hit 8 consecutive rows and so 32 distinct banks,
+//     and every operand address is a per-lane base plus an immediate;
+//   * per wave: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 rows).
+//     K rows sit in LDS in a permuted key order (bits 2 and 3 of the key
+//     swapped) that makes the score tile's lane layout the P^T operand layout
+//     of the second product O^T += V^T P^T (32 dims x 32 rows), so the
+//     probabilities never leave their lanes;
+//   * software pipeline: K runs one tile ahead of V.  While the softmax of
+//     tile t runs on the VALU, the score MFMAs of tile t+1 are in flight;
+//     K and V tiles are double-buffered, the global loads of tiles t+3 (K)
+//     and t+2 (V) are in flight during iteration t, and one barrier per tile
+//     separates the buffers' writers from their readers;
+//   * online softmax in the exp2 domain, one fused multiply-add and one exp
+//     per score; the running maximum is replaced only when the tile's
+//     maximum exceeds it by more than 2^8 (exact either way: each term is
+//     exp2(x - m_used)); the normaliser sums the probabilities as rounded to
+//     bf16 for the P.V product (v_dot2_f32_bf16 on the packed pairs);
+//   * segments' q-blocks are dispatched heaviest-first, and consecutive
+//     work-groups take the KV heads of one q-block so that the groups of one
+//     KV head land on one XCD (round-robin dispatch) and share its L2.
 
 #include "common.h"
 #include "internal.h"
+
+// Scheduling hint for the block that interleaves the next tile's score MFMAs
+// with the exponentials (compile-time choice, measured).
+#ifndef NK_PREFILL_IGLP
+#define NK_PREFILL_IGLP -1
+#endif
+#if NK_PREFILL_IGLP >= 0
+#define NK_PREFILL_SCHED_HINT() __builtin_amdgcn_iglp_opt(NK_PREFILL_IGLP)
+#else
+#define NK_PREFILL_SCHED_HINT() ((void)0)
+#endif
+
+// Waves per work-group for head dims up to 128 (compile-time, measured):
+// 8 = one work-group per CU, 4 = two work-groups per CU whose barriers are
+// independent.
+#ifndef NK_PREFILL_NW
+#define NK_PREFILL_NW 8
+#endif
 
 namespace nk {
 namespace {
 
 constexpr int BN = 64;     // keys per KV tile
 
-// 16-byte slot swizzle of an LDS row: rows of 128 bytes (V^T tiles, D = 64
-// K tiles) pair up in a 256-byte bank window, wider rows span it.
-template <int ROW_BYTES>
-NK_DEVICE int swz(int row, int slot) {
-  if (ROW_BYTES == 128) return slot ^ ((row >> 1) & 7);
-  return slot ^ (row & 15);
+// Key (within a 32-key subtile) held by LDS row r of a K tile: bits 2 and 3
+// of r swapped.  An involution.
+NK_DEVICE constexpr int perm_key(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// Physical key (within a 32-key subtile) that score-tile row rho holds:
-// bits 2 and 3 of rho swapped.
-NK_DEVICE int perm_key(int rho) {
-  return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
-}
+// The page table is read-only while a kernel runs: reading it through the
+// constant address space lets wave-uniform lookups use scalar loads.
+typedef __attribute__((address_space(4))) const int32_t *const_i32_ptr;
 
-template <int D, int P, bool FP8, int NT>
-struct Loader {
-  static constexpr int CH = BN * D / 8;             // chunks per tile (K or V)
-  static constexpr int PER = CH / NT;               // chunks per thread
-  static_assert(CH % NT == 0, "tile chunks must divide over the threads");
-  using Raw = typename std::conditional<FP8, u32x2_t, bf16x8_t>::type;
-  Raw k[PER], v[PER];
-  float ks, vs;                                     // fp8: one key's scales (threads < BN)
-
-  NK_DEVICE void load(const AttnArgs &a, const int32_t *pt, int tile_base, int L, int g, int tid) {
-    const int hkv = a.cache.num_kv_heads;
-    const int last_page = (L - 1) / P;
-    constexpr int esz = FP8 ? 1 : 2;
-    const uint8_t *kb = (const uint8_t *)a.cache.k_pages;
-    const uint8_t *vb = (const uint8_t *)a.cache.v_pages;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NT;
-      // K: chunk c -> (page of the tile, 32-dim block, key in page, 8 dims);
-      // consecutive chunks are consecutive in the page's [dim/32][key][32]
-      {
-        const int e8 = c & 3, rest = c >> 2;
-        const int kip = rest % P, rest2 = rest / P;
-        const int blk = rest2 % (D / 32), pit = rest2 / (D / 32);
-        const int kk = tile_base + pit * P + kip;
-        const int page = pt[min(kk / P, last_page)];
-        const size_t ph = (size_t)page * hkv + g;
-        k[i] = *(const Raw *)(kb + (ph * P * D + ((size_t)blk * P + kip) * 32 + 8 * e8) * esz);
-      }
-      // V: chunk c -> dim c / 8, keys 8*(c % 8) ..
-      {
-        const int d = c / 8, ks8 = c % 8;
-        const int kk = tile_base + 8 * ks8;
-        const int page = pt[min(kk / P, last_page)];
-        v[i] = *(const Raw *)(vb + ((((size_t)page * hkv + g) * D + d) * P + (kk % P)) * esz);
-      }
-    }
-    if (FP8 && tid < BN) {
-      const int kk = tile_base + tid;
-      const int page = pt[min(kk / P, last_page)];
-      const size_t idx = ((size_t)page * hkv + g) * P + (kk % P);
-      ks = a.cache.k_scales[idx];
-      vs = a.cache.v_scales[idx];
-    }
-  }
-
-  // Write to LDS; keys >= L become zeros (their slots may hold anything).
-  NK_DEVICE void store(bf16_t *sk, bf16_t *sv, float *sks, float *svs, int tile_base, int L, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NT;
-      {
-        const int e8 = c & 3, rest = c >> 2;
-        const int kip = rest % P, rest2 = rest / P;
-        const int blk = rest2 % (D / 32), pit = rest2 / (D / 32);
-        const int key = pit * P + kip, slot = blk * 4 + e8;
-        bf16x8_t x;
-        if constexpr (FP8) x = fp8x8_to_bf16x8(k[i]); else x = k[i];
-        if (tile_base + key >= L) x = bf16x8_t{};
-        *(bf16x8_t *)(sk + key * D + 8 * swz<D * 2>(key, slot)) = x;
-      }
-      {
-        const int d = c / 8, ks8 = c % 8;
-        bf16x8_t x;
-        if constexpr (FP8) x = fp8x8_to_bf16x8(v[i]); else x = v[i];
-        const int k0 = tile_base + 8 * ks8;
-        if (k0 + 8 > L) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (k0 + e >= L) x[e] = (bf16_t)0.f;
-        }
-        *(bf16x8_t *)(sv + d * BN + 8 * swz<BN * 2>(d, ks8)) = x;
-      }
-    }
-    if (FP8 && tid < BN) {
-      const bool in = tile_base + tid < L;
-      sks[tid] = in ? ks : 0.f;
-      svs[tid] = in ? vs : 0.f;
-    }
-  }
+template <int D, int P, bool FP8, int NW>
+struct Cfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int KROW = 2 * D + 16;             // bytes per K row (key) in LDS
+  static constexpr int VROW = 2 * BN + 16;            // bytes per V^T row (dim) in LDS
+  static constexpr int KBUF = BN * KROW;
+  static constexpr int VBUF = D * VROW;
+  static constexpr int SBUF = FP8 ? BN * 4 : 0;       // one scale per LDS row
+  static constexpr int V_OFF = 2 * KBUF;
+  static constexpr int KS_OFF = 2 * KBUF + 2 * VBUF;
+  static constexpr int VS_OFF = KS_OFF + 2 * SBUF;
+  static constexpr int LDS = 2 * (KBUF + VBUF + 2 * SBUF);
+  static constexpr int ESZ = FP8 ? 1 : 2;
+  static constexpr int PAGE_CH = D * P / 8;            // 8-element chunks per page block
+  static constexpr int PER = BN * D / 8 / NT;          // chunks per thread per tile (K or V)
+  static constexpr int NPG = BN / P;                   // pages per tile
+  static_assert(PAGE_CH % 64 == 0, "a wave's chunk must lie in one page");
+  static_assert((BN * D / 8) % NT == 0, "tile chunks must divide over the threads");
 };
 
-template <int D, int P, bool FP8, int NWAVES>
-__global__ void __launch_bounds__(NWAVES * 64) attn_prefill_kernel(AttnArgs a, int GW, int max_qb) {
-  constexpr int NT = NWAVES * 64;
+NK_DEVICE uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t v = {(bf16_t)lo, (bf16_t)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// max over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the two
+// 32-lane halves of a register pair, so one of the two outputs holds the
+// partner's value whichever half the lane is in
+NK_DEVICE float halves_max(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+NK_DEVICE float halves_sum(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+NK_DEVICE float dot2_ones(uint32_t pk, float acc) {
+  const bf16x2_t ones = {(bf16_t)1.0f, (bf16_t)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, acc, false);
+}
+
+// One work item: BM query rows (q-block qb) of segment s for the GW query
+// heads of head block hy (KV head hy / HB).  Every thread of the work-group
+// calls it with the same arguments.
+template <int D, int P, bool FP8, int NW>
+NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, uint8_t *lds) {
+  using C = Cfg<D, P, FP8, NW>;
+  constexpr int NT = C::NT;
   constexpr int KD = D / 16;      // k-steps of the score MFMA (16 dims each)
   constexpr int DT = D / 32;      // 32-dim tiles of the output MFMA
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-  bf16_t *sk = (bf16_t *)smem_raw;                       // [BN][D]
-  bf16_t *sv = sk + BN * D;                              // [D][BN]
-  float *sks = (float *)(sv + D * BN);                   // [BN] (e4m3 only)
-  float *svs = sks + BN;
+  constexpr int PER = C::PER;
+  constexpr int NPG = C::NPG;
+  using Raw = typename std::conditional<FP8, u32x2_t, bf16x8_t>::type;
 
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
   const int HB = G / GW;                      // head blocks per KV head
-  const int NH = hkv * HB;
-  const int B = a.num_seqs;
-  const int TB = NWAVES / GW;                 // 32-row blocks per work-group
+  const int TB = NW / GW;                     // 32-row blocks per work-group
   const int BM = 32 * TB;
-
-  // heaviest-first: q-block index descends along the grid; the KV heads of
-  // one q-block are consecutive
-  const long long lin = blockIdx.x;
-  const int hy = (int)(lin % NH);
-  const long long rest = lin / NH;
-  const int s = (int)(rest % B);
-  const int qb = max_qb - 1 - (int)(rest / B);
   const int g = hy / HB;
   const int hblk = hy % HB;
 
   const int q0 = a.q_offsets[s];
   const int q_len = a.q_offsets[s + 1] - q0;
-  if (q_len <= 1) return;
   const int r0 = qb * BM;
-  if (r0 >= q_len) return;
   const int L = a.kv_lens[s];
   const int shift = L - q_len;                // row r sits at position r + shift
   const int r_last = min(r0 + BM, q_len) - 1;
@@ -187,13 +162,12 @@ __global__ void __launch_bounds__(NWAVES * 64) attn_prefill_kernel(AttnArgs a, i
     }
     return;
   }
-  const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int hl = w % GW;
-  const int tb = w / GW;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = wv % GW;
+  const int tb = wv / GW;
   const int head = g * G + hblk * GW + hl;
   const int rw = r0 + 32 * tb;                // wave's first row
   const int qcol = lane & 31;                 // this lane's query row (column of S^T)
@@ -203,137 +177,265 @@ __global__ void __launch_bounds__(NWAVES * 64) attn_prefill_kernel(AttnArgs a, i
   const int my_pos = my_row + shift;
   const int my_lo = a.window_left < 0 ? 0 : max(0, my_pos - a.window_left);
   const int my_hi = min(my_pos, L - 1);
-  // wave key range
-  const int w_rows_last = min(rw + 31, q_len - 1);
+  // the wave's key range (over its valid rows)
   const bool wave_active = rw < q_len;
+  const int w_rows_last = min(rw + 31, q_len - 1);
   const int wk_hi = min(w_rows_last + shift, L - 1);
   const int wk_lo = a.window_left < 0 ? 0 : max(0, rw + shift - a.window_left);
 
-  // Q operand (B of the score product): lane holds Q[row][16kk + 8*half .. +8]
+  // ---- Q operand (B of the score product): lane holds Q[row][16kk + 8*half .. +8].
+  // A negative scale is folded into Q's sign (exact), a zero scale into a
+  // zero Q, so that the exp2-domain factor c2 is positive.
+  float c2 = a.softmax_scale * kLog2e;
+  uint32_t qxor = 0;
+  bool qzero = !row_valid;
+  if (c2 < 0.f) { c2 = -c2; qxor = 0x80008000u; }
+  else if (c2 == 0.f) { c2 = 1.f; qzero = true; }
   bf16x8_t qop[KD];
   {
     const bf16_t *qrow = (const bf16_t *)a.q + ((size_t)(q0 + (row_valid ? my_row : 0)) * a.hq + head) * D;
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
-      bf16x8_t v = *(const bf16x8_t *)(qrow + 16 * kk + 8 * half);
-      qop[kk] = row_valid ? v : bf16x8_t{};
+      u32x4_t v = *(const u32x4_t *)(qrow + 16 * kk + 8 * half);
+      v ^= qxor;
+      if (qzero) v = u32x4_t{};
+      qop[kk] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
-  const float qk_scale = a.softmax_scale * kLog2e;
+  // ---- loader geometry, fixed per thread
+  const int last_page = (L - 1) / P;
+  const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
+  const const_i32_ptr ptc = (const_i32_ptr)pt;
+  const size_t head_bytes = (size_t)P * D * C::ESZ;     // one page's K (or V) block of one head
+  const size_t page_bytes = (size_t)hkv * head_bytes;
+  const uint8_t *kb = (const uint8_t *)a.cache.k_pages + (size_t)g * head_bytes;
+  const uint8_t *vb = (const uint8_t *)a.cache.v_pages + (size_t)g * head_bytes;
+  int pit[PER];                                         // page of the tile (wave-uniform)
+  uint32_t kg[PER], vg[PER], kl[PER], vl[PER], vkey[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * NT;
+    pit[i] = (wv * 64 + i * NT) / C::PAGE_CH;
+    const int w = c % C::PAGE_CH;
+    // K: lanes take consecutive LDS rows; the page block is [dim/32][token][32]
+    const int kslot = w % P, e8 = (w / P) & 3, blk = w / (4 * P);
+    kg[i] = (uint32_t)((blk * P * 32 + perm_key(kslot) * 32 + e8 * 8) * C::ESZ);
+    kl[i] = (uint32_t)((pit[i] * P + kslot) * C::KROW + (blk * 32 + e8 * 8) * 2);
+    // V: the page block is [dim][token]; a chunk is 8 tokens of one dim
+    const int d = w / (P / 8), kq = w % (P / 8);
+    vg[i] = (uint32_t)((d * P + kq * 8) * C::ESZ);
+    vkey[i] = (uint32_t)(pit[i] * P + kq * 8);
+    vl[i] = (uint32_t)(d * C::VROW + vkey[i] * 2);
+  }
+
+  Raw kst[PER], vst[PER];
+  float kss = 0.f, vss = 0.f;                            // e4m3: scales of LDS row tid
+  auto page_of = [&](int tile, int j) -> size_t {
+    return (size_t)(uint32_t)ptc[min(tile * NPG + j, last_page)];
+  };
+  auto scale_index = [&](int tile) -> size_t {          // e4m3, threads < BN
+    const int key = tile * BN + 32 * (tid >> 5) + perm_key(tid & 31);
+    const int page = pt[min(key / P, last_page)];
+    return ((size_t)page * hkv + g) * P + key % P;
+  };
+  // pages of the K tile last requested: the V tile requested one iteration
+  // later is the same tile
+  size_t pgk[PER];
+  auto load_k = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pgk[i] = page_of(tile, pit[i]);
+    __builtin_amdgcn_sched_barrier(0);     // all page lookups in flight together
+#pragma unroll
+    for (int i = 0; i < PER; ++i) kst[i] = *(const Raw *)(kb + pgk[i] * page_bytes + kg[i]);
+    if (FP8 && tid < BN) kss = a.cache.k_scales[scale_index(tile)];
+  };
+  // V of `tile` through the given pages
+  auto load_v = [&](int tile, const size_t (&pg)[PER]) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) vst[i] = *(const Raw *)(vb + pg[i] * page_bytes + vg[i]);
+    if (FP8 && tid < BN) vss = a.cache.v_scales[scale_index(tile)];
+  };
+  auto widen = [&](const Raw &r) -> bf16x8_t {
+    if constexpr (FP8) return fp8x8_to_bf16x8(r); else return r;
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) *(bf16x8_t *)(lds + buf * C::KBUF + kl[i]) = widen(kst[i]);
+    if (FP8 && tid < BN) ((float *)(lds + C::KS_OFF + buf * C::SBUF))[tid] = kss;
+  };
+  // keys >= L become zeros (their slots may hold anything, and 0 * NaN is NaN)
+  auto store_v = [&](int buf, int tile) {
+    const int base = tile * BN;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      bf16x8_t x = widen(vst[i]);
+      if (base + BN > L) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (base + (int)vkey[i] + e >= L) x[e] = (bf16_t)0.f;
+      }
+      *(bf16x8_t *)(lds + C::V_OFF + buf * C::VBUF + vl[i]) = x;
+    }
+    if (FP8 && tid < BN) {
+      const int key = base + 32 * (tid >> 5) + perm_key(tid & 31);
+      ((float *)(lds + C::VS_OFF + buf * C::SBUF))[tid] = key < L ? vss : 0.f;
+    }
+  };
+
+  // ---- MFMA operand bases: per-lane base plus immediates
+  const uint8_t *klane = lds + qcol * C::KROW + 16 * half;
+  const uint8_t *vlane = lds + C::V_OFF + qcol * C::VROW + 16 * half;
+
+  auto scores = [&](int buf, f32x16_t (&sc)[2]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      sc[st] = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        const bf16x8_t kop = *(const bf16x8_t *)(klane + buf * C::KBUF + st * 32 * C::KROW + 32 * kk);
+        sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], sc[st], 0, 0, 0);
+      }
+    }
+  };
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
 
-  Loader<D, P, FP8, NT> ld;
-  const int t_first = kmin_wg / BN, t_last = kmax_wg / BN;
-  ld.load(a, pt, t_first * BN, L, g, tid);
-
-  for (int t = t_first; t <= t_last; ++t) {
-    const int tile_base = t * BN;
-    __syncthreads();
-    ld.store(sk, sv, sks, svs, tile_base, L, tid);
-    __syncthreads();
-    if (t < t_last) ld.load(a, pt, (t + 1) * BN, L, g, tid);
-
-    if (!wave_active || tile_base > wk_hi || tile_base + BN - 1 < wk_lo) continue;
-
-    // ---- scores S^T for two 32-key subtiles
-    f32x16_t sacc[2];
+  // Softmax of the score tile `sc` (tile `tile`, V in buffer `vbuf`) and the
+  // P.V product.  The score MFMAs of the next tile (K buffer `kbuf_next`,
+  // into `sn`) are issued once the running maximum is settled, so that they
+  // run under the exponentials.
+  auto softmax_pv = [&](bool mask, int tile, int vbuf, int kbuf_next, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    const int tile_base = tile * BN;
+    // element v of subtile st holds key tile_base + 32st + 16(v>>3) + 8half + (v&7)
+    if constexpr (FP8) {
+      const float *ks = (const float *)(lds + C::KS_OFF + (tile & 1) * C::SBUF);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      sacc[st] = f32x16_t{};
-      const int key = 32 * st + perm_key(qcol);        // A row = lane % 32
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        const int slot = 2 * kk + half;
-        const bf16x8_t kop = *(const bf16x8_t *)(sk + key * D + 8 * swz<D * 2>(key, slot));
-        sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], sacc[st], 0, 0, 0);
-      }
-    }
-    // element v of subtile st holds key tile_base + 32st + perm_key(rho),
-    // rho = 8*(v/4) + 4*half + v%4
-    float x[32];
-    const bool need_mask = tile_base + BN - 1 > rw + shift || tile_base + BN > L ||
-                           (a.window_left >= 0 && tile_base < w_rows_last + shift - a.window_left) ||
-                           !row_valid || rw + 31 >= q_len;
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t k4 = *(const f32x4_t *)(ks + 32 * st + 8 * j + 4 * half);
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float xv = sacc[st][v] * qk_scale;
-        if (FP8) {
-          const int key = 32 * st + perm_key(8 * (v >> 2) + 4 * half + (v & 3));
-          xv *= sks[key];
+          for (int r = 0; r < 4; ++r) sc[st][4 * j + r] *= k4[r];
         }
-        x[16 * st + v] = xv;
-      }
-    if (need_mask) {
+    }
+    if (mask) {
+      const int rel_hi = row_valid ? my_hi - tile_base - 8 * half : -1000000;
+      const int rel_lo = my_lo - tile_base - 8 * half;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = tile_base + 32 * st + perm_key(8 * (v >> 2) + 4 * half + (v & 3));
-          if (!row_valid || key < my_lo || key > my_hi) x[16 * st + v] = -INFINITY;
+          const int kv = 32 * st + 16 * (v >> 3) + (v & 7);
+          if (kv > rel_hi || kv < rel_lo) sc[st][v] = -INFINITY;
         }
     }
-    float tmax = x[0];
+    float tmax = sc[0][0];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, x[i]);
-    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
-    // lazy rescale: keep the used maximum unless the new one exceeds it by 8
-    const bool grow = tmax > m_run + 8.f || (m_run == -INFINITY && tmax != -INFINITY);
+    for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, sc[i >> 4][i & 15]);
+    tmax = halves_max(tmax);
+    const float tm = tmax * c2;
+    const bool grow = tm > m_run + 8.f;
     if (__any(grow)) {
-      const float m_new = grow ? tmax : m_run;
-      const float corr = (m_run == -INFINITY || !grow) ? (grow ? 0.f : 1.f) : fast_exp2(m_run - m_new);
+      const float m_new = grow ? tm : m_run;
+      const float corr = grow ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
       l_run *= corr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
       m_run = m_new;
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float p[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) p[i] = fast_exp2(x[i] - m_use);
-    if (FP8) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) l_run += p[i];
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
+    scores(kbuf_next, sn);
+    NK_PREFILL_SCHED_HINT();
+    uint32_t pk[16];
+    if constexpr (FP8) {
+      const float *vs = (const float *)(lds + C::VS_OFF + vbuf * C::SBUF);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = 32 * st + perm_key(8 * (v >> 2) + 4 * half + (v & 3));
-          p[16 * st + v] *= svs[key];
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t v4 = *(const f32x4_t *)(vs + 32 * st + 8 * j + 4 * half);
+          float p[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = fast_exp2(fmaf(sc[st][4 * j + r], c2, nm));
+            l_run += p[r];
+          }
+          pk[8 * st + 2 * j] = pack_bf16(p[0] * v4[0], p[1] * v4[1]);
+          pk[8 * st + 2 * j + 1] = pack_bf16(p[2] * v4[2], p[3] * v4[3]);
         }
     } else {
-      // the normaliser sums the probabilities as the P.V product sees them
-      // (rounded to bf16), so the weights stay self-consistent: a dominant
-      // key reproduces its value row exactly even when p is up to 2^8
+      float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        p[i] = (float)(bf16_t)p[i];
-        l_run += p[i];
+      for (int j = 0; j < 16; ++j) {
+        const int st = j >> 3, v = 2 * (j & 7);
+        pk[j] = pack_bf16(fast_exp2(fmaf(sc[st][v], c2, nm)), fast_exp2(fmaf(sc[st][v + 1], c2, nm)));
+        if (j & 1) l1 = dot2_ones(pk[j], l1); else l0 = dot2_ones(pk[j], l0);
       }
+      l_run += l0 + l1;
     }
     // ---- O^T += V^T P^T over four 16-key chunks
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      bf16x8_t pop;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pop[e] = (bf16_t)p[16 * (c >> 1) + 8 * (c & 1) + e];
+      const int b = 8 * (c >> 1) + 4 * (c & 1);
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[b], pk[b + 1], pk[b + 2], pk[b + 3]});
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + qcol;                  // A row = lane % 32
-        const int slot = 2 * c + half;                 // keys 16c + 8*half ..
-        const bf16x8_t vop = *(const bf16x8_t *)(sv + d * BN + 8 * swz<BN * 2>(d, slot));
+        const bf16x8_t vop = *(const bf16x8_t *)(vlane + vbuf * C::VBUF + dt * 32 * C::VROW + 32 * c);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, o[dt], 0, 0, 0);
       }
     }
+  };
+
+  const int t0 = kmin_wg / BN, t1 = kmax_wg / BN;
+  // One pipeline iteration for tile t: S(t) is in sc, S(t+1) goes to sn
+  // (past the last tile it reads a stale buffer and is never used).  The
+  // loads of K(t+2) and V(t+1) are issued first and land in LDS at the end of
+  // the iteration, so no load is in flight across the loop edge.
+  auto iterate = [&](int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    const int tile_base = t * BN;
+    const bool more_k = t + 2 <= t1, more_v = t + 1 <= t1;
+    size_t pgv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pgv[i] = pgk[i];
+    if (more_k) load_k(t + 2);
+    if (more_v) load_v(t + 1, pgv);
+    const bool act = wave_active && tile_base <= wk_hi && tile_base + BN - 1 >= wk_lo;
+    const bool msk = tile_base + BN - 1 > rw + shift ||
+                     (a.window_left >= 0 && tile_base < w_rows_last + shift - a.window_left);
+    if (act) softmax_pv(msk, t, t & 1, (t + 1) & 1, sc, sn);
+    else scores((t + 1) & 1, sn);
+    // K(t+2) replaces K(t), V(t+1) replaces V(t-1)
+    if (more_k) store_k(t & 1);
+    if (more_v) store_v((t + 1) & 1, t + 1);
+    __syncthreads();
+  };
+
+  // ---- prologue: K(t0), V(t0), K(t0+1) in LDS; S(t0)
+  f32x16_t sa[2], sb[2];
+  load_k(t0);
+  load_v(t0, pgk);
+  store_k(t0 & 1);
+  store_v(t0 & 1, t0);
+  if (t0 + 1 <= t1) {
+    load_k(t0 + 1);
+    store_k((t0 + 1) & 1);
+  }
+  __syncthreads();
+  scores(t0 & 1, sa);
+  __syncthreads();          // K(t0)'s buffer is rewritten in the first iteration
+
+  for (int t = t0; t <= t1; t += 2) {
+    iterate(t, sa, sb);
+    if (t + 1 > t1) break;
+    iterate(t + 1, sb, sa);
   }
 
   if (!wave_active) return;
-  l_run += shfl_xor_f32(l_run, 32);
+  l_run = halves_sum(l_run);
   if (!row_valid) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   bf16_t *orow = (bf16_t *)a.out + ((size_t)(q0 + my_row) * a.hq + head) * D;
@@ -351,29 +453,198 @@ __global__ void __launch_bounds__(NWAVES * 64) attn_prefill_kernel(AttnArgs a, i
     a.lse[(size_t)(q0 + my_row) * a.hq + head] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
 }
 
+// Key tiles a work item visits (0 when none of its rows sees a key); the
+// same bounds as prefill_item.
+NK_DEVICE int item_tiles(const AttnArgs &a, int BM, int s, int qb) {
+  const int q0 = a.q_offsets[s];
+  const int q_len = a.q_offsets[s + 1] - q0;
+  const int L = a.kv_lens[s];
+  const int shift = L - q_len;
+  const int r0 = qb * BM;
+  const int r_last = min(r0 + BM, q_len) - 1;
+  const int kmax = min(r_last + shift, L - 1);
+  const int kmin = a.window_left < 0 ? 0 : max(0, r0 + shift - a.window_left);
+  return (kmax < kmin || L <= 0) ? 0 : kmax / BN - kmin / BN + 1;
+}
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 4096;        // work classes (tiles, capped)
+
+// Exclusive prefix sum over the work-group (kPlanThreads threads); *total
+// receives the sum.  `part` holds one int per wave.
+NK_DEVICE int block_exclusive_scan(int v, int *part, int *total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) part[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int p = lane < kPlanThreads / 64 ? part[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int y = __shfl_up(p, d, kWave);
+      if (lane >= d) p += y;
+    }
+    if (lane < kPlanThreads / 64) part[lane] = p;          // inclusive wave totals
+  }
+  __syncthreads();
+  const int before = (w > 0 ? part[w - 1] : 0) + x - v;
+  *total = part[kPlanThreads / 64 - 1];
+  __syncthreads();                                          // part is reused by the next call
+  return before;
+}
+
+NK_DEVICE int segment_of_item(const int32_t *segoff, int num_seqs, int i) {
+  int lo = 0, hi = num_seqs - 1;                            // last s with segoff[s] <= i
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segoff[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Builds the prefill work list: every (segment, q-block) of the segments
+// with more than one row, ordered by the key tiles it visits, most first
+// (a counting sort; equal classes in any order), and zeroes the queue
+// counters.  One work-group.
+__global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, int BM) {
+  __shared__ int hist[kPlanBins];
+  __shared__ int part[kPlanThreads / 64];
+  int32_t *sc = a.sched;
+  int32_t *segoff = sc + kSchedSegOff;
+  int2 *items = (int2 *)(sc + sched_items_offset(a.num_seqs));
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPlanBins; i += kPlanThreads) hist[i] = 0;
+  if (tid < kSchedQueues) sc[tid * kSchedCounterStride] = 0;
+
+  int base = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
+    const int s = c0 + tid;
+    int n = 0;
+    if (s < a.num_seqs) {
+      const int q_len = a.q_offsets[s + 1] - a.q_offsets[s];
+      n = q_len > 1 ? (q_len + BM - 1) / BM : 0;
+    }
+    int tot;
+    const int ex = block_exclusive_scan(n, part, &tot);
+    if (s < a.num_seqs) segoff[s] = base + ex;
+    base += tot;
+  }
+  const int n_items = min(base, a.sched_items_max);
+  if (tid == 0) { segoff[a.num_seqs] = base; sc[kSchedCount] = n_items; }
+  __syncthreads();
+
+  for (int i = tid; i < n_items; i += kPlanThreads) {
+    const int s = segment_of_item(segoff, a.num_seqs, i);
+    const int w = item_tiles(a, BM, s, i - segoff[s]);
+    atomicAdd(&hist[kPlanBins - 1 - min(w, kPlanBins - 1)], 1);
+  }
+  __syncthreads();
+  {
+    // bins ascend as work descends; 4 bins per thread
+    int v[kPlanBins / kPlanThreads], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanBins / kPlanThreads; ++j) { v[j] = hist[tid * (kPlanBins / kPlanThreads) + j]; sum += v[j]; }
+    int tot;
+    int run = block_exclusive_scan(sum, part, &tot);
+#pragma unroll
+    for (int j = 0; j < kPlanBins / kPlanThreads; ++j) {
+      hist[tid * (kPlanBins / kPlanThreads) + j] = run;
+      run += v[j];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_items; i += kPlanThreads) {
+    const int s = segment_of_item(segoff, a.num_seqs, i);
+    const int qb = i - segoff[s];
+    const int w = item_tiles(a, BM, s, qb);
+    const int pos = atomicAdd(&hist[kPlanBins - 1 - min(w, kPlanBins - 1)], 1);
+    items[pos] = int2{s, qb};
+  }
+}
+
+// Persistent prefill: each work-group takes work units from its queue until
+// the queue is empty.  Queue q serves the work-groups with blockIdx % NQ == q
+// (one queue per XCD under round-robin dispatch, so that the head blocks of
+// one queue share that XCD's L2); a unit is (item, head block).
+template <int D, int P, bool FP8, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int unit_slot;
+  const int hkv = a.cache.num_kv_heads;
+  const int NH = hkv * (a.hq / hkv / GW);       // head blocks per item
+  const int NHq = NH / NQ;                      // of them in this queue
+  const int q = blockIdx.x % NQ;
+  int32_t *ctr = a.sched + q * kSchedCounterStride;
+  const int2 *items = (const int2 *)(a.sched + sched_items_offset(a.num_seqs));
+  const long long units = (long long)a.sched[kSchedCount] * NHq;
+  if (threadIdx.x == 0) unit_slot = atomicAdd(ctr, 1);
+  __syncthreads();
+  int u = unit_slot;
+  while (u < units) {
+    __syncthreads();                            // every thread has read unit_slot
+    int next = 0;
+    if (threadIdx.x == 0) next = atomicAdd(ctr, 1);   // in flight while the item runs
+    const int2 it = items[u / NHq];
+    prefill_item<D, P, FP8, NW>(a, GW, it.x, it.y, q + NQ * (u % NHq), lds);
+    if (threadIdx.x == 0) unit_slot = next;
+    __syncthreads();
+    u = unit_slot;
+  }
+}
+
+struct DeviceShape { int cus = 0; };
+DeviceShape &device_shape(int dev) {
+  static DeviceShape shapes[64];
+  return shapes[dev & 63];
+}
+
 template <int D, int P, bool FP8>
 hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
-  constexpr int NWAVES = D == 256 ? 4 : 8;
+  constexpr int NW = D == 256 ? 4 : NK_PREFILL_NW;
+  using C = Cfg<D, P, FP8, NW>;
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
   int GW = 1;                                  // heads per work-group: power of 2 dividing G
-  while (GW * 2 <= NWAVES && G % (GW * 2) == 0) GW *= 2;
-  const int BM = 32 * (NWAVES / GW);
-  const int max_qb = (a.max_q_len + BM - 1) / BM;
-  const long long grid = (long long)max_qb * a.num_seqs * hkv * (G / GW);
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const size_t lds = (size_t)2 * BN * D * sizeof(bf16_t) + (FP8 ? 2 * BN * sizeof(float) : 0);
-  auto kern = attn_prefill_kernel<D, P, FP8, NWAVES>;
-  if (lds > 65536) {
-    static bool attr_set = false;     // idempotent; a race only repeats the call
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  while (GW * 2 <= NW && G % (GW * 2) == 0) GW *= 2;
+  const int BM = 32 * (NW / GW);
+  const int NH = hkv * (G / GW);
+  const int NQ = NH % kSchedQueues == 0 ? kSchedQueues : 1;
+  if (!a.sched) return hipErrorInvalidValue;
+  auto kern = attn_prefill_kernel<D, P, FP8, NW>;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static int per_cu[64];                       // resident work-groups per CU, per device
+  int &res = per_cu[dev & 63];
+  if (res == 0) {                              // idempotent; a race only repeats the queries
+    if (C::LDS > 65536) {
+      e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
       if (e != hipSuccess) return e;
-      attr_set = true;
     }
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NW * 64, C::LDS);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidConfiguration;
+    res = n;
   }
-  kern<<<(unsigned)grid, NWAVES * 64, lds, stream>>>(a, GW, max_qb);
+  DeviceShape &ds = device_shape(dev);
+  if (ds.cus == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    ds.cus = cus;
+  }
+  // enough work-groups to fill every CU, at least one per queue
+  int grid = ds.cus * res;
+  grid = (grid + NQ - 1) / NQ * NQ;
+  prefill_plan_kernel<<<1, kPlanThreads, 0, stream>>>(a, BM);
+  kern<<<grid, NW * 64, C::LDS, stream>>>(a, GW, NQ);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Launch descriptors shared between the C-ABI layer (api.hip) and the
-// kernel files.  Host-side only types plus the launcher prototypes.
+// kernel files: argument structs, the workspace layout of the prefill work
+// list, and the launcher prototypes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,7 +36,25 @@ struct AttnArgs {
   int32_t max_chunks;       // chunks per decode row (upper bound)
   float *part_out;          // [num_seqs * max_chunks][hq][D]
   float *part_lse;          // [num_seqs * max_chunks][hq]
+  // prefill work list (workspace): queue counters, item count, per-segment
+  // item offsets and the (segment, q-block) items, heaviest first
+  int32_t *sched;
+  int32_t sched_items_max;
 };
+
+// Prefill schedule layout inside the workspace (int32 offsets).
+constexpr int kSchedQueues = 8;               // one work queue per XCD
+constexpr int kSchedCounterStride = 32;       // one 128-byte line per counter
+constexpr int kSchedCount = kSchedQueues * kSchedCounterStride;   // item count
+constexpr int kSchedSegOff = kSchedCount + 64;                    // [num_seqs + 1]
+__host__ __device__ inline size_t sched_items_offset(int num_seqs) {                  // int2 items
+  return ((size_t)kSchedSegOff + num_seqs + 1 + 63) / 64 * 64;
+}
+// q-blocks of a prefill batch: at most one per 32 rows plus one per segment
+__host__ __device__ inline int sched_items_max(int num_seqs, int total_q) { return total_q / 32 + num_seqs + 1; }
+__host__ __device__ inline size_t sched_bytes(int num_seqs, int total_q) {
+  return (sched_items_offset(num_seqs) + 2 * (size_t)sched_items_max(num_seqs, total_q)) * 4;
+}
 
 // Each launcher enqueues its kernel(s) on `stream` and returns a
 // hipError_t (hipSuccess when the launch was accepted).
