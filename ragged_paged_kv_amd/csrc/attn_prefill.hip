@@ -62,6 +62,10 @@
 #ifndef NK_PREFILL_NW
 #define NK_PREFILL_NW 8
 #endif
+// LDS operand reads in flight ahead of the MFMA that consumes them
+#ifndef NK_PREFILL_LDS_AHEAD
+#define NK_PREFILL_LDS_AHEAD 4
+#endif
 
 namespace nk {
 namespace {
@@ -85,11 +89,10 @@ struct Cfg {
   static constexpr int VROW = 2 * BN + 16;            // bytes per V^T row (dim) in LDS
   static constexpr int KBUF = BN * KROW;
   static constexpr int VBUF = D * VROW;
-  static constexpr int SBUF = FP8 ? BN * 4 : 0;       // one scale per LDS row
+  static constexpr int SBUF = FP8 ? BN * 4 : 0;       // K scales, one per LDS row
   static constexpr int V_OFF = 2 * KBUF;
   static constexpr int KS_OFF = 2 * KBUF + 2 * VBUF;
-  static constexpr int VS_OFF = KS_OFF + 2 * SBUF;
-  static constexpr int LDS = 2 * (KBUF + VBUF + 2 * SBUF);
+  static constexpr int LDS = 2 * (KBUF + VBUF + SBUF);
   static constexpr int ESZ = FP8 ? 1 : 2;
   static constexpr int PAGE_CH = D * P / 8;            // 8-element chunks per page block
   static constexpr int PER = BN * D / 8 / NT;          // chunks per thread per tile (K or V)
@@ -230,17 +233,13 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
   }
 
   Raw kst[PER], vst[PER];
-  float kss = 0.f, vss = 0.f;                            // e4m3: scales of LDS row tid
+  f32x4_t vsc[PER][2];                                  // e4m3: the scales of a V chunk's 8 keys
+  float kss = 0.f;                                      // e4m3: K scale of LDS row tid
   auto page_of = [&](int tile, int j) -> size_t {
     return (size_t)(uint32_t)ptc[min(tile * NPG + j, last_page)];
   };
-  auto scale_index = [&](int tile) -> size_t {          // e4m3, threads < BN
-    const int key = tile * BN + 32 * (tid >> 5) + perm_key(tid & 31);
-    const int page = pt[min(key / P, last_page)];
-    return ((size_t)page * hkv + g) * P + key % P;
-  };
-  // pages of the K tile last requested: the V tile requested one iteration
-  // later is the same tile
+  // pages of the K tile last requested: the V tile requested one step later
+  // is the same tile
   size_t pgk[PER];
   auto load_k = [&](int tile) {
 #pragma unroll
@@ -248,28 +247,47 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
     __builtin_amdgcn_sched_barrier(0);     // all page lookups in flight together
 #pragma unroll
     for (int i = 0; i < PER; ++i) kst[i] = *(const Raw *)(kb + pgk[i] * page_bytes + kg[i]);
-    if (FP8 && tid < BN) kss = a.cache.k_scales[scale_index(tile)];
+    if (FP8 && tid < BN) {
+      const int key = tile * BN + 32 * (tid >> 5) + perm_key(tid & 31);
+      const int page = pt[min(key / P, last_page)];
+      kss = a.cache.k_scales[((size_t)page * hkv + g) * P + key % P];
+    }
   };
   // V of `tile` through the given pages
-  auto load_v = [&](int tile, const size_t (&pg)[PER]) {
+  auto load_v = [&](const size_t (&pg)[PER]) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) vst[i] = *(const Raw *)(vb + pg[i] * page_bytes + vg[i]);
-    if (FP8 && tid < BN) vss = a.cache.v_scales[scale_index(tile)];
-  };
-  auto widen = [&](const Raw &r) -> bf16x8_t {
-    if constexpr (FP8) return fp8x8_to_bf16x8(r); else return r;
+    for (int i = 0; i < PER; ++i) {
+      vst[i] = *(const Raw *)(vb + pg[i] * page_bytes + vg[i]);
+      if constexpr (FP8) {
+        const float *sp = a.cache.v_scales + (pg[i] * hkv + g) * P + (vkey[i] % P);
+        vsc[i][0] = *(const f32x4_t *)sp;
+        vsc[i][1] = *(const f32x4_t *)(sp + 4);
+      }
+    }
   };
   auto store_k = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) *(bf16x8_t *)(lds + buf * C::KBUF + kl[i]) = widen(kst[i]);
+    for (int i = 0; i < PER; ++i) {
+      bf16x8_t x;
+      if constexpr (FP8) x = fp8x8_to_bf16x8(kst[i]); else x = kst[i];
+      *(bf16x8_t *)(lds + buf * C::KBUF + kl[i]) = x;
+    }
     if (FP8 && tid < BN) ((float *)(lds + C::KS_OFF + buf * C::SBUF))[tid] = kss;
   };
-  // keys >= L become zeros (their slots may hold anything, and 0 * NaN is NaN)
+  // e4m3 V enters LDS as bf16(code * scale); keys >= L become zeros (their
+  // slots may hold anything, and 0 * NaN is NaN)
   auto store_v = [&](int buf, int tile) {
     const int base = tile * BN;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      bf16x8_t x = widen(vst[i]);
+      bf16x8_t x;
+      if constexpr (FP8) {
+        const bf16x8_t c = fp8x8_to_bf16x8(vst[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (bf16_t)((float)c[e] * vsc[i][e >> 2][e & 3]);
+      } else {
+        x = vst[i];
+      }
       if (base + BN > L) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -277,42 +295,76 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
       }
       *(bf16x8_t *)(lds + C::V_OFF + buf * C::VBUF + vl[i]) = x;
     }
-    if (FP8 && tid < BN) {
-      const int key = base + 32 * (tid >> 5) + perm_key(tid & 31);
-      ((float *)(lds + C::VS_OFF + buf * C::SBUF))[tid] = key < L ? vss : 0.f;
-    }
   };
 
   // ---- MFMA operand bases: per-lane base plus immediates
   const uint8_t *klane = lds + qcol * C::KROW + 16 * half;
   const uint8_t *vlane = lds + C::V_OFF + qcol * C::VROW + 16 * half;
 
-  auto scores = [&](int buf, f32x16_t (&sc)[2]) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      sc[st] = f32x16_t{};
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        const bf16x8_t kop = *(const bf16x8_t *)(klane + buf * C::KBUF + st * 32 * C::KROW + 32 * kk);
-        sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], sc[st], 0, 0, 0);
-      }
-    }
-  };
-
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
+  f32x16_t sc[2];          // scores S^T of the next tile (two 32-key subtiles)
+  uint32_t pk[16];         // probabilities of the current tile, bf16 pairs
+#pragma unroll
+  for (int j = 0; j < 16; ++j) pk[j] = 0u;
 
-  // Softmax of the score tile `sc` (tile `tile`, V in buffer `vbuf`) and the
-  // P.V product.  The score MFMAs of the next tile (K buffer `kbuf_next`,
-  // into `sn`) are issued once the running maximum is settled, so that they
-  // run under the exponentials.
-  auto softmax_pv = [&](bool mask, int tile, int vbuf, int kbuf_next, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
-    const int tile_base = tile * BN;
-    // element v of subtile st holds key tile_base + 32st + 16(v>>3) + 8half + (v&7)
+  const int t0 = kmin_wg / BN, t1 = kmax_wg / BN;
+  auto active = [&](int t) { return wave_active && t * BN <= wk_hi && t * BN + BN - 1 >= wk_lo; };
+
+  // M(t), t >= t0: S(t+1) = K(t+1) Q^T and O^T += V(t)^T P(t)^T -- MFMA
+  // work only, one straight block (past the last tile S reads a stale
+  // buffer and is never used; P is zero where the wave sees no key of the
+  // tile, and V(t) is a loaded tile, finite).  The LDS operand reads run
+  // NK_PREFILL_LDS_AHEAD MFMAs ahead.
+  auto mfma_step = [&](int t) {
+    const uint8_t *kt = klane + ((t + 1) & 1) * C::KBUF;
+    const uint8_t *vt = vlane + (t & 1) * C::VBUF;
+    auto kop = [&](int i) { return *(const bf16x8_t *)(kt + (i / KD) * 32 * C::KROW + 32 * (i % KD)); };
+    auto vop = [&](int i) { return *(const bf16x8_t *)(vt + (i % DT) * 32 * C::VROW + 32 * (i / DT)); };
+    constexpr int NS = 2 * KD, NP = 4 * DT, AH = NK_PREFILL_LDS_AHEAD;
+    bf16x8_t ring[AH];
+#pragma unroll
+    for (int i = 0; i < AH; ++i) ring[i] = i < NS ? kop(i) : vop(i - NS);
+#pragma unroll
+    for (int i = 0; i < NS + NP; ++i) {
+      const bf16x8_t opnd = ring[i % AH];
+      if (i + AH < NS + NP) ring[i % AH] = i + AH < NS ? kop(i + AH) : vop(i + AH - NS);
+      if (i < NS) {
+        const int st = i / KD, kk = i % KD;
+        sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, qop[kk], kk == 0 ? f32x16_t{} : sc[st], 0, 0, 0);
+      } else {
+        const int c = (i - NS) / DT, dt = (i - NS) % DT, b = 8 * (c >> 1) + 4 * (c & 1);
+        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[b], pk[b + 1], pk[b + 2], pk[b + 3]});
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, pop, o[dt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < AH; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+    }
+#pragma unroll
+    for (int i = 0; i < NS + NP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+      if (i + AH < NS + NP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // V(t): softmax of S(t+1) into P(t+1), with the running maximum and sum
+  // (element v of subtile st holds key 32st + 16(v>>3) + 8half + (v&7) of
+  // the tile) -- VALU work only.  S is dead afterwards and is overwritten in
+  // place.
+  auto softmax_step = [&](int t) {
+    const int tn = t + 1;
+    if (tn > t1 || !active(tn)) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pk[j] = 0u;
+      return;
+    }
+    const int tile_base = tn * BN;
     if constexpr (FP8) {
-      const float *ks = (const float *)(lds + C::KS_OFF + (tile & 1) * C::SBUF);
+      const float *ks = (const float *)(lds + C::KS_OFF + (tn & 1) * C::SBUF);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -322,6 +374,8 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
           for (int r = 0; r < 4; ++r) sc[st][4 * j + r] *= k4[r];
         }
     }
+    const bool mask = tile_base + BN - 1 > rw + shift ||
+                      (a.window_left >= 0 && tile_base < w_rows_last + shift - a.window_left);
     if (mask) {
       const int rel_hi = row_valid ? my_hi - tile_base - 8 * half : -1000000;
       const int rel_lo = my_lo - tile_base - 8 * half;
@@ -348,90 +402,74 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
       m_run = m_new;
     }
     const float nm = m_run == -INFINITY ? 0.f : -m_run;
-    scores(kbuf_next, sn);
-    NK_PREFILL_SCHED_HINT();
-    uint32_t pk[16];
-    if constexpr (FP8) {
-      const float *vs = (const float *)(lds + C::VS_OFF + vbuf * C::SBUF);
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4_t v4 = *(const f32x4_t *)(vs + 32 * st + 8 * j + 4 * half);
-          float p[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[r] = fast_exp2(fmaf(sc[st][4 * j + r], c2, nm));
-            l_run += p[r];
-          }
-          pk[8 * st + 2 * j] = pack_bf16(p[0] * v4[0], p[1] * v4[1]);
-          pk[8 * st + 2 * j + 1] = pack_bf16(p[2] * v4[2], p[3] * v4[3]);
-        }
-    } else {
-      float l0 = 0.f, l1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int st = j >> 3, v = 2 * (j & 7);
-        pk[j] = pack_bf16(fast_exp2(fmaf(sc[st][v], c2, nm)), fast_exp2(fmaf(sc[st][v + 1], c2, nm)));
-        if (j & 1) l1 = dot2_ones(pk[j], l1); else l0 = dot2_ones(pk[j], l0);
-      }
-      l_run += l0 + l1;
+    for (int j = 0; j < 16; ++j) {
+      const int st = j >> 3, v = 2 * (j & 7);
+      pk[j] = pack_bf16(fast_exp2(fmaf(sc[st][v], c2, nm)), fast_exp2(fmaf(sc[st][v + 1], c2, nm)));
+      if (j & 1) l1 = dot2_ones(pk[j], l1); else l0 = dot2_ones(pk[j], l0);
     }
-    // ---- O^T += V^T P^T over four 16-key chunks
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int b = 8 * (c >> 1) + 4 * (c & 1);
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[b], pk[b + 1], pk[b + 2], pk[b + 3]});
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8_t vop = *(const bf16x8_t *)(vlane + vbuf * C::VBUF + dt * 32 * C::VROW + 32 * c);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, o[dt], 0, 0, 0);
-      }
-    }
+    l_run += l0 + l1;
   };
 
-  const int t0 = kmin_wg / BN, t1 = kmax_wg / BN;
-  // One pipeline iteration for tile t: S(t) is in sc, S(t+1) goes to sn
-  // (past the last tile it reads a stale buffer and is never used).  The
-  // loads of K(t+2) and V(t+1) are issued first and land in LDS at the end of
-  // the iteration, so no load is in flight across the loop edge.
-  auto iterate = [&](int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
-    const int tile_base = t * BN;
-    const bool more_k = t + 2 <= t1, more_v = t + 1 <= t1;
+  // L(t): K(t+2) and V(t+1) from the staging registers into LDS (replacing
+  // K(t) and V(t-1)), then request K(t+3) and V(t+2)
+  auto load_step = [&](int t) {
+    if (t + 2 <= t1) store_k(t & 1);
+    if (t + 1 <= t1) store_v((t + 1) & 1, t + 1);
     size_t pgv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) pgv[i] = pgk[i];
-    if (more_k) load_k(t + 2);
-    if (more_v) load_v(t + 1, pgv);
-    const bool act = wave_active && tile_base <= wk_hi && tile_base + BN - 1 >= wk_lo;
-    const bool msk = tile_base + BN - 1 > rw + shift ||
-                     (a.window_left >= 0 && tile_base < w_rows_last + shift - a.window_left);
-    if (act) softmax_pv(msk, t, t & 1, (t + 1) & 1, sc, sn);
-    else scores((t + 1) & 1, sn);
-    // K(t+2) replaces K(t), V(t+1) replaces V(t-1)
-    if (more_k) store_k(t & 1);
-    if (more_v) store_v((t + 1) & 1, t + 1);
-    __syncthreads();
+    if (t + 3 <= t1) load_k(t + 3);
+    if (t + 2 <= t1) load_v(pgv);
   };
 
-  // ---- prologue: K(t0), V(t0), K(t0+1) in LDS; S(t0)
-  f32x16_t sa[2], sb[2];
+  // ---- prologue: K(t0) in LDS; K(t0+1), V(t0) staged
   load_k(t0);
-  load_v(t0, pgk);
   store_k(t0 & 1);
-  store_v(t0 & 1, t0);
-  if (t0 + 1 <= t1) {
-    load_k(t0 + 1);
-    store_k((t0 + 1) & 1);
+  {
+    size_t pgv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pgv[i] = pgk[i];
+    if (t0 + 1 <= t1) load_k(t0 + 1);
+    load_v(pgv);
   }
   __syncthreads();
-  scores(t0 & 1, sa);
-  __syncthreads();          // K(t0)'s buffer is rewritten in the first iteration
 
-  for (int t = t0; t <= t1; t += 2) {
-    iterate(t, sa, sb);
-    if (t + 1 > t1) break;
-    iterate(t + 1, sb, sa);
+  // ---- ping-pong: waves w and w + NW/2 share a SIMD.  Both groups run the
+  // same sequence M(it), barrier, V(it) + L, barrier; group 1 starts one
+  // barrier later, so that between two barriers one wave of each SIMD issues
+  // MFMAs while the other works on the VALU.  M(it) of either group reads
+  // K(it+1) and V(it); the loads of group 0 (L(it), after its V(it)) and of
+  // group 1 (L(it+1), after its V(it), i.e. during group 0's M(it+1)) write
+  // the other buffers.
+  const int grp = wv >= NW / 2 ? 1 : 0;
+  if (grp) {
+    load_step(t0 - 1);
+    __syncthreads();
+  }
+  // M(t0 - 1): S(t0) only (no V tile before t0)
+  {
+    const uint8_t *kt = klane + (t0 & 1) * C::KBUF;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      sc[st] = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+        sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(kt + st * 32 * C::KROW + 32 * kk),
+                                                         qop[kk], sc[st], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  softmax_step(t0 - 1);
+  load_step(t0 - 1 + grp);
+  __syncthreads();
+  for (int it = t0; it <= t1; ++it) {
+    mfma_step(it);
+    __syncthreads();
+    softmax_step(it);
+    load_step(it + grp);
+    if (grp == 0 || it < t1) __syncthreads();
   }
 
   if (!wave_active) return;
@@ -444,10 +482,10 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // values v = 4j..4j+3 are dims 32dt + 8j + 4*half + 0..3
-      bf16x4_t pk;
+      bf16x4_t ov;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pk[r] = (bf16_t)(o[dt][4 * j + r] * inv);
-      *(bf16x4_t *)(orow + 32 * dt + 8 * j + 4 * half) = pk;
+      for (int r = 0; r < 4; ++r) ov[r] = (bf16_t)(o[dt][4 * j + r] * inv);
+      *(bf16x4_t *)(orow + 32 * dt + 8 * j + 4 * half) = ov;
     }
   if (a.lse && half == 0)
     a.lse[(size_t)(q0 + my_row) * a.hq + head] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
