@@ -38,13 +38,17 @@
 // Pages in flight per wave and the waves-per-SIMD the register allocation
 // aims for (compile-time; chosen by measurement on MI355X).
 #ifndef NK_DECODE_NPF_BF16
-#define NK_DECODE_NPF_BF16 3
+#define NK_DECODE_NPF_BF16 4
 #endif
 #ifndef NK_DECODE_NPF_FP8
 #define NK_DECODE_NPF_FP8 6
 #endif
 #ifndef NK_DECODE_WAVES_PER_EU
 #define NK_DECODE_WAVES_PER_EU 2
+#endif
+// 16-key steps that share one softmax update (1 or 2)
+#ifndef NK_DECODE_STEPS_PER_UPDATE
+#define NK_DECODE_STEPS_PER_UPDATE 2
 #endif
 // K/V pages are read once per call: non-temporal loads keep them from
 // displacing other lines in the caches (measured: +8% for bf16 pages, a
@@ -121,6 +125,33 @@ NK_DEVICE void load_page(Page<D, FP8> &pg, const nk_paged_kv_t &c, int page, int
   }
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48), on the VALU: v_permlane16_swap / v_permlane32_swap exchange rows of
+// a register pair, so one of the two outputs holds the partner row's value
+// whichever row the lane is in.
+NK_DEVICE float rows_max(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  u = __builtin_bit_cast(uint32_t, v);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+NK_DEVICE float rows_sum(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  u = __builtin_bit_cast(uint32_t, v);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+NK_DEVICE float dot2_ones(bf16x2_t p, float acc) {
+  const bf16x2_t ones = {(bf16_t)1.0f, (bf16_t)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+}
+
 NK_DEVICE bf16x4_t fp8x4_to_bf16x4(uint32_t w) {
   bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
   bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
@@ -131,6 +162,8 @@ template <int D, int P, bool FP8, int NPF, int CH>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NK_DECODE_WAVES_PER_EU)))
 attn_decode_kernel(AttnArgs a) {
   using PG = Page<D, FP8>;
+  constexpr int NS = (NPF % 2 == 0 && D <= 128) ? NK_DECODE_STEPS_PER_UPDATE : 1;   // steps per softmax update
+  static_assert(CH % NS == 0 && NPF % NS == 0, "steps per update must divide the ring and the sub-chunk");
   constexpr int KK = PG::KK, DT = PG::DT;
   constexpr int SUB = P / 16;                 // 16-key steps per page
 
@@ -184,81 +217,109 @@ attn_decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // step i covers keys cs + 16 i .. +15: page (cs + 16 i) / P, sub-block
-  auto issue = [&](PG &pg, int i) {
-    const int key0 = cs + 16 * min(i, nsteps - 1);   // past the end: reload the last page (cache hit)
-    const int page = pt[key0 / P];
+  // step i covers keys cs + 16 i .. +15: page (cs + 16 i) / P, sub-block.
+  // The page ids of a sub-chunk's steps are fetched with one vector load
+  // (lane j: step base + j) and read back per step into scalar registers.
+  int step_page = 0;
+  auto fetch_pages = [&](int base) {
+    const int i = min(base + (lane % CH), nsteps - 1);   // past the end: the last page (cache hit)
+    step_page = pt[(cs + 16 * i) / P];
+  };
+  auto issue = [&](PG &pg, int i, int j) {
+    const int key0 = cs + 16 * min(i, nsteps - 1);
+    const int page = __builtin_amdgcn_readlane(step_page, j);
     load_page<D, P, FP8>(pg, a.cache, page, SUB == 1 ? 0 : (key0 % P), g, loff);
   };
 
-  auto consume = [&](const PG &pg, int i) {
-    const int kb = cs + 16 * i;
-    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // NS consecutive 16-key steps (pages pg[0..NS-1], steps i..i+NS-1) share
+  // one update of the running maximum; the maximum is replaced only when a
+  // score exceeds it by more than 2^8 (exact either way: each term is
+  // exp2(x - m_used)), and the normaliser sums the probabilities as rounded
+  // to bf16 for the P.V product
+  auto consume = [&](const PG *const *pg, int i) {
+    float x[NS][4];
+    bool edge = false;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bf16x8_t kop;
-      if constexpr (FP8) kop = fp8x8_to_bf16x8(pg.k[kk]); else kop = pg.k[kk];
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sacc, 0, 0, 0);
+    for (int u = 0; u < NS; ++u) {
+      const int kb = cs + 16 * (i + u);
+      f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        bf16x8_t kop;
+        if constexpr (FP8) kop = fp8x8_to_bf16x8(pg[u]->k[kk]); else kop = pg[u]->k[kk];
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sacc, 0, 0, 0);
+      }
+      // lane holds keys kb + 4*lg + r of head column n
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[u][r] = FP8 ? sacc[r] * qk_scale * pg[u]->ks[r] : sacc[r] * qk_scale;
+      edge |= kb < vlo || kb + 16 > ce || i + u >= nsteps;
     }
-    // lane holds keys kb + 4*lg + r of head column n
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = FP8 ? sacc[r] * qk_scale * pg.ks[r] : sacc[r] * qk_scale;
-    const bool edge = kb < vlo || kb + 16 > ce;
     if (edge) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 4 * lg + r;
-        if (key < vlo || key >= ce) x[r] = -INFINITY;
-      }
+      for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = cs + 16 * (i + u) + 4 * lg + r;
+          if (key < vlo || key >= ce) x[u][r] = -INFINITY;
+        }
     }
-    float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f32(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    if (__any(m_new > m_run)) {
-      const float corr = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+    float tmax = x[0][0];
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, x[u][r]);
+    tmax = rows_max(tmax);
+    const bool grow = tmax > m_run + 8.f;
+    if (__any(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float corr = grow ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
       l_run *= corr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = fast_exp2(x[r] - m_use);
-      l_run += p[r];
-    }
-    if constexpr (FP8) {
+    for (int u = 0; u < NS; ++u) {
+      const int kb = cs + 16 * (i + u);
+      float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] *= pg.vs[r];
-    }
-    bf16x4_t pop;
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[u][r] - m_use);
+      bf16x4_t pop;
+      if constexpr (FP8) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pop[r] = (bf16_t)p[r];
-    if (edge) {
-      // masked keys may hold anything (unwritten slots, NaN scales): zero them
+        for (int r = 0; r < 4; ++r) l_run += p[r];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 4 * lg + r;
-        if (key < vlo || key >= ce) pop[r] = (bf16_t)0.f;
+        for (int r = 0; r < 4; ++r) pop[r] = (bf16_t)(p[r] * pg[u]->vs[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pop[r] = (bf16_t)p[r];
+        l_run = dot2_ones(bf16x2_t{pop[0], pop[1]}, l_run);
+        l_run = dot2_ones(bf16x2_t{pop[2], pop[3]}, l_run);
       }
+      if (edge) {
+        // masked keys may hold anything (unwritten slots, NaN scales): zero them
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        bf16x4_t vv;
-        if constexpr (FP8) vv = fp8x4_to_bf16x4(pg.v[dt]); else vv = pg.v[dt];
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb + 4 * lg + r;
+          if (key < vlo || key >= ce) pop[r] = (bf16_t)0.f;
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kb + 4 * lg + r < vlo || kb + 4 * lg + r >= ce) vv[r] = (bf16_t)0.f;
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, pop, o[dt], 0, 0, 0);
-      }
-    } else {
+        for (int dt = 0; dt < DT; ++dt) {
+          bf16x4_t vv;
+          if constexpr (FP8) vv = fp8x4_to_bf16x4(pg[u]->v[dt]); else vv = pg[u]->v[dt];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        bf16x4_t vv;
-        if constexpr (FP8) vv = fp8x4_to_bf16x4(pg.v[dt]); else vv = pg.v[dt];
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, pop, o[dt], 0, 0, 0);
+          for (int r = 0; r < 4; ++r)
+            if (kb + 4 * lg + r < vlo || kb + 4 * lg + r >= ce) vv[r] = (bf16_t)0.f;
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, pop, o[dt], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          bf16x4_t vv;
+          if constexpr (FP8) vv = fp8x4_to_bf16x4(pg[u]->v[dt]); else vv = pg[u]->v[dt];
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, pop, o[dt], 0, 0, 0);
+        }
       }
     }
   };
@@ -270,19 +331,26 @@ attn_decode_kernel(AttnArgs a) {
   // loads re-read the last page, a cache hit).
   for (int sub = 0; sub * CH < nsteps; ++sub) {
     const int base = sub * CH;
+    fetch_pages(base);
     PG ring[NPF];
 #pragma unroll
-    for (int j = 0; j < NPF; ++j) issue(ring[j], base + j);
+    for (int j = 0; j < NPF; ++j) issue(ring[j], base + j, j);
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      if (base + j < nsteps) consume(ring[j % NPF], base + j);
-      if (j + NPF < CH) issue(ring[j % NPF], base + j + NPF);
+    for (int j = 0; j < CH; j += NS) {
+      if (base + j < nsteps) {
+        const PG *pgs[NS];
+#pragma unroll
+        for (int u = 0; u < NS; ++u) pgs[u] = &ring[(j + u) % NPF];
+        consume(pgs, base + j);
+      }
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        if (j + u + NPF < CH) issue(ring[(j + u) % NPF], base + j + u + NPF, j + u + NPF);
     }
   }
 
   // per-column sum over the four lane groups
-  l_run += shfl_xor_f32(l_run, 16);
-  l_run += shfl_xor_f32(l_run, 32);
+  l_run = rows_sum(l_run);
 
   if (!col_valid) return;
   const int head = g * G + hq_local;
@@ -309,7 +377,7 @@ attn_decode_kernel(AttnArgs a) {
 
 template <int D, int P, bool FP8>
 hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
-  constexpr int NPF = FP8 ? NK_DECODE_NPF_FP8 : (D == 256 ? 2 : NK_DECODE_NPF_BF16);
+  constexpr int NPF = D == 256 ? 2 : (FP8 ? NK_DECODE_NPF_FP8 : NK_DECODE_NPF_BF16);
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
   dim3 grid((unsigned)(a.num_seqs * a.max_chunks * hkv), (unsigned)((G + 15) / 16), 1);
