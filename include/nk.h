@@ -45,9 +45,18 @@
  *             (within one page and head, K is stored in blocks of 32
  *             dimensions: block b holds dims 32b..32b+31 of every token of the
  *             page, token after token)
- *   V pages   [num_pages][num_kv_heads][head_dim][page_size]
- *             (within one page and head, V is stored dimension-major: the
- *             page's tokens are contiguous for each dimension)
+ *   V pages   [num_pages][num_kv_heads][page_size/16][head_dim/(16*NV)]
+ *             [64][4*NV], NV = 4 / element bytes (f32 1, bf16 2, e4m3 4):
+ *             within one page and head, each 16-token block is stored as
+ *             runs of 16 bytes.  Run r = 16*g + l of dim group c holds the
+ *             4 tokens 4g..4g+3 (of the block) of the dims 16*(c*NV + j) + l,
+ *             j = 0..NV-1, dim-major within the run: element (dim d, token t)
+ *             of a page is at
+ *               ((t/16) * head_dim/(16*NV) + c) * 64 * 4*NV
+ *               + (16*((t%16)/4) + d%16) * 4*NV + ((d/16)%NV) * 4 + t%4
+ *             with c = (d/16)/NV.  (This is the order in which the 64 lanes
+ *             of a wave hold a V^T operand of the 16x16x16 MFMA, so that one
+ *             16-byte load per lane fetches NV operands.)
  *   scales    [num_pages][num_kv_heads][page_size] float32, K and V apart,
  *             only for NK_E4M3 caches: the stored code times its scale is the
  *             value

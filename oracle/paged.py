@@ -6,9 +6,11 @@ Layout (one layer):
 * K pages  ``[num_pages][num_kv_heads][head_dim/32][page_size][32]`` -- within
   a page, for one head, K is stored in blocks of 32 dimensions: block b holds
   dims 32b..32b+31 of every token of the page, token after token.
-* V pages  ``[num_pages][num_kv_heads][head_dim][page_size]`` -- within a page,
-  for one head, values are stored dimension-major (the page's tokens are
-  contiguous for each dimension).
+* V pages  ``[num_pages][num_kv_heads][page_size/16][head_dim/(16*NV)][64][4*NV]``
+  with NV = 4 / element bytes (f32 1, bf16 2, e4m3 4) -- within a page, for
+  one head, each block of 16 tokens is a sequence of 16-byte runs; run
+  ``16*g + l`` of dim group ``c`` holds tokens ``4g..4g+3`` of the block for
+  the dims ``16*(c*NV + j) + l``, ``j = 0..NV-1`` (dim-major within the run).
 * fp8 scales (K and V separately) ``[num_pages][num_kv_heads][page_size]``.
 * ``page_table[s][p]`` is the physical page holding logical slots
   ``p*page_size .. p*page_size + page_size - 1`` of sequence ``s``.
@@ -69,11 +71,12 @@ class PagedCache:
             raise ValueError("K pages must be [num_pages][heads][head_dim/32][page_size][32]")
         d = nb * 32
         c = cls(dtype, n, h, p, d)
-        if v_pages.shape != (n, h, d, p):
-            raise ValueError("V pages must be [num_pages][heads][head_dim][page_size]")
+        nv = v_run_width(dtype)
+        if tuple(v_pages.shape) != (n, h, p // 16, d // (16 * nv), 64, 4 * nv):
+            raise ValueError("V pages must be [num_pages][heads][page_size/16][head_dim/(16*NV)][64][4*NV]")
         # [n][h][d/32][p][32] -> token-major [n][h][p][d]
         c.k = _decode(dtype, np.transpose(k_pages, (0, 1, 3, 2, 4)).reshape(n, h, p, d))
-        c.v = _decode(dtype, v_pages)
+        c.v = _decode(dtype, v_storage_to_logical(dtype, np.asarray(v_pages)))
         if dtype == "e4m3":
             c.k_scale = np.asarray(k_scales, dtype=np.float32).astype(np.float64)
             c.v_scale = np.asarray(v_scales, dtype=np.float32).astype(np.float64)
@@ -85,7 +88,7 @@ class PagedCache:
         n, h, p, d = self.k.shape
         k = _encode(self.dtype, self.k)
         k = np.ascontiguousarray(np.transpose(k.reshape(n, h, p, d // 32, 32), (0, 1, 3, 2, 4)))
-        v = _encode(self.dtype, self.v)
+        v = v_logical_to_storage(self.dtype, _encode(self.dtype, self.v))
         if self.dtype == "e4m3":
             return k, v, self.k_scale.astype(np.float32), self.v_scale.astype(np.float32)
         return k, v, None, None
@@ -117,6 +120,34 @@ class PagedCache:
             K = K * self.k_scale[pages, :, offs][:, :, None]
             V = V * self.v_scale[pages, :, offs][:, :, None]
         return K, V
+
+
+def v_run_width(dtype):
+    """NV: 16-dim groups per 16-byte V run (4 / element bytes)."""
+    return {"f32": 1, "bf16": 2, "e4m3": 4}[dtype]
+
+
+def v_storage_to_logical(dtype, raw):
+    """[n][h][P/16][D/(16 NV)][64][4 NV] -> [n][h][D][P] (same element type).
+
+    Axes after splitting 64 into (g, l) and 4 NV into (j, t4): token
+    16*sb + 4*g + t4, dim 16*(c*NV + j) + l."""
+    nv = v_run_width(dtype)
+    n, h, nsb, nc, lanes, run = raw.shape
+    if lanes != 64 or run != 4 * nv:
+        raise ValueError("V pages must be [num_pages][heads][page_size/16][head_dim/(16*NV)][64][4*NV]")
+    x = raw.reshape(n, h, nsb, nc, 4, 16, nv, 4)            # n h sb c g l j t4
+    x = np.transpose(x, (0, 1, 3, 6, 5, 2, 4, 7))           # n h c j l sb g t4
+    return x.reshape(n, h, nc * nv * 16, nsb * 16)
+
+
+def v_logical_to_storage(dtype, v):
+    """Inverse of v_storage_to_logical."""
+    nv = v_run_width(dtype)
+    n, h, d, p = v.shape
+    x = v.reshape(n, h, d // (16 * nv), nv, 16, p // 16, 4, 4)   # n h c j l sb g t4
+    x = np.transpose(x, (0, 1, 5, 2, 6, 4, 3, 7))                # n h sb c g l j t4
+    return np.ascontiguousarray(x).reshape(n, h, p // 16, d // (16 * nv), 64, 4 * nv)
 
 
 def _decode(dtype, raw):

@@ -67,10 +67,10 @@ template <int D, bool FP8>
 struct Page {
   static constexpr int KK = D / 32;   // k-steps of the score MFMA
   static constexpr int DT = D / 16;   // d-tiles of the output MFMA
+  static constexpr int NV = FP8 ? 4 : 2;   // d-tiles per 16-byte V run
   using KVec = typename std::conditional<FP8, u32x2_t, bf16x8_t>::type;   // 8 dims of one key
-  using VVec = typename std::conditional<FP8, uint32_t, bf16x4_t>::type;  // 4 keys of one dim
   KVec k[KK];
-  VVec v[DT];
+  u32x4_t v[DT / NV];                 // V runs: this lane's 4 keys of NV d-tiles each
   f32x4_t ks, vs;                     // e4m3: scales of this lane's 4 keys
 };
 
@@ -95,8 +95,21 @@ NK_DEVICE LaneOffsets lane_offsets(int lane) {
   constexpr int esz = FP8 ? 1 : 2;
   const int lr = lane & 15, lg = lane >> 4;
   return LaneOffsets{(uint32_t)((lr * 32 + 8 * lg) * esz),    // K: key lr, dims 8*lg.. of a block
-                     (uint32_t)((lr * P + 4 * lg) * esz),     // V: dim lr, keys 4*lg..
+                     (uint32_t)(16 * lane),                   // V: run `lane` of a dim group
                      (uint32_t)(4 * lg * sizeof(float))};     // scales of keys 4*lg..
+}
+
+NK_DEVICE bf16x4_t fp8x4_to_bf16x4(uint32_t w);
+
+// Operand of d-tile dt (V^T, lane lr + 16 lg: dim 16 dt + lr, keys 4 lg..)
+template <int D, bool FP8>
+NK_DEVICE bf16x4_t v_operand(const Page<D, FP8> &pg, int dt) {
+  if constexpr (FP8) {
+    return fp8x4_to_bf16x4(pg.v[dt >> 2][dt & 3]);
+  } else {
+    const u32x4_t r = pg.v[dt >> 1];
+    return __builtin_bit_cast(bf16x4_t, u32x2_t{r[2 * (dt & 1)], r[2 * (dt & 1) + 1]});
+  }
 }
 
 // Load one 16-key step: the page's base pointer is wave-uniform (scalar
@@ -110,13 +123,15 @@ NK_DEVICE void load_page(Page<D, FP8> &pg, const nk_paged_kv_t &c, int page, int
   const size_t ph = (size_t)page * hkv + g;
   // K page-head: [dim/32][slot][32]; block kk of the 16 keys is contiguous
   const uint8_t *kpage = (const uint8_t *)c.k_pages + (ph * P * D + sb * 32) * esz;
-  const uint8_t *vpage = (const uint8_t *)c.v_pages + (ph * D * P + sb) * esz;
+  // V page-head: 16-key blocks of 16-byte runs in MFMA operand order, one
+  // run per lane and dim group
+  const uint8_t *vpage = (const uint8_t *)c.v_pages + (ph * D * P + sb * D) * esz;
 #pragma unroll
   for (int kk = 0; kk < PG::KK; ++kk)
     pg.k[kk] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const typename PG::KVec *)(kpage + lo.k + kk * P * 32 * esz));
 #pragma unroll
-  for (int dt = 0; dt < PG::DT; ++dt)
-    pg.v[dt] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const typename PG::VVec *)(vpage + lo.v + 16 * dt * P * esz));
+  for (int r = 0; r < PG::DT / PG::NV; ++r)
+    pg.v[r] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const u32x4_t *)(vpage + lo.v + 1024 * r));
   if constexpr (FP8) {
     const uint8_t *sk = (const uint8_t *)(c.k_scales + ph * P + sb);
     const uint8_t *sv = (const uint8_t *)(c.v_scales + ph * P + sb);
@@ -306,8 +321,7 @@ attn_decode_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          bf16x4_t vv;
-          if constexpr (FP8) vv = fp8x4_to_bf16x4(pg[u]->v[dt]); else vv = pg[u]->v[dt];
+          bf16x4_t vv = v_operand<D, FP8>(*pg[u], dt);
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (kb + 4 * lg + r < vlo || kb + 4 * lg + r >= ce) vv[r] = (bf16_t)0.f;
@@ -316,9 +330,7 @@ attn_decode_kernel(AttnArgs a) {
       } else {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          bf16x4_t vv;
-          if constexpr (FP8) vv = fp8x4_to_bf16x4(pg[u]->v[dt]); else vv = pg[u]->v[dt];
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, pop, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand<D, FP8>(*pg[u], dt), pop, o[dt], 0, 0, 0);
         }
       }
     }

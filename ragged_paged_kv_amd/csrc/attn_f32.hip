@@ -71,11 +71,15 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
       const float pi = __shfl(pj, i, kWave);
       const int kk = base + i;
       const int page = pt[kk / P];
-      const float *vcol = vp + ((size_t)page * hkv + g) * D * P + kk % P;
+      // V page-head block in MFMA operand order (one 16-dim tile per
+      // 16-byte run for float32): element (d, t) at
+      // ((t/16)*(D/16) + d/16)*256 + (16*((t%16)/4) + d%16)*4 + t%4
+      const int t = kk % P;
+      const float *vblk = vp + ((size_t)page * hkv + g) * D * P + (t >> 4) * 16 * D + 64 * ((t & 15) >> 2) + (t & 3);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int d = lane + r * kWave;
-        if (d < D) o[r] = fmaf(pi, vcol[(size_t)d * P], o[r]);
+        if (d < D) o[r] = fmaf(pi, vblk[(d >> 4) * 256 + (d & 15) * 4], o[r]);
       }
     }
     m = nm;

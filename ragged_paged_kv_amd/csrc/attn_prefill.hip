@@ -216,6 +216,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
   const uint8_t *vb = (const uint8_t *)a.cache.v_pages + (size_t)g * head_bytes;
   int pit[PER];                                         // page of the tile (wave-uniform)
   uint32_t kg[PER], vg[PER], kl[PER], vl[PER], vkey[PER];
+  constexpr int NV = FP8 ? 4 : 2;                        // 16-dim groups per 16-byte V run
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = tid + i * NT;
@@ -225,15 +226,21 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
     const int kslot = w % P, e8 = (w / P) & 3, blk = w / (4 * P);
     kg[i] = (uint32_t)((blk * P * 32 + perm_key(kslot) * 32 + e8 * 8) * C::ESZ);
     kl[i] = (uint32_t)((pit[i] * P + kslot) * C::KROW + (blk * 32 + e8 * 8) * 2);
-    // V: the page block is [dim][token]; a chunk is 8 tokens of one dim
-    const int d = w / (P / 8), kq = w % (P / 8);
-    vg[i] = (uint32_t)((d * P + kq * 8) * C::ESZ);
-    vkey[i] = (uint32_t)(pit[i] * P + kq * 8);
-    vl[i] = (uint32_t)(d * C::VROW + vkey[i] * 2);
+    // V: the page block is 16-token blocks of 16-byte runs in MFMA operand
+    // order; a chunk (8 elements) is 4 tokens of 2 dims 16 apart: run
+    // R = w * 8 / (4 NV) holds dims 16 (c NV + j) + l of tokens 16 sb + 4 gq..
+    const int e0 = 8 * w, R = e0 / (4 * NV), jq = (e0 % (4 * NV)) / 4;
+    const int runs_per_block = (D / (16 * NV)) * 64;
+    const int sb = R / runs_per_block, rr = R % runs_per_block;
+    const int cg = rr / 64, L = rr % 64, gq = L / 16, l = L % 16;
+    const int dim0 = 16 * (cg * NV + jq) + l;              // and dim0 + 16
+    vg[i] = (uint32_t)(e0 * C::ESZ);
+    vkey[i] = (uint32_t)(pit[i] * P + 16 * sb + 4 * gq);
+    vl[i] = (uint32_t)(dim0 * C::VROW + vkey[i] * 2);
   }
 
   Raw kst[PER], vst[PER];
-  f32x4_t vsc[PER][2];                                  // e4m3: the scales of a V chunk's 8 keys
+  f32x4_t vsc[PER];                                     // e4m3: the scales of a V chunk's 4 keys
   float kss = 0.f;                                      // e4m3: K scale of LDS row tid
   auto page_of = [&](int tile, int j) -> size_t {
     return (size_t)(uint32_t)ptc[min(tile * NPG + j, last_page)];
@@ -259,9 +266,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
     for (int i = 0; i < PER; ++i) {
       vst[i] = *(const Raw *)(vb + pg[i] * page_bytes + vg[i]);
       if constexpr (FP8) {
-        const float *sp = a.cache.v_scales + (pg[i] * hkv + g) * P + (vkey[i] % P);
-        vsc[i][0] = *(const f32x4_t *)sp;
-        vsc[i][1] = *(const f32x4_t *)(sp + 4);
+        vsc[i] = *(const f32x4_t *)(a.cache.v_scales + (pg[i] * hkv + g) * P + (vkey[i] % P));
       }
     }
   };
@@ -280,20 +285,23 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
     const int base = tile * BN;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
+      // elements 0..3: dim dim0, tokens vkey..+3; 4..7: dim dim0 + 16
       bf16x8_t x;
       if constexpr (FP8) {
         const bf16x8_t c = fp8x8_to_bf16x8(vst[i]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (bf16_t)((float)c[e] * vsc[i][e >> 2][e & 3]);
+        for (int e = 0; e < 8; ++e) x[e] = (bf16_t)((float)c[e] * vsc[i][e & 3]);
       } else {
         x = vst[i];
       }
       if (base + BN > L) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (base + (int)vkey[i] + e >= L) x[e] = (bf16_t)0.f;
+          if (base + (int)vkey[i] + (e & 3) >= L) x[e] = (bf16_t)0.f;
       }
-      *(bf16x8_t *)(lds + C::V_OFF + buf * C::VBUF + vl[i]) = x;
+      uint8_t *dst = lds + C::V_OFF + buf * C::VBUF + vl[i];
+      *(bf16x4_t *)dst = bf16x4_t{x[0], x[1], x[2], x[3]};
+      *(bf16x4_t *)(dst + 16 * C::VROW) = bf16x4_t{x[4], x[5], x[6], x[7]};
     }
   };
 

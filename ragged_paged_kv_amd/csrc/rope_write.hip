@@ -97,22 +97,36 @@ template <> NK_DEVICE void store_k8<kCacheE4M3>(void *row, int d0, const double 
   *(u32x2_t *)((uint8_t *)row + d0) = w;
 }
 
-// Store 8 V elements d0..d0+7 into a dimension-major page (stride P).
-template <int CACHE> NK_DEVICE void store_v8(void *col, int d0, int P, const double *x);
-template <> NK_DEVICE void store_v8<kCacheF32>(void *col, int d0, int P, const double *x) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ((float *)col)[(size_t)(d0 + e) * P] = (float)x[e];
+// V page-head block in MFMA operand order (include/nk.h): element (dim d,
+// slot t) sits at v_index(d, t); for 8 consecutive dims of one 16-dim tile
+// the offsets step by 4*NV elements, NV = 4 / element bytes.
+template <int CACHE> constexpr int v_nv() { return CACHE == kCacheF32 ? 1 : (CACHE == kCacheBF16 ? 2 : 4); }
+template <int CACHE> NK_DEVICE size_t v_index(int d, int t, int D) {
+  constexpr int NV = v_nv<CACHE>();
+  const int c = (d >> 4) / NV;
+  return ((size_t)(t >> 4) * (D / (16 * NV)) + c) * (64 * 4 * NV) +
+         (size_t)(16 * ((t & 15) >> 2) + (d & 15)) * (4 * NV) + ((d >> 4) % NV) * 4 + (t & 3);
 }
-template <> NK_DEVICE void store_v8<kCacheBF16>(void *col, int d0, int P, const double *x) {
+
+// Store 8 V elements d0..d0+7 (d0 a multiple of 8) of slot t.
+template <int CACHE> NK_DEVICE void store_v8(void *blk, int d0, int t, int D, const double *x);
+template <> NK_DEVICE void store_v8<kCacheF32>(void *blk, int d0, int t, int D, const double *x) {
+  float *p = (float *)blk + v_index<kCacheF32>(d0, t, D);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ((bf16_t *)col)[(size_t)(d0 + e) * P] = (bf16_t)round_odd_f32(x[e]);
+  for (int e = 0; e < 8; ++e) p[e * 4] = (float)x[e];
 }
-template <> NK_DEVICE void store_v8<kCacheE4M3>(void *col, int d0, int P, const double *x) {
+template <> NK_DEVICE void store_v8<kCacheBF16>(void *blk, int d0, int t, int D, const double *x) {
+  bf16_t *p = (bf16_t *)blk + v_index<kCacheBF16>(d0, t, D);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e * 8] = (bf16_t)round_odd_f32(x[e]);
+}
+template <> NK_DEVICE void store_v8<kCacheE4M3>(void *blk, int d0, int t, int D, const double *x) {
+  uint8_t *p = (uint8_t *)blk + v_index<kCacheE4M3>(d0, t, D);
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
     uint32_t c = fp8x2(x[e], x[e + 1]);
-    ((uint8_t *)col)[(size_t)(d0 + e) * P] = (uint8_t)(c & 0xff);
-    ((uint8_t *)col)[(size_t)(d0 + e + 1) * P] = (uint8_t)(c >> 8);
+    p[e * 16] = (uint8_t)(c & 0xff);
+    p[(e + 1) * 16] = (uint8_t)(c >> 8);
   }
 }
 
@@ -224,9 +238,10 @@ __global__ void __launch_bounds__(256) rope_write_kernel(RopeArgs a) {
     store_k8<CACHE>(kph + ((size_t)(a0 >> 5) * P + off) * 32 * esz, a0 & 31, xa);
     store_k8<CACHE>(kph + ((size_t)(b0 >> 5) * P + off) * 32 * esz, b0 & 31, xb);
   } else {
-    void *col = (uint8_t *)a.cache.v_pages + (ph * D * P + off) * (size_t)esz;
-    store_v8<CACHE>(col, a0, P, xa);
-    store_v8<CACHE>(col, b0, P, xb);
+    // V page: MFMA operand order, see v_index
+    void *blk = (uint8_t *)a.cache.v_pages + ph * D * (size_t)P * esz;
+    store_v8<CACHE>(blk, a0, off, D, xa);
+    store_v8<CACHE>(blk, b0, off, D, xb);
   }
 }
 

@@ -266,13 +266,19 @@ _SENTINEL = {"f32": (np.float32, np.uint32(0xFFFFFFFF)), "bf16": (np.uint16, np.
              "e4m3": (np.uint8, np.uint8(0xFF))}
 
 
+# 16-dim groups per 16-byte V run: 4 / element bytes
+_V_RUN = {"f32": 1, "bf16": 2, "e4m3": 4}
+
+
 def sentinel_cache(w):
     """Empty cache storage: every element the dtype's all-ones NaN pattern,
     scales NaN.  Returns dict(k_pages [pages, heads, D/32, P, 32], v_pages
-    [pages, heads, D, P], k_scales, v_scales [pages, heads, P])."""
+    [pages, heads, P/16, D/(16 NV), 64, 4 NV], k_scales, v_scales
+    [pages, heads, P]); NV = 4 / element bytes."""
     dt, pat = _SENTINEL[w.cache_dtype]
+    nv = _V_RUN[w.cache_dtype]
     kshape = (w.num_pages, w.num_kv_heads, w.head_dim // 32, w.page_size, 32)
-    vshape = (w.num_pages, w.num_kv_heads, w.head_dim, w.page_size)
+    vshape = (w.num_pages, w.num_kv_heads, w.page_size // 16, w.head_dim // (16 * nv), 64, 4 * nv)
     if w.cache_dtype == "f32":
         k = np.full(kshape, pat, dtype=np.uint32).view(np.float32)
         v = np.full(vshape, pat, dtype=np.uint32).view(np.float32)
@@ -301,7 +307,15 @@ def build_cache(w, threads=8):
         offs = slots % w.page_size
         # K pages hold blocks of 32 dims: [page][head][dim/32][slot][32]
         c["k_pages"][pages, :, :, offs, :] = K.reshape(n, w.num_kv_heads, w.head_dim // 32, 32)
-        c["v_pages"][pages, :, :, offs] = V
+        # V pages: per 16-slot block, runs 16*g + l of 4 slots x NV dims
+        nv = _V_RUN[w.cache_dtype]
+        d = np.arange(w.head_dim)
+        grp, j, l = (d // 16) // nv, (d // 16) % nv, d % 16
+        lane = 16 * ((offs % 16) // 4)[:, None] + l[None, :]
+        pos = 4 * j[None, :] + (offs % 4)[:, None]
+        heads = np.arange(w.num_kv_heads)
+        c["v_pages"][pages[:, None, None], heads[None, :, None], (offs // 16)[:, None, None],
+                     grp[None, None, :], lane[:, None, :], pos[:, None, :]] = V
         if ks is not None:
             c["k_scales"][pages, :, offs] = ks
             c["v_scales"][pages, :, offs] = vs

@@ -15,6 +15,7 @@ import torch
 
 import synth
 from oracle import formats
+from oracle.paged import v_storage_to_logical
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -53,11 +54,30 @@ def _written_mask(w):
 
 
 def _cache_rows(w, k_pages, v_pages, seq, slots, page_table):
-    """Rows [n, heads, D] of K (stored in 32-dim blocks) and V (dim-major)."""
+    """Rows [n, heads, D] of K (stored in 32-dim blocks) and V (16-byte runs
+    in MFMA operand order), raw storage elements."""
     pages = page_table[seq][slots // w.page_size].astype(np.int64)
     offs = slots % w.page_size
     k = k_pages[pages, :, :, offs, :]                 # [n, heads, D/32, 32]
-    return k.reshape(len(slots), w.num_kv_heads, w.head_dim), v_pages[pages, :, :, offs]
+    v = v_storage_to_logical(w.cache_dtype, v_pages[pages])   # [n, heads, D, P]
+    return k.reshape(len(slots), w.num_kv_heads, w.head_dim), v[np.arange(len(slots)), :, :, offs]
+
+
+def _raw(t, dtype):
+    """CPU tensor -> numpy raw storage (float32 / uint16 bf16 bits / uint8 codes)."""
+    if dtype == "f32":
+        return t.numpy()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.view(torch.uint8).numpy()
+
+
+def _values(raw, dtype):
+    if dtype == "f32":
+        return raw.astype(np.float64)
+    if dtype == "bf16":
+        return formats.bf16_value(raw)
+    return formats.e4m3_value(raw)
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
@@ -84,18 +104,17 @@ def test_workload_full_size(k):
     c = d["cache"]
     kg_all = c.k_pages.cpu()
     vg_all = c.v_pages.cpu()
-    kg_vals = gu.host_values(kg_all, w.cache_dtype)
-    vg_vals = gu.host_values(vg_all, w.cache_dtype)
+    kg_raw, vg_raw = _raw(kg_all, w.cache_dtype), _raw(vg_all, w.cache_dtype)
     ok_adj = 0
     for i, s in enumerate(seqs):
         L, ql = int(w.kv_lens[s]), int(w.q_lens[s])
         slots = np.arange(L - ql, L)
-        kg, vg = _cache_rows(w, kg_vals, vg_vals, s, slots, w.page_table)
+        kr_, vr_ = _cache_rows(w, kg_raw, vg_raw, s, slots, w.page_table)
+        kg, vg = _values(kr_, w.cache_dtype), _values(vr_, w.cache_dtype)
         ko = cache_o.k[ws.page_table[i][slots // w.page_size].astype(np.int64), :, slots % w.page_size, :]
         vo = cache_o.v[ws.page_table[i][slots // w.page_size].astype(np.int64), :, :, slots % w.page_size]
         if w.cache_dtype == "e4m3":
-            kcg, vcg = _cache_rows(w, kg_all.view(torch.uint8).numpy(), vg_all.view(torch.uint8).numpy(),
-                                   s, slots, w.page_table)
+            kcg, vcg = kr_, vr_
             kco, vco = formats.e4m3_code(ko), formats.e4m3_code(vo)
             for a, b, what in ((kcg, kco, "K codes"), (vcg, vco, "V codes")):
                 ok_adj += int(np.sum(a != b))
@@ -119,11 +138,12 @@ def test_workload_full_size(k):
     kr = raw["k_pages"].view(np.uint8).reshape(kb.shape)
     kb, kr = np.transpose(kb, (0, 1, 3, 2, 4)), np.transpose(kr, (0, 1, 3, 2, 4))   # slot before block
     assert np.array_equal(kb[~mask], kr[~mask]), "K bytes outside the appended slots changed"
-    vb = vg_all.view(torch.uint8).numpy()
-    vr = raw["v_pages"].view(np.uint8).reshape(vb.shape)
-    vmask = np.repeat(np.transpose(mask, (0, 1, 2))[:, :, None, :], w.head_dim, axis=2)
-    vmask = np.repeat(vmask, vb.shape[-1] // w.page_size, axis=3) if vb.shape[-1] != w.page_size else vmask
-    assert np.array_equal(vb[~vmask], vr[~vmask]), "V bytes outside the appended slots changed"
+    # V: compare element bit patterns in logical [page][head][dim][slot] order
+    vb = v_storage_to_logical(w.cache_dtype, vg_raw)
+    vr = v_storage_to_logical(w.cache_dtype, raw["v_pages"].reshape(vg_raw.shape))
+    if w.cache_dtype == "f32":
+        vb, vr = vb.view(np.uint32), vr.view(np.uint32)
+    assert np.all((vb == vr) | mask[:, :, None, :]), "V bytes outside the appended slots changed"
     gu.say(f"workload {k}: untouched bytes ok")
 
     # --- attention output

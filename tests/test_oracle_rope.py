@@ -132,7 +132,7 @@ def _tiny(k):
         order = "permuted"
     else:
         q_lens, kv_lens = np.array([1, 1]), np.array([33, 18])
-        kw = dict(num_q_heads=8, num_kv_heads=1, head_dim=32, rotary_dim=32, rope_layout="half",
+        kw = dict(num_q_heads=8, num_kv_heads=1, head_dim=64, rotary_dim=64, rope_layout="half",
                   rope_theta=1e6, page_size=16, in_dtype="bf16", cache_dtype="e4m3",
                   softmax_scale=0.25, window_left=-1, qk_norm=False, explicit_positions=False)
         order = "permuted"
@@ -141,6 +141,17 @@ def _tiny(k):
            page_table=table, num_pages=npages, split_tokens=0, **kw)
     w.seq_ids = np.arange(w.num_seqs); w.token_ids = np.arange(w.total_q); w.full_total_q = w.total_q
     return w
+
+
+def _v_raw(v_pages, w, page, head, d, t):
+    """Element (dim d, slot t) of a V page-head block, by the header's offset
+    formula on the flattened block."""
+    nv = {"f32": 1, "bf16": 2, "e4m3": 4}[w.cache_dtype]
+    D = w.head_dim
+    c = (d // 16) // nv
+    idx = ((t // 16) * (D // (16 * nv)) + c) * 64 * 4 * nv + (16 * ((t % 16) // 4) + d % 16) * 4 * nv \
+        + ((d // 16) % nv) * 4 + t % 4
+    return v_pages[page, head].reshape(-1)[idx]
 
 
 def _values(dtype, raw):
@@ -195,7 +206,8 @@ def test_brute_force_matches_oracle(k):
                         vr = formats.storage_round(v[t, h], w.cache_dtype).tolist()
                 else:                                            # prior rows, read raw
                     kr = _values(w.cache_dtype, raw["k_pages"][page, h, :, off, :].reshape(-1))
-                    vr = _values(w.cache_dtype, raw["v_pages"][page, h, :, off])
+                    vr = _values(w.cache_dtype, np.array([_v_raw(raw["v_pages"], w, page, h, dd, off)
+                                                          for dd in range(w.head_dim)]))
                     if w.cache_dtype == "e4m3":
                         kr = kr * float(raw["k_scales"][page, h, off])
                         vr = vr * float(raw["v_scales"][page, h, off])
