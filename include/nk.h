@@ -41,10 +41,16 @@
  *
  * Paged cache layout (one layer), nk_paged_kv_t:
  *
- *   K pages   [num_pages][num_kv_heads][head_dim/32][page_size][32]
- *             (within one page and head, K is stored in blocks of 32
- *             dimensions: block b holds dims 32b..32b+31 of every token of the
- *             page, token after token)
+ *   K pages   [num_pages][num_kv_heads][head_dim/(32*NK)][page_size][32*NK],
+ *             NK = 2 for e4m3 and 1 otherwise: within one page and head, K is
+ *             stored in blocks of 32*NK dimensions, token after token; a
+ *             token's row of a block is 4 runs of NK*8 elements, run g holding
+ *             dims 8g..8g+7 of each of the block's NK 32-dim halves: element
+ *             (dim d, token t) of a page is at
+ *               ((d/(32*NK)) * page_size + t) * 32*NK + ((d%32)/8) * NK*8
+ *               + ((d/32)%NK) * 8 + d%8
+ *             (for bf16 and f32 simply [head_dim/32][page_size][32]; a run is
+ *             what one lane of the 16x16x32 MFMA holds of NK K operands)
  *   V pages   [num_pages][num_kv_heads][page_size/16][head_dim/(16*NV)]
  *             [64][4*NV], NV = 4 / element bytes (f32 1, bf16 2, e4m3 4):
  *             within one page and head, each 16-token block is stored as

@@ -3,9 +3,11 @@
 
 Layout (one layer):
 
-* K pages  ``[num_pages][num_kv_heads][head_dim/32][page_size][32]`` -- within
-  a page, for one head, K is stored in blocks of 32 dimensions: block b holds
-  dims 32b..32b+31 of every token of the page, token after token.
+* K pages  ``[num_pages][num_kv_heads][head_dim/(32*NK)][page_size][32*NK]``
+  with NK = 2 for e4m3 and 1 otherwise -- within a page, for one head, K is
+  stored in blocks of 32*NK dimensions, token after token; a token's row of
+  a block is 4 runs of NK*8 elements, run g holding dims 8g..8g+7 of each
+  32-dim half (for NK = 1: dims 32b..32b+31 in order).
 * V pages  ``[num_pages][num_kv_heads][page_size/16][head_dim/(16*NV)][64][4*NV]``
   with NV = 4 / element bytes (f32 1, bf16 2, e4m3 4) -- within a page, for
   one head, each block of 16 tokens is a sequence of 16-byte runs; run
@@ -67,15 +69,14 @@ class PagedCache:
         """Build from raw arrays: float32 (f32), uint16 bit patterns (bf16)
         or uint8 codes (e4m3), shaped as the layout above."""
         n, h, nb, p, blk = k_pages.shape
-        if blk != 32:
-            raise ValueError("K pages must be [num_pages][heads][head_dim/32][page_size][32]")
-        d = nb * 32
+        if blk != 32 * k_block_halves(dtype):
+            raise ValueError("K pages must be [num_pages][heads][head_dim/(32*NK)][page_size][32*NK]")
+        d = nb * blk
         c = cls(dtype, n, h, p, d)
         nv = v_run_width(dtype)
         if tuple(v_pages.shape) != (n, h, p // 16, d // (16 * nv), 64, 4 * nv):
             raise ValueError("V pages must be [num_pages][heads][page_size/16][head_dim/(16*NV)][64][4*NV]")
-        # [n][h][d/32][p][32] -> token-major [n][h][p][d]
-        c.k = _decode(dtype, np.transpose(k_pages, (0, 1, 3, 2, 4)).reshape(n, h, p, d))
+        c.k = _decode(dtype, k_storage_to_logical(dtype, np.asarray(k_pages)))
         c.v = _decode(dtype, v_storage_to_logical(dtype, np.asarray(v_pages)))
         if dtype == "e4m3":
             c.k_scale = np.asarray(k_scales, dtype=np.float32).astype(np.float64)
@@ -86,8 +87,7 @@ class PagedCache:
         """Raw arrays (k_pages, v_pages, k_scales, v_scales); unwritten slots
         (NaN) become the dtype's NaN pattern, scales NaN."""
         n, h, p, d = self.k.shape
-        k = _encode(self.dtype, self.k)
-        k = np.ascontiguousarray(np.transpose(k.reshape(n, h, p, d // 32, 32), (0, 1, 3, 2, 4)))
+        k = k_logical_to_storage(self.dtype, _encode(self.dtype, self.k))
         v = v_logical_to_storage(self.dtype, _encode(self.dtype, self.v))
         if self.dtype == "e4m3":
             return k, v, self.k_scale.astype(np.float32), self.v_scale.astype(np.float32)
@@ -120,6 +120,31 @@ class PagedCache:
             K = K * self.k_scale[pages, :, offs][:, :, None]
             V = V * self.v_scale[pages, :, offs][:, :, None]
         return K, V
+
+
+def k_block_halves(dtype):
+    """NK: 32-dim halves per K block (2 for e4m3, else 1)."""
+    return 2 if dtype == "e4m3" else 1
+
+
+def k_storage_to_logical(dtype, raw):
+    """[n][h][D/(32 NK)][P][32 NK] -> token-major [n][h][P][D]."""
+    nk = k_block_halves(dtype)
+    n, h, nb, p, row = raw.shape
+    if row != 32 * nk:
+        raise ValueError("K pages must be [num_pages][heads][head_dim/(32*NK)][page_size][32*NK]")
+    x = raw.reshape(n, h, nb, p, 4, nk, 8)                  # n h s t g half e
+    x = np.transpose(x, (0, 1, 3, 2, 5, 4, 6))              # n h t s half g e
+    return x.reshape(n, h, p, nb * nk * 32)
+
+
+def k_logical_to_storage(dtype, k):
+    """Inverse of k_storage_to_logical."""
+    nk = k_block_halves(dtype)
+    n, h, p, d = k.shape
+    x = k.reshape(n, h, p, d // (32 * nk), nk, 4, 8)         # n h t s half g e
+    x = np.transpose(x, (0, 1, 3, 2, 5, 4, 6))               # n h s t g half e
+    return np.ascontiguousarray(x).reshape(n, h, d // (32 * nk), p, 32 * nk)
 
 
 def v_run_width(dtype):

@@ -68,8 +68,8 @@ struct Page {
   static constexpr int KK = D / 32;   // k-steps of the score MFMA
   static constexpr int DT = D / 16;   // d-tiles of the output MFMA
   static constexpr int NV = FP8 ? 4 : 2;   // d-tiles per 16-byte V run
-  using KVec = typename std::conditional<FP8, u32x2_t, bf16x8_t>::type;   // 8 dims of one key
-  KVec k[KK];
+  static constexpr int NK = FP8 ? 2 : 1;   // k-steps per 16-byte K run
+  u32x4_t k[KK / NK];                 // K runs: 8 dims of this lane's key for NK k-steps each
   u32x4_t v[DT / NV];                 // V runs: this lane's 4 keys of NV d-tiles each
   f32x4_t ks, vs;                     // e4m3: scales of this lane's 4 keys
 };
@@ -94,12 +94,24 @@ template <int D, int P, bool FP8>
 NK_DEVICE LaneOffsets lane_offsets(int lane) {
   constexpr int esz = FP8 ? 1 : 2;
   const int lr = lane & 15, lg = lane >> 4;
-  return LaneOffsets{(uint32_t)((lr * 32 + 8 * lg) * esz),    // K: key lr, dims 8*lg.. of a block
+  constexpr int NK = FP8 ? 2 : 1;
+  return LaneOffsets{(uint32_t)((lr * 32 * NK + 8 * NK * lg) * esz),   // K: key lr, run lg of a block
                      (uint32_t)(16 * lane),                   // V: run `lane` of a dim group
                      (uint32_t)(4 * lg * sizeof(float))};     // scales of keys 4*lg..
 }
 
 NK_DEVICE bf16x4_t fp8x4_to_bf16x4(uint32_t w);
+
+// Operand of k-step kk (K, lane lr + 16 lg: key lr, dims 32 kk + 8 lg..)
+template <int D, bool FP8>
+NK_DEVICE bf16x8_t k_operand(const Page<D, FP8> &pg, int kk) {
+  if constexpr (FP8) {
+    const u32x4_t r = pg.k[kk >> 1];
+    return fp8x8_to_bf16x8(u32x2_t{r[2 * (kk & 1)], r[2 * (kk & 1) + 1]});
+  } else {
+    return __builtin_bit_cast(bf16x8_t, pg.k[kk]);
+  }
+}
 
 // Operand of d-tile dt (V^T, lane lr + 16 lg: dim 16 dt + lr, keys 4 lg..)
 template <int D, bool FP8>
@@ -121,14 +133,14 @@ NK_DEVICE void load_page(Page<D, FP8> &pg, const nk_paged_kv_t &c, int page, int
   constexpr int esz = FP8 ? 1 : 2;
   const int hkv = c.num_kv_heads;
   const size_t ph = (size_t)page * hkv + g;
-  // K page-head: [dim/32][slot][32]; block kk of the 16 keys is contiguous
-  const uint8_t *kpage = (const uint8_t *)c.k_pages + (ph * P * D + sb * 32) * esz;
+  // K page-head: [dim/(32 NK)][slot][32 NK]; block r of the 16 keys is contiguous
+  const uint8_t *kpage = (const uint8_t *)c.k_pages + (ph * P * D + sb * 32 * PG::NK) * esz;
   // V page-head: 16-key blocks of 16-byte runs in MFMA operand order, one
   // run per lane and dim group
   const uint8_t *vpage = (const uint8_t *)c.v_pages + (ph * D * P + sb * D) * esz;
 #pragma unroll
-  for (int kk = 0; kk < PG::KK; ++kk)
-    pg.k[kk] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const typename PG::KVec *)(kpage + lo.k + kk * P * 32 * esz));
+  for (int r = 0; r < PG::KK / PG::NK; ++r)
+    pg.k[r] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const u32x4_t *)(kpage + lo.k + r * P * 32 * PG::NK * esz));
 #pragma unroll
   for (int r = 0; r < PG::DT / PG::NV; ++r)
     pg.v[r] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const u32x4_t *)(vpage + lo.v + 1024 * r));
@@ -260,9 +272,7 @@ attn_decode_kernel(AttnArgs a) {
       f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        bf16x8_t kop;
-        if constexpr (FP8) kop = fp8x8_to_bf16x8(pg[u]->k[kk]); else kop = pg[u]->k[kk];
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<D, FP8>(*pg[u], kk), qop[kk], sacc, 0, 0, 0);
       }
       // lane holds keys kb + 4*lg + r of head column n
 #pragma unroll

@@ -222,9 +222,11 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
     const int c = tid + i * NT;
     pit[i] = (wv * 64 + i * NT) / C::PAGE_CH;
     const int w = c % C::PAGE_CH;
-    // K: lanes take consecutive LDS rows; the page block is [dim/32][token][32]
+    // K: lanes take consecutive LDS rows; the page block is
+    // [dim/(32 NK)][token][run (4)][half (NK)][8], NK 2 for e4m3, else 1
+    constexpr int NK = FP8 ? 2 : 1;
     const int kslot = w % P, e8 = (w / P) & 3, blk = w / (4 * P);
-    kg[i] = (uint32_t)((blk * P * 32 + perm_key(kslot) * 32 + e8 * 8) * C::ESZ);
+    kg[i] = (uint32_t)((((blk / NK) * P + perm_key(kslot)) * 32 * NK + e8 * NK * 8 + (blk % NK) * 8) * C::ESZ);
     kl[i] = (uint32_t)((pit[i] * P + kslot) * C::KROW + (blk * 32 + e8 * 8) * 2);
     // V: the page block is 16-token blocks of 16-byte runs in MFMA operand
     // order; a chunk (8 elements) is 4 tokens of 2 dims 16 apart: run

@@ -97,6 +97,15 @@ template <> NK_DEVICE void store_k8<kCacheE4M3>(void *row, int d0, const double 
   *(u32x2_t *)((uint8_t *)row + d0) = w;
 }
 
+// K page-head block (include/nk.h): blocks of 32*NK dims (NK 2 for e4m3,
+// else 1), slot after slot; a slot's row of a block is 4 runs of NK*8
+// elements, run g holding dims 8g..8g+7 of each 32-dim half.  Offset of
+// (dim d, slot t), d a multiple of 8: the 8 dims d..d+7 are contiguous.
+template <int CACHE> NK_DEVICE size_t k_index(int d, int t, int P) {
+  constexpr int NK = CACHE == kCacheE4M3 ? 2 : 1;
+  return ((size_t)(d / (32 * NK)) * P + t) * (32 * NK) + ((d & 31) >> 3) * (NK * 8) + ((d >> 5) % NK) * 8;
+}
+
 // V page-head block in MFMA operand order (include/nk.h): element (dim d,
 // slot t) sits at v_index(d, t); for 8 consecutive dims of one 16-dim tile
 // the offsets step by 4*NV elements, NV = 4 / element bytes.
@@ -233,10 +242,10 @@ __global__ void __launch_bounds__(256) rope_write_kernel(RopeArgs a) {
 
   constexpr int esz = CACHE == kCacheF32 ? 4 : (CACHE == kCacheBF16 ? 2 : 1);
   if (kind == 1) {
-    // K page: blocks of 32 dims, [dim/32][slot][32]
+    // K page: blocks of 32*NK dims, see k_index
     uint8_t *kph = (uint8_t *)a.cache.k_pages + ph * P * (size_t)D * esz;
-    store_k8<CACHE>(kph + ((size_t)(a0 >> 5) * P + off) * 32 * esz, a0 & 31, xa);
-    store_k8<CACHE>(kph + ((size_t)(b0 >> 5) * P + off) * 32 * esz, b0 & 31, xb);
+    store_k8<CACHE>(kph + k_index<CACHE>(a0, off, P) * esz, 0, xa);
+    store_k8<CACHE>(kph + k_index<CACHE>(b0, off, P) * esz, 0, xb);
   } else {
     // V page: MFMA operand order, see v_index
     void *blk = (uint8_t *)a.cache.v_pages + ph * D * (size_t)P * esz;

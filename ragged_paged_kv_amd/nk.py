@@ -124,7 +124,8 @@ def _i32(t, name):
 class PagedKVCache:
     """One layer's paged cache (device tensors in the layout of nk.h).
 
-    k_pages [num_pages, Hkv, D/32, P, 32], v_pages [num_pages, Hkv, P/16,
+    k_pages [num_pages, Hkv, D/(32 NK), P, 32 NK] (NK 2 for e4m3, else 1),
+    v_pages [num_pages, Hkv, P/16,
     D/(16 NV), 64, 4 NV] with NV = 4 / element bytes (float32, bfloat16 or
     uint8 e4m3 codes), k_scales/v_scales [num_pages, Hkv, P] float32 for
     e4m3, page_table [num_seqs, stride] int32.
@@ -132,9 +133,10 @@ class PagedKVCache:
 
     def __init__(self, k_pages, v_pages, page_table, k_scales=None, v_scales=None):
         n, h, nb, p, blk = k_pages.shape
-        d = nb * 32
-        if blk != 32:
-            raise ValueError("k_pages must be [num_pages, heads, head_dim/32, page_size, 32]")
+        nk = 2 if k_pages.element_size() == 1 else 1
+        d = nb * blk
+        if blk != 32 * nk:
+            raise ValueError("k_pages must be [num_pages, heads, head_dim/(32*NK), page_size, 32*NK]")
         nv = 4 // k_pages.element_size()
         if d % (16 * nv) or p % 16 or tuple(v_pages.shape) != (n, h, p // 16, d // (16 * nv), 64, 4 * nv):
             raise ValueError("v_pages must be [num_pages, heads, page_size/16, head_dim/(16*NV), 64, 4*NV]")

@@ -272,12 +272,14 @@ _V_RUN = {"f32": 1, "bf16": 2, "e4m3": 4}
 
 def sentinel_cache(w):
     """Empty cache storage: every element the dtype's all-ones NaN pattern,
-    scales NaN.  Returns dict(k_pages [pages, heads, D/32, P, 32], v_pages
+    scales NaN.  Returns dict(k_pages [pages, heads, D/(32 NK), P, 32 NK]
+    (NK 2 for e4m3, else 1), v_pages
     [pages, heads, P/16, D/(16 NV), 64, 4 NV], k_scales, v_scales
     [pages, heads, P]); NV = 4 / element bytes."""
     dt, pat = _SENTINEL[w.cache_dtype]
     nv = _V_RUN[w.cache_dtype]
-    kshape = (w.num_pages, w.num_kv_heads, w.head_dim // 32, w.page_size, 32)
+    nk = 2 if w.cache_dtype == "e4m3" else 1
+    kshape = (w.num_pages, w.num_kv_heads, w.head_dim // (32 * nk), w.page_size, 32 * nk)
     vshape = (w.num_pages, w.num_kv_heads, w.page_size // 16, w.head_dim // (16 * nv), 64, 4 * nv)
     if w.cache_dtype == "f32":
         k = np.full(kshape, pat, dtype=np.uint32).view(np.float32)
@@ -305,8 +307,11 @@ def build_cache(w, threads=8):
         slots = np.arange(n)
         pages = w.page_table[s][slots // w.page_size].astype(np.int64)
         offs = slots % w.page_size
-        # K pages hold blocks of 32 dims: [page][head][dim/32][slot][32]
-        c["k_pages"][pages, :, :, offs, :] = K.reshape(n, w.num_kv_heads, w.head_dim // 32, 32)
+        # K pages hold blocks of 32*NK dims: [page][head][block][slot][32*NK],
+        # a slot's row of a block ordered (8-dim group, 32-dim half, dim)
+        nk = 2 if w.cache_dtype == "e4m3" else 1
+        kb = K.reshape(n, w.num_kv_heads, w.head_dim // (32 * nk), nk, 4, 8).transpose(0, 1, 2, 4, 3, 5)
+        c["k_pages"][pages, :, :, offs, :] = kb.reshape(n, w.num_kv_heads, w.head_dim // (32 * nk), 32 * nk)
         # V pages: per 16-slot block, runs 16*g + l of 4 slots x NV dims
         nv = _V_RUN[w.cache_dtype]
         d = np.arange(w.head_dim)

@@ -15,7 +15,7 @@ import torch
 
 import synth
 from oracle import formats
-from oracle.paged import v_storage_to_logical
+from oracle.paged import k_storage_to_logical, v_storage_to_logical
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -54,13 +54,14 @@ def _written_mask(w):
 
 
 def _cache_rows(w, k_pages, v_pages, seq, slots, page_table):
-    """Rows [n, heads, D] of K (stored in 32-dim blocks) and V (16-byte runs
-    in MFMA operand order), raw storage elements."""
+    """Rows [n, heads, D] of K (blocks of 32 NK dims) and V (16-byte runs in
+    MFMA operand order), raw storage elements."""
     pages = page_table[seq][slots // w.page_size].astype(np.int64)
     offs = slots % w.page_size
-    k = k_pages[pages, :, :, offs, :]                 # [n, heads, D/32, 32]
+    k = k_storage_to_logical(w.cache_dtype, k_pages[pages])   # [n, heads, P, D]
     v = v_storage_to_logical(w.cache_dtype, v_pages[pages])   # [n, heads, D, P]
-    return k.reshape(len(slots), w.num_kv_heads, w.head_dim), v[np.arange(len(slots)), :, :, offs]
+    n = np.arange(len(slots))
+    return k[n, :, offs, :], v[n, :, :, offs]
 
 
 def _raw(t, dtype):
@@ -133,7 +134,7 @@ def test_workload_full_size(k):
     # --- nothing else in the cache changed
     raw = d["raw_cache"]
     mask = _written_mask(w)
-    nb = w.head_dim // 32
+    nb = kg_all.shape[2]
     kb = kg_all.view(torch.uint8).numpy().reshape(w.num_pages, w.num_kv_heads, nb, w.page_size, -1)
     kr = raw["k_pages"].view(np.uint8).reshape(kb.shape)
     kb, kr = np.transpose(kb, (0, 1, 3, 2, 4)), np.transpose(kr, (0, 1, 3, 2, 4))   # slot before block

@@ -5,7 +5,8 @@ values -> storage is the identity (K and V, every element type)."""
 import numpy as np
 import pytest
 
-from oracle.paged import PagedCache, v_logical_to_storage, v_storage_to_logical
+from oracle.paged import (PagedCache, k_logical_to_storage, k_storage_to_logical, v_logical_to_storage,
+                          v_storage_to_logical)
 
 
 def _formula(d, t, D, nv):
@@ -28,6 +29,21 @@ def test_v_order_is_the_header_formula(dtype, nv, D, P):
     np.testing.assert_array_equal(v_storage_to_logical(dtype, raw), logical)
 
 
+@pytest.mark.parametrize("dtype,nk", [("f32", 1), ("bf16", 1), ("e4m3", 2)])
+@pytest.mark.parametrize("D,P", [(64, 16), (128, 32), (256, 16)])
+def test_k_order_is_the_header_formula(dtype, nk, D, P):
+    rng = np.random.default_rng(9)
+    logical = rng.integers(0, 1 << 16, size=(3, 2, P, D))          # [page][head][token][dim]
+    raw = k_logical_to_storage(dtype, logical)
+    assert raw.shape == (3, 2, D // (32 * nk), P, 32 * nk)
+    flat = raw.reshape(3, 2, -1)
+    for d in range(0, D, 5):
+        for t in range(P):
+            idx = ((d // (32 * nk)) * P + t) * 32 * nk + ((d % 32) // 8) * nk * 8 + ((d // 32) % nk) * 8 + d % 8
+            assert flat[0, 1, idx] == logical[0, 1, t, d]
+    np.testing.assert_array_equal(k_storage_to_logical(dtype, raw), logical)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "e4m3"])
 def test_storage_round_trip(dtype):
     rng = np.random.default_rng(8)
@@ -39,7 +55,7 @@ def test_storage_round_trip(dtype):
         k = rng.integers(0, 0x7f80, size=(n, h, d // 32, p, 32)).astype(np.uint16)
         v = rng.integers(0, 0x7f80, size=(n, h, p // 16, d // 32, 64, 8)).astype(np.uint16)
     else:
-        k = rng.integers(0, 0x7f, size=(n, h, d // 32, p, 32)).astype(np.uint8)
+        k = rng.integers(0, 0x7f, size=(n, h, d // 64, p, 64)).astype(np.uint8)
         v = rng.integers(0, 0x7f, size=(n, h, p // 16, d // 64, 64, 16)).astype(np.uint8)
     ks = vs = None
     if dtype == "e4m3":

@@ -143,6 +143,14 @@ def _tiny(k):
     return w
 
 
+def _k_raw(k_pages, w, page, head, d, t):
+    """Element (dim d, slot t) of a K page-head block, by the header's offset
+    formula on the flattened block."""
+    nk = 2 if w.cache_dtype == "e4m3" else 1
+    idx = ((d // (32 * nk)) * w.page_size + t) * 32 * nk + ((d % 32) // 8) * nk * 8 + ((d // 32) % nk) * 8 + d % 8
+    return k_pages[page, head].reshape(-1)[idx]
+
+
 def _v_raw(v_pages, w, page, head, d, t):
     """Element (dim d, slot t) of a V page-head block, by the header's offset
     formula on the flattened block."""
@@ -205,7 +213,8 @@ def test_brute_force_matches_oracle(k):
                         kr = formats.storage_round(np.array(kr), w.cache_dtype).tolist()
                         vr = formats.storage_round(v[t, h], w.cache_dtype).tolist()
                 else:                                            # prior rows, read raw
-                    kr = _values(w.cache_dtype, raw["k_pages"][page, h, :, off, :].reshape(-1))
+                    kr = _values(w.cache_dtype, np.array([_k_raw(raw["k_pages"], w, page, h, dd, off)
+                                                          for dd in range(w.head_dim)]))
                     vr = _values(w.cache_dtype, np.array([_v_raw(raw["v_pages"], w, page, h, dd, off)
                                                           for dd in range(w.head_dim)]))
                     if w.cache_dtype == "e4m3":
