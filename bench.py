@@ -18,8 +18,11 @@ bracketed by torch.cuda.synchronize().  Before every step a 1 GiB buffer is
 read (outside the step's events) so that the 256 MB Infinity Cache and the
 L2s hold none of the step's inputs -- a read, not a write, so that the step
 does not pay for writing back someone else's dirty lines; each step is timed
-with HIP events on the step's stream and ms_per_step is the median.  Per-kernel durations come from
-the library's own event pairs around each launch (nk_profile_*).
+with HIP events on the step's stream and ms_per_step is the median.  Kernel
+durations come from the library's own event pairs around each launch
+(nk_profile_*): inside the timed region only the workload's dominant kernels
+carry them (every pair costs the stream a few microseconds); a second pass
+of the same number of steps times all kernels for the per-kernel table.
 """
 
 import argparse
@@ -45,7 +48,29 @@ DESCR = {
     "mixed_window_bf16": "sliding-window mixed batch, bf16: 4 prefill 1024-4096 + 60 decode 2048-8192, Hq16/Hkv8, D256, window 1024",
     "tiny_prefill_f32": "tiny ragged prefill, fp32: segments 5 and 12, Hq4/Hkv2, D64",
 }
-KERNEL_SOURCES = ["attn_decode.hip", "attn_prefill.hip", "rope_write.hip", "lse_merge.hip", "common.h"]
+# kernels whose launches carry event pairs inside the timed region
+DOMINANT = {
+    "decode_bf16": ("attn_decode",),
+    "prefill_bf16": ("attn_prefill",),
+    "decode_fp8": ("attn_decode",),
+    "mixed_window_bf16": ("attn_prefill", "attn_decode"),
+    "tiny_prefill_f32": ("attn_f32",),
+}
+KERNEL_SOURCES = ["attn_decode.hip", "attn_prefill.hip", "rope_write.hip", "lse_merge.hip", "common.h", "internal.h"]
+# the sources a kernel family is built from: a counter summary stays valid
+# while these are unchanged
+FAMILY_SOURCES = {
+    "attn_decode": ["attn_decode.hip", "common.h", "internal.h"],
+    "attn_prefill": ["attn_prefill.hip", "common.h", "internal.h"],
+    "rope_write": ["rope_write.hip", "common.h", "internal.h"],
+}
+
+
+def family_sources(kernel_name):
+    for fam, files in FAMILY_SOURCES.items():
+        if fam in kernel_name:
+            return files
+    return KERNEL_SOURCES
 
 
 def source_hash(files=KERNEL_SOURCES):
@@ -129,33 +154,47 @@ def measure(st, steps, warmup, flush, split=None):
 
     scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
     sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def timed(nsteps, families):
+        """nsteps steps, each after a cache-clearing read and between two
+        events; the library brackets only the launches of `families`."""
+        nk.profile_reset()
+        if families:
+            nk.profile_enable(True, families)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for i in range(nsteps):
+            if scratch is not None:
+                torch.sum(scratch, dim=0, out=sink)
+            evs[i][0].record()
+            step()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        nk.profile_enable(False)
+        kern = {}
+        for fam in nk.PROFILE_FAMILIES:
+            tot, n = nk.profile_read(fam)
+            if n:
+                kern[fam] = {"avg_ms": tot / n, "launches": n}
+        return sorted(a.elapsed_time(b) for a, b in evs), wall, kern
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    nk.profile_reset()
-    nk.profile_enable(True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(steps):
-        if scratch is not None:
-            torch.sum(scratch, dim=0, out=sink)
-        evs[i][0].record()
-        step()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    nk.profile_enable(False)
-    times = sorted(a.elapsed_time(b) for a, b in evs)
+    # the timed region: only the dominant kernels carry event pairs (each pair
+    # costs the stream a few microseconds, which would otherwise show up in
+    # the step time); a second pass of the same steps times every kernel
+    times, wall, kern_timed = timed(steps, DOMINANT[w.name])
     ms = times[len(times) // 2]
-    kern = {}
-    for fam in ("rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge"):
-        tot, n = nk.profile_read(fam)
-        if n:
-            kern[fam] = {"avg_ms": tot / n, "launches": n}
+    _, _, kern = timed(steps, nk.PROFILE_FAMILIES)
+    for fam, rec in kern_timed.items():
+        kern[fam] = rec
     res = {
         "workload": w.name, "descr": DESCR[w.name], "ms_per_step": ms, "ms_min": times[0], "ms_max": times[-1],
-        "wall_s_incl_flush": wall, "kernels": kern, "split_tokens": split_used,
+        "wall_s_incl_flush": wall, "kernels": kern, "kernels_timed_in_region": sorted(kern_timed),
+        "split_tokens": split_used,
         "decode_bytes": work.decode_bytes(w), "prefill_flops": work.prefill_flops(w), "rope_bytes": work.rope_bytes(w),
     }
     if res["decode_bytes"]:
@@ -219,7 +258,7 @@ def load_traffic(kernel_key):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(family_sources(rec.get("kernel", ""))):
         return None
     return rec.get("bytes_per_launch")
 
@@ -286,7 +325,7 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes
     rec = {"kernel": kernel_match, "fetch_kib": kf, "write_kib": kw, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "copy_bytes": copy_bytes, "fetch_scale": fs, "write_scale": wsf,
            "bytes_per_launch": (kf * 1024 * fs + kw * 1024 * wsf) if None not in (kf, kw, fs, wsf) else None,
-           "source_hash": source_hash()}
+           "source_hash": source_hash(family_sources(kernel_match))}
     with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -334,7 +373,7 @@ def main():
                "write_kib_per_dispatch": kw, "copy_bytes": args.copy_bytes, "copy_fetch_kib": cf,
                "copy_write_kib": cw, "fetch_scale": fs, "write_scale": wsf,
                "bytes_per_launch": (kf * 1024 * fs + kw * 1024 * wsf) if None not in (kf, kw, fs, wsf) else None,
-               "source_hash": source_hash()}
+               "source_hash": source_hash(family_sources(args.pmc_kernel))}
         with open(out, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec, indent=1))

@@ -233,15 +233,26 @@ const char *nk_status_string(int status);
 int nk_version(void);
 
 /*
- * Kernel timing (diagnostics).  When enabled, every launch the entry points
- * make is bracketed by two HIP events recorded on the call's stream, kept per
- * kernel family ("rope_write", "attn_decode", "attn_prefill", "attn_f32",
- * "lse_merge").  nk_profile_read waits for the recorded events and returns
- * the summed milliseconds and the launch count of one family since the last
+ * Kernel timing (diagnostics).  nk_profile_enable takes a mask of kernel
+ * families: NK_PROF_ROPE_WRITE ("rope_write"), NK_PROF_ATTN_DECODE
+ * ("attn_decode"), NK_PROF_ATTN_PREFILL ("attn_prefill", which includes its
+ * scheduling kernel), NK_PROF_ATTN_F32 ("attn_f32"), NK_PROF_LSE_MERGE
+ * ("lse_merge"); NK_PROF_ALL selects every family and 0 turns timing off.
+ * Every launch of a selected family is bracketed by two HIP events recorded
+ * on the call's stream.  The events themselves cost the stream a few
+ * microseconds, so a caller timing whole steps selects only the family it
+ * needs.  nk_profile_read waits for the recorded events and returns the
+ * summed milliseconds and the launch count of one family since the last
  * reset.  Events are created on first use and reused; this is the only state
  * the library keeps.  Not for concurrent use from several threads.
  */
-int nk_profile_enable(int enable);
+#define NK_PROF_ROPE_WRITE 1
+#define NK_PROF_ATTN_DECODE 2
+#define NK_PROF_ATTN_PREFILL 4
+#define NK_PROF_ATTN_F32 8
+#define NK_PROF_LSE_MERGE 16
+#define NK_PROF_ALL 31
+int nk_profile_enable(int family_mask);
 int nk_profile_reset(void);
 int nk_profile_read(const char *kernel, double *total_ms_host, int64_t *launches_host);
 

@@ -95,7 +95,7 @@ WorkspacePlan plan_workspace(int q_dtype, int cache_dtype, int num_seqs, int tot
 // ------------------------------------------------------------------ profiling
 struct ProfileState {
   std::mutex mu;
-  bool enabled = false;
+  int mask = 0;
   struct Rec { const char *family; hipEvent_t a, b; bool pending; };
   std::vector<Rec> recs;
   std::vector<std::pair<std::string, std::pair<double, int64_t>>> totals;
@@ -123,9 +123,16 @@ void flush_pending(ProfileState &p) {
 
 namespace nk {
 
+static int family_bit(const char *family) {
+  static const char *const names[] = {"rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge"};
+  for (int i = 0; i < 5; ++i)
+    if (std::strcmp(family, names[i]) == 0) return 1 << i;
+  return 0;
+}
+
 ProfileScope::ProfileScope(const char *family, hipStream_t s) : slot(-1), stream(s) {
   ProfileState &p = prof();
-  if (!p.enabled) return;
+  if (!(p.mask & family_bit(family))) return;
   std::lock_guard<std::mutex> lock(p.mu);
   int idx = -1;
   for (size_t i = 0; i < p.recs.size(); ++i)
@@ -286,8 +293,9 @@ int nk_attention_lse_merge(const float *partial_out, const float *partial_lse,
              ? NK_OK : NK_ERR_DEVICE;
 }
 
-int nk_profile_enable(int enable) {
-  prof().enabled = enable != 0;
+int nk_profile_enable(int family_mask) {
+  if (family_mask & ~NK_PROF_ALL) return NK_ERR_INVALID_ARG;
+  prof().mask = family_mask;
   return NK_OK;
 }
 

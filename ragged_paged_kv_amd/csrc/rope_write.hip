@@ -12,7 +12,8 @@
 // once from it (see round_odd_f32), so q_out and the appended cache rows are
 // exactly the float64 definition rounded to the storage type.
 //
-// Design: a streaming pass, HBM-bound.  One thread owns a "unit" of 16
+// Design: a streaming pass, HBM-bound.  One work-group per token (more if its
+// units exceed 1024 threads).  One thread owns a "unit" of 16
 // elements of one head of one token: for the rotate-half layout the 8
 // elements [8j, 8j+8) and their partners [R/2+8j, R/2+8j+8); for the
 // interleaved layout and for pass-through dims, 16 consecutive elements.
@@ -41,9 +42,14 @@ enum CacheKind { kCacheF32 = 0, kCacheBF16 = 1, kCacheE4M3 = 2 };
 // rounding of the float64.
 
 NK_DEVICE float round_odd_f32(double d) {
-  float f = __double2float_rz(d);
-  if ((double)f != d) f = __uint_as_float(__float_as_uint(f) | 1u);
-  return f;
+  // nearest float32 first (one conversion instruction); where that rounded
+  // away from zero, step one unit back toward zero (the truncation), then
+  // mark any inexact result by setting the last bit
+  const float f = (float)d;
+  const double fd = f;
+  uint32_t u = __float_as_uint(f);
+  if (fd != d) u = (u - (fabs(fd) > fabs(d) ? 1u : 0u)) | 1u;
+  return __uint_as_float(u);
 }
 
 template <typename T> struct InTraits;
@@ -117,55 +123,152 @@ template <int CACHE> NK_DEVICE size_t v_index(int d, int t, int D) {
          (size_t)(16 * ((t & 15) >> 2) + (d & 15)) * (4 * NV) + ((d >> 4) % NV) * 4 + (t & 3);
 }
 
-// Store 8 V elements d0..d0+7 (d0 a multiple of 8) of slot t.
-template <int CACHE> NK_DEVICE void store_v8(void *blk, int d0, int t, int D, const double *x);
-template <> NK_DEVICE void store_v8<kCacheF32>(void *blk, int d0, int t, int D, const double *x) {
-  float *p = (float *)blk + v_index<kCacheF32>(d0, t, D);
+// V append, one wave per (group of consecutive tokens, kv head).  A 16-byte
+// run of a V page holds 4 consecutive slots (a "quad") of NV dims (v_index):
+// one token alone can only fill esz bytes of each run.  The wave therefore
+// writes every quad whose first new slot belongs to one of its tokens,
+// reading the quad's other new rows itself (they may belong to the next
+// group): rows go to LDS in run order, and a full quad leaves as whole
+// 16-byte runs; quads cut by the start or end of a segment's new slots are
+// written element by element.
+template <typename TIn, int CACHE, int D>
+NK_DEVICE void append_v_quads(const RopeArgs &a, int t0, int ntok, int head, uint8_t *stage) {
+  constexpr int esz = CACHE == kCacheF32 ? 4 : (CACHE == kCacheBF16 ? 2 : 1);
+  constexpr int NV = v_nv<CACHE>();
+  constexpr int E = D / 16;        // elements of a row per lane, 16 lanes per row
+  constexpr int NR = D / NV;       // 16-byte runs per quad and head
+  const int P = a.cache.page_size, hkv = a.cache.num_kv_heads;
+  const int lane = threadIdx.x & 63, b = lane >> 4, chunk = lane & 15;
+  int s = find_segment(a.q_offsets, a.num_seqs, t0);
+  int q0 = a.q_offsets[s], q_end = a.q_offsets[s + 1], kv = a.kv_lens[s];
+  for (int t = t0; t < t0 + ntok; ++t) {
+    if (t >= q_end) {        // next non-empty segment
+      s = find_segment(a.q_offsets, a.num_seqs, t);
+      q0 = a.q_offsets[s]; q_end = a.q_offsets[s + 1]; kv = a.kv_lens[s];
+    }
+    const int slot = kv - (q_end - q0) + (t - q0);
+    // only the first new slot of a quad starts one; slot < 0 violates the
+    // precondition and has nowhere to go
+    if (slot < 0 || ((slot & 3) != 0 && t != q0)) continue;
+    const int a0 = slot & 3, n = min(4 - a0, q_end - t);
+    const int page = a.cache.page_table[(size_t)s * a.cache.page_table_stride + slot / P];
+    const size_t ph = (size_t)page * hkv + head;
+
+    // row b of the quad (slot slot - a0 + b) is token t + b - a0
+    if (b >= a0 && b < a0 + n) {
+      const TIn *src = (const TIn *)a.v + ((size_t)(t + b - a0) * hkv + head) * D + chunk * E;
+      TIn x[E];
+      constexpr int W = (int)(16 / sizeof(TIn)) < E ? (int)(16 / sizeof(TIn)) : E;   // per vector load
+      typedef TIn vec_t __attribute__((__vector_size__(W * sizeof(TIn))));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e * 4] = (float)x[e];
-}
-template <> NK_DEVICE void store_v8<kCacheBF16>(void *blk, int d0, int t, int D, const double *x) {
-  bf16_t *p = (bf16_t *)blk + v_index<kCacheBF16>(d0, t, D);
+      for (int e = 0; e < E; e += W) {
+        const vec_t v = *(const vec_t *)(src + e);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e * 8] = (bf16_t)round_odd_f32(x[e]);
-}
-template <> NK_DEVICE void store_v8<kCacheE4M3>(void *blk, int d0, int t, int D, const double *x) {
-  uint8_t *p = (uint8_t *)blk + v_index<kCacheE4M3>(d0, t, D);
+        for (int k = 0; k < W; ++k) x[e + k] = v[k];
+      }
+      if (CACHE == kCacheE4M3) {
+        double xd[E], m = 0.0;
 #pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    uint32_t c = fp8x2(x[e], x[e + 1]);
-    p[e * 16] = (uint8_t)(c & 0xff);
-    p[(e + 1) * 16] = (uint8_t)(c >> 8);
+        for (int e = 0; e < E; ++e) { xd[e] = (double)(float)x[e]; m = fmax(m, fabs(xd[e])); }
+#pragma unroll
+        for (int mask = 1; mask < 16; mask <<= 1) m = fmax(m, __shfl_xor(m, mask, kWave));
+        const float scale = (float)(m / 448.0);
+        const double sd = scale;
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          const uint32_t c2 = scale > 0.f ? fp8x2(xd[e] / sd, xd[e + 1] / sd) : 0u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int d = chunk * E + e + h;
+            stage[((((d >> 4) / NV) * 16 + (d & 15)) * 4 * NV + ((d >> 4) % NV) * 4 + b) * esz] =
+                (uint8_t)(c2 >> (8 * h));
+          }
+        }
+        if (chunk == 0) a.cache.v_scales[ph * P + (slot % P - a0 + b)] = scale;   // slot within the page
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int d = chunk * E + e;
+          *(TIn *)(stage + ((((d >> 4) / NV) * 16 + (d & 15)) * 4 * NV + ((d >> 4) % NV) * 4 + b) * esz) = x[e];
+        }
+      }
+    }   // (a row's 16 lanes are all in or all out, so the absmax shuffles stay in active lanes)
+    // LDS operations of one wave are performed in order; the barrier keeps
+    // the compiler from moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const int qs = slot - a0;                    // first slot of the quad
+    uint8_t *blk = (uint8_t *)a.cache.v_pages + ph * (size_t)P * D * esz;
+#pragma unroll
+    for (int r = lane; r < NR; r += 64) {
+      const int c = r >> 4, r16 = r & 15;
+      const size_t off = ((size_t)((qs % P) >> 4) * (D / (16 * NV)) + c) * (64 * 4 * NV) +
+                         (size_t)(16 * ((qs & 15) >> 2) + r16) * (4 * NV);
+      const u32x4_t run = *(const u32x4_t *)(stage + r * 16);
+      if (a0 == 0 && n == 4) {
+        *(u32x4_t *)(blk + off * esz) = run;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4 * NV; ++j) {
+          if ((j & 3) < a0 || (j & 3) >= a0 + n) continue;
+          const uint8_t *e8 = (const uint8_t *)&run + j * esz;
+          if (esz == 4) *(uint32_t *)(blk + (off + j) * esz) = *(const uint32_t *)e8;
+          else if (esz == 2) *(uint16_t *)(blk + (off + j) * esz) = *(const uint16_t *)e8;
+          else blk[off + j] = *e8;
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
 template <typename TIn, int CACHE, bool INTERLEAVED>
-__global__ void __launch_bounds__(256) rope_write_kernel(RopeArgs a) {
+__global__ void __launch_bounds__(1024) rope_write_kernel(RopeArgs a, int units_per_token, int blocks_per_token,
+                                                          int v_blocks, int v_group) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t v_stage[];
   const int D = a.cache.head_dim;
+  const int hkv = a.cache.num_kv_heads;
+  if ((int)blockIdx.x < v_blocks) {
+    // V append first (its waves are latency-bound; the streaming Q/K blocks
+    // dispatched behind them overlap that latency): one wave per (group of
+    // v_group tokens, kv head), 4*D elements of LDS each
+    const int item = (int)blockIdx.x * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6);
+    const int g = item / hkv, head = item - g * hkv;
+    const int t0 = g * v_group;
+    if (t0 >= a.total_tokens) return;
+    const int ntok = min(v_group, a.total_tokens - t0);
+    constexpr int esz = CACHE == kCacheF32 ? 4 : (CACHE == kCacheBF16 ? 2 : 1);
+    uint8_t *stage = v_stage + (threadIdx.x >> 6) * (size_t)(4 * D * esz);
+    if (D == 64) append_v_quads<TIn, CACHE, 64>(a, t0, ntok, head, stage);
+    else if (D == 128) append_v_quads<TIn, CACHE, 128>(a, t0, ntok, head, stage);
+    else append_v_quads<TIn, CACHE, 256>(a, t0, ntok, head, stage);
+    return;
+  }
+  const unsigned qb = blockIdx.x - (unsigned)v_blocks;
   const int R = a.rotary_dim;
   const int P = a.cache.page_size;
-  const int hkv = a.cache.num_kv_heads;
   const int units_per_head = D >> 4;
-  const int heads_per_token = a.hq + 2 * hkv;
-  const long long units = (long long)a.total_tokens * heads_per_token * units_per_head;
-  const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= units) return;
+  // Q and K: one token per work-group (blocks_per_token of them when its
+  // units do not fit one), so the token and its segment are wave-uniform
+  const int t = (int)(qb / (unsigned)blocks_per_token);
+  const int lu = (int)(qb - (unsigned)t * blocks_per_token) * blockDim.x + threadIdx.x;
+  if (lu >= units_per_token) return;
+  const int hh = lu / units_per_head;
+  const int j = lu - hh * units_per_head;
 
-  const int j = (int)(u % units_per_head);
-  const long long th = u / units_per_head;
-  const int hh = (int)(th % heads_per_token);
-  const int t = (int)(th / heads_per_token);
-
-  const int kind = hh < a.hq ? 0 : (hh < a.hq + hkv ? 1 : 2);   // q, k, v
-  const int head = kind == 0 ? hh : (kind == 1 ? hh - a.hq : hh - a.hq - hkv);
+  const int kind = hh < a.hq ? 0 : 1;   // q, k
+  const int head = kind == 0 ? hh : hh - a.hq;
   const int hn = kind == 0 ? a.hq : hkv;
-  const TIn *src = (const TIn *)(kind == 0 ? a.q : (kind == 1 ? a.k : a.v)) +
-                   ((size_t)t * hn + head) * D;
+  const TIn *src = (const TIn *)(kind == 0 ? a.q : a.k) + ((size_t)t * hn + head) * D;
 
   // run A / run B of this unit and whether it rotates
-  const bool rotates = kind != 2 && (INTERLEAVED ? 16 * j < R : j < (R >> 4));
+  const bool rotates = INTERLEAVED ? 16 * j < R : j < (R >> 4);
   int a0, b0;
-  if (INTERLEAVED || kind == 2) {
+  if (INTERLEAVED) {
     a0 = 16 * j; b0 = a0 + 8;
   } else if (rotates) {
     a0 = 8 * j; b0 = (R >> 1) + 8 * j;
@@ -237,34 +340,36 @@ __global__ void __launch_bounds__(256) rope_write_kernel(RopeArgs a) {
       xa[e] = scale > 0.f ? xa[e] / sd : 0.0;
       xb[e] = scale > 0.f ? xb[e] / sd : 0.0;
     }
-    if (j == 0) (kind == 1 ? a.cache.k_scales : a.cache.v_scales)[ph * P + off] = scale;
+    if (j == 0) a.cache.k_scales[ph * P + off] = scale;
   }
 
+  // K page: blocks of 32*NK dims, see k_index
   constexpr int esz = CACHE == kCacheF32 ? 4 : (CACHE == kCacheBF16 ? 2 : 1);
-  if (kind == 1) {
-    // K page: blocks of 32*NK dims, see k_index
-    uint8_t *kph = (uint8_t *)a.cache.k_pages + ph * P * (size_t)D * esz;
-    store_k8<CACHE>(kph + k_index<CACHE>(a0, off, P) * esz, 0, xa);
-    store_k8<CACHE>(kph + k_index<CACHE>(b0, off, P) * esz, 0, xb);
-  } else {
-    // V page: MFMA operand order, see v_index
-    void *blk = (uint8_t *)a.cache.v_pages + ph * D * (size_t)P * esz;
-    store_v8<CACHE>(blk, a0, off, D, xa);
-    store_v8<CACHE>(blk, b0, off, D, xb);
-  }
+  uint8_t *kph = (uint8_t *)a.cache.k_pages + ph * P * (size_t)D * esz;
+  store_k8<CACHE>(kph + k_index<CACHE>(a0, off, P) * esz, 0, xa);
+  store_k8<CACHE>(kph + k_index<CACHE>(b0, off, P) * esz, 0, xb);
 }
 
 template <typename TIn, int CACHE>
 hipError_t launch_layout(const RopeArgs &a, hipStream_t stream) {
-  const int hkv = a.cache.num_kv_heads;
-  const long long units = (long long)a.total_tokens * (a.hq + 2 * hkv) * (a.cache.head_dim / 16);
-  const int block = 256;
-  const long long grid = (units + block - 1) / block;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  constexpr int esz = CACHE == kCacheF32 ? 4 : (CACHE == kCacheBF16 ? 2 : 1);
+  const int hkv = a.cache.num_kv_heads, D = a.cache.head_dim;
+  const int upt = (a.hq + hkv) * (D / 16);          // Q and K units of a token
+  const int bpt = (upt + 1023) / 1024;
+  const int block = ((upt + bpt - 1) / bpt + 63) / 64 * 64;
+  const long long qk_blocks = (long long)a.total_tokens * bpt;
+  // V groups: 4 tokens per wave when segments are long enough for whole
+  // quads to be common, else one (decode steps: every token its own quad)
+  const int v_group = a.total_tokens >= 4 * a.num_seqs ? 4 : 1;
+  const long long v_items = (long long)((a.total_tokens + v_group - 1) / v_group) * hkv;
+  const long long v_blocks = (v_items + block / 64 - 1) / (block / 64);
+  if (qk_blocks + v_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const unsigned grid = (unsigned)(qk_blocks + v_blocks);
+  const size_t lds = (size_t)(block / 64) * 4 * D * esz;
   if (a.layout == NK_ROPE_INTERLEAVED)
-    rope_write_kernel<TIn, CACHE, true><<<(unsigned)grid, block, 0, stream>>>(a);
+    rope_write_kernel<TIn, CACHE, true><<<grid, block, lds, stream>>>(a, upt, bpt, (int)v_blocks, v_group);
   else
-    rope_write_kernel<TIn, CACHE, false><<<(unsigned)grid, block, 0, stream>>>(a);
+    rope_write_kernel<TIn, CACHE, false><<<grid, block, lds, stream>>>(a, upt, bpt, (int)v_blocks, v_group);
   return hipGetLastError();
 }
 

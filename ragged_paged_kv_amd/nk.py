@@ -244,8 +244,17 @@ def attention_lse_merge(partial_out, partial_lse, merge_offsets, out, lse_out=No
     return out, lse_out
 
 
-def profile_enable(on=True):
-    lib().nk_profile_enable(1 if on else 0)
+PROFILE_FAMILIES = ("rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge")
+
+
+def profile_enable(on=True, families=None):
+    """Bracket the launches of `families` (default: all) with HIP events;
+    on=False turns timing off."""
+    fams = PROFILE_FAMILIES if families is None else families
+    mask = 0
+    for f in fams:
+        mask |= 1 << PROFILE_FAMILIES.index(f)
+    _check(lib().nk_profile_enable(mask if on else 0), "nk_profile_enable")
 
 
 def profile_reset():

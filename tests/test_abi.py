@@ -128,3 +128,7 @@ def test_profile_api_without_gpu(L):
     assert L.nk_profile_enable(0) == 0
     ms, n = nk.profile_read("attn_decode")
     assert n == 0 and ms == 0.0
+    assert L.nk_profile_enable(1 << 5) == nk.NK_ERR_INVALID_ARG       # no such family
+    assert L.nk_profile_enable(-1) == nk.NK_ERR_INVALID_ARG
+    nk.profile_enable(True, ["attn_decode", "lse_merge"])             # host-side only, no launch
+    nk.profile_enable(False)
