@@ -36,9 +36,11 @@
 #include "internal.h"
 
 // Pages in flight per wave and the waves-per-SIMD the register allocation
-// aims for (compile-time; chosen by measurement on MI355X).
+// aims for (compile-time; chosen by measurement on MI355X).  More bf16 pages
+// in flight only lengthen the memory queues: 2 waves x 2 pages per SIMD read
+// the batched-decode pages 3-4 % faster than 2 x 4 or 1 x 8.
 #ifndef NK_DECODE_NPF_BF16
-#define NK_DECODE_NPF_BF16 4
+#define NK_DECODE_NPF_BF16 2
 #endif
 #ifndef NK_DECODE_NPF_FP8
 #define NK_DECODE_NPF_FP8 6
