@@ -36,16 +36,17 @@ int check_cache(const nk_paged_kv_t *c) {
 }
 
 // Keys per split-KV chunk of a decode row: about 4096 single-wave work items
-// over the batch (four per SIMD of a 256-CU part, all resident at once),
-// chunks of 128..4096 keys, a multiple of 32.
+// over the batch at head_dim 128 (four per SIMD of a 256-CU part, all
+// resident at once), proportionally fewer for wider heads (each step moves
+// more bytes), chunks of 128..4096 keys, a multiple of 32.
 int split_tokens(int num_seqs, int max_kv_len, int hq, int hkv, int head_dim, int window_left,
                  int requested) {
-  (void)head_dim;
   if (requested > 0) return requested;
   const long long span = window_left < 0 ? max_kv_len : std::min<long long>(max_kv_len, (long long)window_left + 32);
   if (span <= 0) return 128;
   const long long rows = (long long)std::max(num_seqs, 1) * hkv * ((hq / hkv + 15) / 16);
-  const long long per_row = std::max(1LL, 4096 / std::max(1LL, rows));
+  const long long target = 4096LL * 128 / std::max(head_dim, 1);
+  const long long per_row = std::max(1LL, target / std::max(1LL, rows));
   long long s = (span + per_row - 1) / per_row;
   s = std::max(128LL, std::min(4096LL, s));
   return (int)((s + 31) / 32 * 32);

@@ -45,6 +45,9 @@
 #ifndef NK_DECODE_NPF_FP8
 #define NK_DECODE_NPF_FP8 6
 #endif
+#ifndef NK_DECODE_NPF_D256        // head_dim 256: a second page in flight spills
+#define NK_DECODE_NPF_D256 1
+#endif
 #ifndef NK_DECODE_WAVES_PER_EU
 #define NK_DECODE_WAVES_PER_EU 2
 #endif
@@ -401,7 +404,7 @@ attn_decode_kernel(AttnArgs a) {
 
 template <int D, int P, bool FP8>
 hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
-  constexpr int NPF = D == 256 ? 2 : (FP8 ? NK_DECODE_NPF_FP8 : NK_DECODE_NPF_BF16);
+  constexpr int NPF = D == 256 ? NK_DECODE_NPF_D256 : (FP8 ? NK_DECODE_NPF_FP8 : NK_DECODE_NPF_BF16);
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
   dim3 grid((unsigned)(a.num_seqs * a.max_chunks * hkv), (unsigned)((G + 15) / 16), 1);

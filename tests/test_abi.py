@@ -109,6 +109,10 @@ def test_workspace_and_split_queries(L):
     s = L.nk_ragged_paged_attention_split_tokens(32, 4096, 32, 8, 128, -1, 0)
     assert s % 32 == 0 and 128 <= s <= 4096
     assert L.nk_ragged_paged_attention_split_tokens(32, 4096, 32, 8, 128, -1, 512) == 512
+    # wider heads move more bytes per key: fewer, longer chunks
+    s128 = L.nk_ragged_paged_attention_split_tokens(64, 8192, 16, 8, 128, 1023, 0)
+    s256 = L.nk_ragged_paged_attention_split_tokens(64, 8192, 16, 8, 256, 1023, 0)
+    assert s256 > s128 and s256 % 32 == 0 and s128 % 32 == 0
     # a window bounds the visible keys, so the chunk count and workspace shrink
     ws_full = L.nk_ragged_paged_attention_workspace_size(nk.NK_BF16, nk.NK_BF16, 8, 8, 1, 100000, 4, 2, 128, -1, 512)
     ws_win = L.nk_ragged_paged_attention_workspace_size(nk.NK_BF16, nk.NK_BF16, 8, 8, 1, 100000, 4, 2, 128, 1023, 512)
