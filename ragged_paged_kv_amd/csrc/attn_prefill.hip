@@ -453,7 +453,9 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
   // K(it+1) and V(it); the loads of group 0 (L(it), after its V(it)) and of
   // group 1 (L(it+1), after its V(it), i.e. during group 0's M(it+1)) write
   // the other buffers.
-  const int grp = wv >= NW / 2 ? 1 : 0;
+  // (only where two waves share a SIMD: with 4 waves per work-group each
+  // SIMD holds one, and an offset group would only wait)
+  const int grp = NW >= 8 && wv >= NW / 2 ? 1 : 0;
   if (grp) {
     load_step(t0 - 1);
     __syncthreads();
