@@ -159,15 +159,17 @@ def test_empty_batch_is_a_no_op():
     assert out.shape[0] == 0
 
 
-def test_lse_merge_entry_point():
+@pytest.mark.parametrize("D", [128, 64, 130, 256, 512])
+def test_lse_merge_entry_point(D):
     rng = np.random.default_rng(7)
-    n, H, D = 23, 5, 128
+    n, H = 93, 5
     po = rng.standard_normal((n, H, D)).astype(np.float32)
     pl = (rng.standard_normal((n, H)) * 4).astype(np.float32)
     pl[3, 2] = -np.inf
     pl[10:12, :] = -np.inf
-    offs = np.array([0, 3, 3, 10, 12, 23], dtype=np.int32)      # an empty row, an all -inf row
-    gu.say("lse merge entry point")
+    # an empty row, an all -inf row, and a row of 70 chunks (more than a wave's lanes)
+    offs = np.array([0, 3, 3, 10, 12, 23, 93], dtype=np.int32)
+    gu.say(f"lse merge entry point, head_dim {D}")
     for dt in (torch.float32, torch.bfloat16):
         out = torch.empty(len(offs) - 1, H, D, dtype=dt, device="cuda")
         lse = torch.empty(len(offs) - 1, H, dtype=torch.float32, device="cuda")
