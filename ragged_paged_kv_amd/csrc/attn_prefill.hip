@@ -250,18 +250,20 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
   // pages of the K tile last requested: the V tile requested one step later
   // is the same tile
   size_t pgk[PER];
-  auto load_k = [&](int tile) {
+  // K of `tile` into the given staging registers
+  auto load_k_to = [&](int tile, Raw (&dst)[PER], float &dss) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) pgk[i] = page_of(tile, pit[i]);
     __builtin_amdgcn_sched_barrier(0);     // all page lookups in flight together
 #pragma unroll
-    for (int i = 0; i < PER; ++i) kst[i] = *(const Raw *)(kb + pgk[i] * page_bytes + kg[i]);
+    for (int i = 0; i < PER; ++i) dst[i] = *(const Raw *)(kb + pgk[i] * page_bytes + kg[i]);
     if (FP8 && tid < BN) {
       const int key = tile * BN + 32 * (tid >> 5) + perm_key(tid & 31);
       const int page = pt[min(key / P, last_page)];
-      kss = a.cache.k_scales[((size_t)page * hkv + g) * P + key % P];
+      dss = a.cache.k_scales[((size_t)page * hkv + g) * P + key % P];
     }
   };
+  auto load_k = [&](int tile) { load_k_to(tile, kst, kss); };
   // V of `tile` through the given pages
   auto load_v = [&](const size_t (&pg)[PER]) {
 #pragma unroll
@@ -272,15 +274,16 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
       }
     }
   };
-  auto store_k = [&](int buf) {
+  auto store_k_from = [&](int buf, const Raw (&src)[PER], float sss) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       bf16x8_t x;
-      if constexpr (FP8) x = fp8x8_to_bf16x8(kst[i]); else x = kst[i];
+      if constexpr (FP8) x = fp8x8_to_bf16x8(src[i]); else x = src[i];
       *(bf16x8_t *)(lds + buf * C::KBUF + kl[i]) = x;
     }
-    if (FP8 && tid < BN) ((float *)(lds + C::KS_OFF + buf * C::SBUF))[tid] = kss;
+    if (FP8 && tid < BN) ((float *)(lds + C::KS_OFF + buf * C::SBUF))[tid] = sss;
   };
+  auto store_k = [&](int buf) { store_k_from(buf, kst, kss); };
   // e4m3 V enters LDS as bf16(code * scale); keys >= L become zeros (their
   // slots may hold anything, and 0 * NaN is NaN)
   auto store_v = [&](int buf, int tile) {
@@ -434,15 +437,18 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
     if (t + 2 <= t1) load_v(pgv);
   };
 
-  // ---- prologue: K(t0) in LDS; K(t0+1), V(t0) staged
-  load_k(t0);
-  store_k(t0 & 1);
+  // ---- prologue: K(t0) in LDS; K(t0+1), V(t0) staged.  All three are
+  // requested before the first is waited for.
   {
+    Raw k0[PER];
+    float ks0 = 0.f;
+    load_k_to(t0, k0, ks0);
     size_t pgv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) pgv[i] = pgk[i];
     if (t0 + 1 <= t1) load_k(t0 + 1);
     load_v(pgv);
+    store_k_from(t0 & 1, k0, ks0);
   }
   __syncthreads();
 
