@@ -130,7 +130,8 @@ NK_DEVICE float dot2_ones(uint32_t pk, float acc) {
 // heads of head block hy (KV head hy / HB).  Every thread of the work-group
 // calls it with the same arguments.
 template <int D, int P, bool FP8, int NW>
-NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, uint8_t *lds) {
+NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, int q_len, int L, int hy,
+                            uint8_t *lds) {
   using C = Cfg<D, P, FP8, NW>;
   constexpr int NT = C::NT;
   constexpr int KD = D / 16;      // k-steps of the score MFMA (16 dims each)
@@ -147,10 +148,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int hy, ui
   const int g = hy / HB;
   const int hblk = hy % HB;
 
-  const int q0 = a.q_offsets[s];
-  const int q_len = a.q_offsets[s + 1] - q0;
   const int r0 = qb * BM;
-  const int L = a.kv_lens[s];
   const int shift = L - q_len;                // row r sits at position r + shift
   const int r_last = min(r0 + BM, q_len) - 1;
   const int kmax_wg = min(r_last + shift, L - 1);
@@ -572,7 +570,7 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
   __shared__ int part[kPlanThreads / 64];
   int32_t *sc = a.sched;
   int32_t *segoff = sc + kSchedSegOff;
-  int2 *items = (int2 *)(sc + sched_items_offset(a.num_seqs));
+  int4 *items = (int4 *)(sc + sched_items_offset(a.num_seqs));   // two int4 per item
   const int tid = threadIdx.x;
   for (int i = tid; i < kPlanBins; i += kPlanThreads) hist[i] = 0;
   if (tid < kSchedQueues) sc[tid * kSchedCounterStride] = 0;
@@ -619,14 +617,18 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
     const int qb = i - segoff[s];
     const int w = item_tiles(a, BM, s, qb);
     const int pos = atomicAdd(&hist[kPlanBins - 1 - min(w, kPlanBins - 1)], 1);
-    items[pos] = int2{s, qb};
+    const int q0 = a.q_offsets[s];
+    items[2 * pos] = int4{s, qb, q0, a.q_offsets[s + 1] - q0};
+    items[2 * pos + 1] = int4{a.kv_lens[s], 0, 0, 0};
   }
 }
 
 // Persistent prefill: each work-group takes work units from its queue until
 // the queue is empty.  Queue q serves the work-groups with blockIdx % NQ == q
 // (one queue per XCD under round-robin dispatch, so that the head blocks of
-// one queue share that XCD's L2); a unit is (item, head block).
+// one queue share that XCD's L2); a unit is (item, head block).  An item
+// record carries its segment's row offset, row count and key count, so a
+// unit starts after one read.
 template <int D, int P, bool FP8, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
@@ -637,7 +639,7 @@ attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
   const int NHq = NH / NQ;                      // of them in this queue
   const int q = blockIdx.x % NQ;
   int32_t *ctr = a.sched + q * kSchedCounterStride;
-  const int2 *items = (const int2 *)(a.sched + sched_items_offset(a.num_seqs));
+  const int4 *items = (const int4 *)(a.sched + sched_items_offset(a.num_seqs));
   const long long units = (long long)a.sched[kSchedCount] * NHq;
   if (threadIdx.x == 0) unit_slot = atomicAdd(ctr, 1);
   __syncthreads();
@@ -646,8 +648,9 @@ attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
     __syncthreads();                            // every thread has read unit_slot
     int next = 0;
     if (threadIdx.x == 0) next = atomicAdd(ctr, 1);   // in flight while the item runs
-    const int2 it = items[u / NHq];
-    prefill_item<D, P, FP8, NW>(a, GW, it.x, it.y, q + NQ * (u % NHq), lds);
+    const int4 rec = items[2 * (u / NHq)];      // {segment, q-block, q0, q_len}
+    const int kv = items[2 * (u / NHq) + 1].x;
+    prefill_item<D, P, FP8, NW>(a, GW, rec.x, rec.y, rec.z, rec.w, kv, q + NQ * (u % NHq), lds);
     if (threadIdx.x == 0) unit_slot = next;
     __syncthreads();
     u = unit_slot;

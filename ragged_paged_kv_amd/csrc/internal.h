@@ -37,7 +37,8 @@ struct AttnArgs {
   float *part_out;          // [num_seqs * max_chunks][hq][D]
   float *part_lse;          // [num_seqs * max_chunks][hq]
   // prefill work list (workspace): queue counters, item count, per-segment
-  // item offsets and the (segment, q-block) items, heaviest first
+  // item offsets and the items, heaviest first (segment, q-block and the
+  // segment's row offset, row count and key count)
   int32_t *sched;
   int32_t sched_items_max;
 };
@@ -47,13 +48,14 @@ constexpr int kSchedQueues = 8;               // one work queue per XCD
 constexpr int kSchedCounterStride = 32;       // one 128-byte line per counter
 constexpr int kSchedCount = kSchedQueues * kSchedCounterStride;   // item count
 constexpr int kSchedSegOff = kSchedCount + 64;                    // [num_seqs + 1]
-__host__ __device__ inline size_t sched_items_offset(int num_seqs) {                  // int2 items
+constexpr int kSchedItemInts = 8;             // {s, q-block, q0, q_len, kv_len, 0, 0, 0}
+__host__ __device__ inline size_t sched_items_offset(int num_seqs) {                  // 32-byte items
   return ((size_t)kSchedSegOff + num_seqs + 1 + 63) / 64 * 64;
 }
 // q-blocks of a prefill batch: at most one per 32 rows plus one per segment
 __host__ __device__ inline int sched_items_max(int num_seqs, int total_q) { return total_q / 32 + num_seqs + 1; }
 __host__ __device__ inline size_t sched_bytes(int num_seqs, int total_q) {
-  return (sched_items_offset(num_seqs) + 2 * (size_t)sched_items_max(num_seqs, total_q)) * 4;
+  return (sched_items_offset(num_seqs) + (size_t)kSchedItemInts * sched_items_max(num_seqs, total_q)) * 4;
 }
 
 // Each launcher enqueues its kernel(s) on `stream` and returns a
