@@ -62,9 +62,19 @@
 #ifndef NK_PREFILL_NW
 #define NK_PREFILL_NW 8
 #endif
-// LDS operand reads in flight ahead of the MFMA that consumes them
+// head_dim 256: the output dimensions of a row block are split over this
+// many waves, each computing the full scores (1 = no split, 4 waves per
+// work-group; 2 = 8 waves, two per SIMD, each holding half of O)
+#ifndef NK_PREFILL_D256_SPLIT
+#define NK_PREFILL_D256_SPLIT 2
+#endif
+// LDS operand reads in flight ahead of the MFMA that consumes them (head
+// dims up to 128; 256 has no registers to spare)
 #ifndef NK_PREFILL_LDS_AHEAD
 #define NK_PREFILL_LDS_AHEAD 4
+#endif
+#ifndef NK_PREFILL_LDS_AHEAD_D256
+#define NK_PREFILL_LDS_AHEAD_D256 2
 #endif
 
 namespace nk {
@@ -135,7 +145,8 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   using C = Cfg<D, P, FP8, NW>;
   constexpr int NT = C::NT;
   constexpr int KD = D / 16;      // k-steps of the score MFMA (16 dims each)
-  constexpr int DT = D / 32;      // 32-dim tiles of the output MFMA
+  constexpr int DH = D == 256 ? NK_PREFILL_D256_SPLIT : 1;   // waves sharing a row block's output dims
+  constexpr int DT = D / 32 / DH; // 32-dim tiles of the output MFMA held by a wave
   constexpr int PER = C::PER;
   constexpr int NPG = C::NPG;
   using Raw = typename std::conditional<FP8, u32x2_t, bf16x8_t>::type;
@@ -143,7 +154,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
   const int HB = G / GW;                      // head blocks per KV head
-  const int TB = NW / GW;                     // 32-row blocks per work-group
+  const int TB = NW / (GW * DH);              // 32-row blocks per work-group
   const int BM = 32 * TB;
   const int g = hy / HB;
   const int hblk = hy % HB;
@@ -168,7 +179,8 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = wv % GW;
-  const int tb = wv / GW;
+  const int dh = (wv / GW) % DH;              // which part of the output dims
+  const int tb = wv / (GW * DH);
   const int head = g * G + hblk * GW + hl;
   const int rw = r0 + 32 * tb;                // wave's first row
   const int qcol = lane & 31;                 // this lane's query row (column of S^T)
@@ -310,7 +322,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
 
   // ---- MFMA operand bases: per-lane base plus immediates
   const uint8_t *klane = lds + qcol * C::KROW + 16 * half;
-  const uint8_t *vlane = lds + C::V_OFF + qcol * C::VROW + 16 * half;
+  const uint8_t *vlane = lds + C::V_OFF + (dh * DT * 32 + qcol) * C::VROW + 16 * half;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t o[DT];
@@ -334,7 +346,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     const uint8_t *vt = vlane + (t & 1) * C::VBUF;
     auto kop = [&](int i) { return *(const bf16x8_t *)(kt + (i / KD) * 32 * C::KROW + 32 * (i % KD)); };
     auto vop = [&](int i) { return *(const bf16x8_t *)(vt + (i % DT) * 32 * C::VROW + 32 * (i / DT)); };
-    constexpr int NS = 2 * KD, NP = 4 * DT, AH = NK_PREFILL_LDS_AHEAD;
+    constexpr int NS = 2 * KD, NP = 4 * DT, AH = D == 256 ? NK_PREFILL_LDS_AHEAD_D256 : NK_PREFILL_LDS_AHEAD;
     bf16x8_t ring[AH];
 #pragma unroll
     for (int i = 0; i < AH; ++i) ring[i] = i < NS ? kop(i) : vop(i - NS);
@@ -501,9 +513,9 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
       bf16x4_t ov;
 #pragma unroll
       for (int r = 0; r < 4; ++r) ov[r] = (bf16_t)(o[dt][4 * j + r] * inv);
-      *(bf16x4_t *)(orow + 32 * dt + 8 * j + 4 * half) = ov;
+      *(bf16x4_t *)(orow + 32 * (dh * DT + dt) + 8 * j + 4 * half) = ov;
     }
-  if (a.lse && half == 0)
+  if (a.lse && half == 0 && dh == 0)
     a.lse[(size_t)(q0 + my_row) * a.hq + head] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
 }
 
@@ -630,7 +642,7 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
 // record carries its segment's row offset, row count and key count, so a
 // unit starts after one read.
 template <int D, int P, bool FP8, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 1 : 2)))
 attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int unit_slot;
@@ -665,13 +677,14 @@ DeviceShape &device_shape(int dev) {
 
 template <int D, int P, bool FP8>
 hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
-  constexpr int NW = D == 256 ? 4 : NK_PREFILL_NW;
+  constexpr int DH = D == 256 ? NK_PREFILL_D256_SPLIT : 1;
+  constexpr int NW = D == 256 ? 4 * DH : NK_PREFILL_NW;
   using C = Cfg<D, P, FP8, NW>;
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
   int GW = 1;                                  // heads per work-group: power of 2 dividing G
-  while (GW * 2 <= NW && G % (GW * 2) == 0) GW *= 2;
-  const int BM = 32 * (NW / GW);
+  while (GW * 2 * DH <= NW && G % (GW * 2) == 0) GW *= 2;
+  const int BM = 32 * (NW / (GW * DH));
   const int NH = hkv * (G / GW);
   const int NQ = NH % kSchedQueues == 0 ? kSchedQueues : 1;
   if (!a.sched) return hipErrorInvalidValue;
