@@ -22,11 +22,13 @@
 //     v_mfma_f32_16x16x16_bf16: the score tile's lane layout (lane holds keys
 //     4*(lane/16)..+3 of head lane%16) is exactly the P^T operand's, so the
 //     probabilities never move between lanes;
-//   * K pages are stored in 32-dim blocks ([dim/32][token][32]) and V pages
-//     dimension-major ([dim][token]): each MFMA operand load of a wave is one
-//     contiguous 1 KiB (bf16) / 512 B (e4m3) block of K or 512 B / 256 B of
-//     V, read straight from HBM into registers; e4m3 codes widen to bf16
-//     exactly in registers;
+//   * K pages are stored in blocks of 32 dims (64 for e4m3, the two 32-dim
+//     halves interleaved in 8-element runs) and V pages as 16-byte runs in
+//     the lane order of the V^T operand (include/nk.h): every load
+//     instruction of a wave reads one contiguous 1 KiB with 16 bytes per
+//     lane, which hold 1 (bf16) or 2 (e4m3) K operands or 2 (bf16) or 4
+//     (e4m3) V operands, straight from HBM into registers with non-temporal
+//     loads; e4m3 codes widen to bf16 exactly in registers;
 //   * a ring of NPF pages is in flight per wave: page i+NPF is requested
 //     before page i is consumed;
 //   * the row's final output (one chunk) or a float32 partial (several

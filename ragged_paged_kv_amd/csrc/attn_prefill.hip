@@ -12,8 +12,9 @@
 //
 // Design (MFMA-bound):
 //   * a work-group owns BM query rows of one segment and GW query heads of one
-//     KV head (GW * BM/32 = waves; each wave owns 32 rows of one head), so
-//     every K/V tile staged in LDS serves all GW heads;
+//     KV head (each wave owns 32 rows of one head; at head_dim 256 two waves
+//     share a row block, each computing the full scores and holding half of
+//     the output dims), so every K/V tile staged in LDS serves all GW heads;
 //   * KV tiles of 64 keys (four 16-token or two 32-token pages).  Each page's
 //     K or V block of one head is contiguous in the cache, so a wave's load
 //     instruction reads one contiguous 1 KiB (bf16) piece of one page, at a
@@ -28,19 +29,20 @@
 //     swapped) that makes the score tile's lane layout the P^T operand layout
 //     of the second product O^T += V^T P^T (32 dims x 32 rows), so the
 //     probabilities never leave their lanes;
-//   * software pipeline: K runs one tile ahead of V.  While the softmax of
-//     tile t runs on the VALU, the score MFMAs of tile t+1 are in flight;
-//     K and V tiles are double-buffered, the global loads of tiles t+3 (K)
-//     and t+2 (V) are in flight during iteration t, and one barrier per tile
-//     separates the buffers' writers from their readers;
+//   * software pipeline: K runs one tile ahead of V; K and V tiles are
+//     double-buffered and the global loads of tiles t+3 (K) and t+2 (V) are
+//     in flight during iteration t.  Where two waves share a SIMD (8 waves
+//     per work-group) they run one barrier apart: while one issues the score
+//     and P.V MFMAs of its tile, the other runs its softmax and tile loads;
 //   * online softmax in the exp2 domain, one fused multiply-add and one exp
 //     per score; the running maximum is replaced only when the tile's
 //     maximum exceeds it by more than 2^8 (exact either way: each term is
 //     exp2(x - m_used)); the normaliser sums the probabilities as rounded to
 //     bf16 for the P.V product (v_dot2_f32_bf16 on the packed pairs);
-//   * segments' q-blocks are dispatched heaviest-first, and consecutive
-//     work-groups take the KV heads of one q-block so that the groups of one
-//     KV head land on one XCD (round-robin dispatch) and share its L2.
+//   * persistent work-groups: a one-work-group plan kernel lists every
+//     (segment, q-block) item, heaviest first, with the segment's offsets;
+//     work-groups pull (item, head block) units from one atomic queue per
+//     XCD, so the head blocks of a queue share that XCD's L2.
 
 #include "common.h"
 #include "internal.h"
