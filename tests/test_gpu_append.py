@@ -32,6 +32,9 @@ CASES = {
                                       rotary_dim=128),
     "e4m3_d64_p32_decode": dict(q_lens=[1] * 6, kv_lens=[1, 2, 3, 4, 5, 64], num_q_heads=4, num_kv_heads=1,
                                 head_dim=64, page_size=32, cache_dtype="e4m3", explicit_positions=False),
+    # 136 heads x 8 units per token: a token's Q/K units span two work-groups
+    "bf16_d128_hq128_two_blocks_per_token": dict(q_lens=[3, 6], kv_lens=[10, 6], num_q_heads=128,
+                                                 num_kv_heads=8, head_dim=128),
 }
 
 
