@@ -26,6 +26,7 @@ of the same number of steps times all kernels for the per-kernel table.
 """
 
 import argparse
+import ctypes
 import glob
 import hashlib
 import json
@@ -39,6 +40,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
 FLUSH_BYTES = 1 << 30
+HIP_EVENT_NO_SYSTEM_FENCE = 0x20000000     # hipEventDisableSystemFence
 
 METRIC = "decode KV GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)"
 DESCR = {
@@ -131,6 +133,41 @@ def prepare(name):
     return st
 
 
+class StepEvent:
+    """A HIP event for timing only (no system-scope fence when recorded, so
+    recording it neither writes back nor invalidates the caches), recorded
+    on torch's current stream."""
+
+    _hip = None
+
+    def __init__(self):
+        if StepEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            StepEvent._hip = hip
+        self.ev = ctypes.c_void_p()
+        rc = StepEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), HIP_EVENT_NO_SYSTEM_FENCE)
+        assert rc == 0, f"hipEventCreateWithFlags: {rc}"
+
+    def record(self):
+        import torch
+        rc = StepEvent._hip.hipEventRecord(self.ev, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0, f"hipEventRecord: {rc}"
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        rc = StepEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        assert rc == 0, f"hipEventElapsedTime: {rc}"
+        return ms.value
+
+    def __del__(self):
+        if self.ev:
+            StepEvent._hip.hipEventDestroy(self.ev)
+
+
 def measure(st, steps, warmup, flush, split=None):
     """Time `steps` hot-path steps on prepared inputs (see module doc)."""
     import torch
@@ -161,7 +198,7 @@ def measure(st, steps, warmup, flush, split=None):
         nk.profile_reset()
         if families:
             nk.profile_enable(True, families)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
+        evs = [(StepEvent(), StepEvent()) for _ in range(nsteps)]
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         for i in range(nsteps):

@@ -94,6 +94,11 @@ WorkspacePlan plan_workspace(int q_dtype, int cache_dtype, int num_seqs, int tot
 }
 
 // ------------------------------------------------------------------ profiling
+// Timing-only events: no system-scope fence when recorded (no cache
+// writeback and invalidation around the bracketed launch, which would cost
+// the stream time and the kernel its warm caches).
+constexpr unsigned kProfileEventFlags = hipEventDisableSystemFence;
+
 struct ProfileState {
   std::mutex mu;
   int mask = 0;
@@ -142,7 +147,9 @@ ProfileScope::ProfileScope(const char *family, hipStream_t s) : slot(-1), stream
     if (p.recs.size() >= 4096) flush_pending(p), idx = 0;
     else {
       ProfileState::Rec r{family, nullptr, nullptr, false};
-      if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
+      if (hipEventCreateWithFlags(&r.a, kProfileEventFlags) != hipSuccess ||
+          hipEventCreateWithFlags(&r.b, kProfileEventFlags) != hipSuccess)
+        return;
       p.recs.push_back(r);
       idx = (int)p.recs.size() - 1;
     }
