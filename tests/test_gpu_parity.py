@@ -45,6 +45,11 @@ CASES = {
     "f32_mixed_d128_p32": dict(q_lens=[9, 1, 30], kv_lens=[9, 77, 45], num_q_heads=6, num_kv_heads=2,
                                head_dim=128, page_size=32, in_dtype="f32", cache_dtype="f32"),
     "prefill_g3_d128": dict(q_lens=[65, 2], kv_lens=[65, 2], num_q_heads=6, num_kv_heads=2, head_dim=128),
+    # head_dim 256 work-groups: 1, 2 or 4 heads x 4, 2 or 1 row blocks x 2 output halves
+    "prefill_d256_mha_p16": dict(q_lens=[150, 37], kv_lens=[150, 60], num_q_heads=2, num_kv_heads=2,
+                                 head_dim=256),
+    "prefill_d256_g8_fp8": dict(q_lens=[70, 5], kv_lens=[100, 5], num_q_heads=16, num_kv_heads=2,
+                                head_dim=256, page_size=32, cache_dtype="e4m3"),
 }
 
 
