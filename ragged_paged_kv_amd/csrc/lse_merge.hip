@@ -9,8 +9,10 @@
 // rows whose chunks are all empty (-inf) give zeros and -inf.
 //
 // Design: one wave per (row, head), the heads of a row on consecutive
-// work-groups (their partials are adjacent); four 16-lane groups stream
-// every fourth chunk, lanes over head dimensions -- HBM-bound.  Two
+// work-groups (their partials are adjacent); four 16-lane groups take every
+// fourth chunk, lanes over head dimensions.  A call moves little data, so
+// its time is the chain of dependent memory accesses, kept to: row bounds,
+// then the partials and their lse values together, then the output.  Two
 // row->partials maps: explicit merge offsets (the public entry point) and
 // the split-KV decode layout (chunks of a decode row at row*max_chunks).
 
@@ -30,69 +32,66 @@ template <> NK_DEVICE void store2<bf16_t>(bf16_t *p, float a, float b) {
 
 // Merge `n` partials starting at `first` (stride `heads` between chunks) for
 // head `h`; write row `out_row`.  The wave splits into four 16-lane groups
-// that take every fourth chunk (two of them in flight per group), each lane
-// holding MAXP pairs of dimensions 2(l + 16 r), r < MAXP; the groups' sums
-// are added across lanes at the end.  The maximum lse and the weight sum are
-// wave reductions over the chunks' lse values read by the lanes in parallel.
+// that take every fourth chunk, each lane holding MAXP pairs of dimensions
+// 2(l + 16 r), r < MAXP; the groups' sums are added across lanes at the end.
+// Latency-bound: the first batch of partial outputs (4 chunks per group) is
+// requested together with the chunks' lse values, so a row of up to 16
+// chunks costs one memory round trip after its chunk count is known.  Lane
+// i holds chunk i's lse and weight; a group reads its chunks' weights from
+// those lanes.
 template <typename TOut, int MAXP>
 NK_DEVICE void merge_row(const float *__restrict__ po, const float *__restrict__ pl, long long first,
                          int n, int heads, int h, int D, TOut *__restrict__ out_row,
                          float *__restrict__ lse_out) {
+  constexpr int CB = 4;                       // chunks per group and batch
   const int lane = threadIdx.x;
   const int grp = lane >> 4, l16 = lane & 15;
-  float M = -INFINITY;
-  for (int b = 0; b < n; b += kWave) {
-    const int i = b + lane;
-    if (i < n) M = fmaxf(M, pl[(first + i) * heads + h]);
-  }
+  f32x2_t v[CB][MAXP];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+      const int c = c0 + grp + 4 * k;
+      const float *o = po + ((first + c) * heads + h) * (long long)D;
+#pragma unroll
+      for (int r = 0; r < MAXP; ++r) {
+        const int d = 2 * (l16 + 16 * r);
+        v[k][r] = c < n && d < D ? *(const f32x2_t *)(o + d) : f32x2_t{0.f, 0.f};
+      }
+    }
+  };
+  auto lse_of = [&](int c) { return pl[(first + c) * heads + h]; };
+  load_batch(0);
+  const float l0 = lane < n ? lse_of(lane) : -INFINITY;
+  float M = l0;
+  for (int b = kWave; b < n; b += kWave)
+    if (b + lane < n) M = fmaxf(M, lse_of(b + lane));
   M = wave_max(M);
   f32x2_t acc[MAXP];
 #pragma unroll
   for (int r = 0; r < MAXP; ++r) acc[r] = f32x2_t{0.f, 0.f};
   float tot = 0.f;
   if (M != -INFINITY) {
-    for (int b = 0; b < n; b += kWave) {
-      const int i = b + lane;
-      const float li = i < n ? pl[(first + i) * heads + h] : -INFINITY;
-      tot += li == -INFINITY ? 0.f : expf(li - M);
-    }
-    tot = wave_sum(tot);
-    auto weight = [&](int c) {
-      const float lc = pl[(first + c) * heads + h];          // same address across the group
-      return lc == -INFINITY ? 0.f : expf(lc - M);
-    };
-    int c = grp;
-    for (; c + 4 < n; c += 8) {
-      const float w0 = weight(c), w1 = weight(c + 4);
-      const float *o0 = po + ((first + c) * heads + h) * (long long)D;
-      const float *o1 = po + ((first + c + 4) * heads + h) * (long long)D;
-      f32x2_t v0[MAXP], v1[MAXP];
+    auto weight_of = [&](float lc) { return lc == -INFINITY ? 0.f : expf(lc - M); };
+    const float w0 = weight_of(l0);           // chunk `lane` (0 past n)
+    float ws = w0;
+    for (int b = kWave; b < n; b += kWave)
+      if (b + lane < n) ws += weight_of(lse_of(b + lane));
+    tot = wave_sum(ws);
+    for (int c0 = 0;;) {
 #pragma unroll
-      for (int r = 0; r < MAXP; ++r) {
-        const int d = 2 * (l16 + 16 * r);
-        v0[r] = d < D ? *(const f32x2_t *)(o0 + d) : f32x2_t{0.f, 0.f};
-        v1[r] = d < D ? *(const f32x2_t *)(o1 + d) : f32x2_t{0.f, 0.f};
-      }
+      for (int k = 0; k < CB; ++k) {
+        const int c = c0 + grp + 4 * k;
+        const float wl = __shfl(w0, c & (kWave - 1), kWave);          // every lane takes part
+        const float w = c >= n ? 0.f : (c < kWave ? wl : weight_of(lse_of(c)));
 #pragma unroll
-      for (int r = 0; r < MAXP; ++r) {
-        acc[r][0] = fmaf(w0, v0[r][0], acc[r][0]);
-        acc[r][1] = fmaf(w0, v0[r][1], acc[r][1]);
-        acc[r][0] = fmaf(w1, v1[r][0], acc[r][0]);
-        acc[r][1] = fmaf(w1, v1[r][1], acc[r][1]);
-      }
-    }
-    if (c < n) {
-      const float w0 = weight(c);
-      const float *o0 = po + ((first + c) * heads + h) * (long long)D;
-#pragma unroll
-      for (int r = 0; r < MAXP; ++r) {
-        const int d = 2 * (l16 + 16 * r);
-        if (d < D) {
-          const f32x2_t v = *(const f32x2_t *)(o0 + d);
-          acc[r][0] = fmaf(w0, v[0], acc[r][0]);
-          acc[r][1] = fmaf(w0, v[1], acc[r][1]);
+        for (int r = 0; r < MAXP; ++r) {
+          acc[r][0] = fmaf(w, v[k][r][0], acc[r][0]);
+          acc[r][1] = fmaf(w, v[k][r][1], acc[r][1]);
         }
       }
+      c0 += 4 * CB;
+      if (c0 >= n) break;
+      load_batch(c0);
     }
     // the four groups hold the same dimensions: lanes l, l^16, l^32, l^48
 #pragma unroll
@@ -130,9 +129,9 @@ template <typename TOut, int MAXP>
 __global__ void __launch_bounds__(64) decode_merge_kernel(AttnArgs a) {
   const int h = (int)(blockIdx.x % (unsigned)a.hq), s = (int)(blockIdx.x / (unsigned)a.hq);     // heads fastest
   const int q0 = a.q_offsets[s];
-  if (a.q_offsets[s + 1] - q0 != 1) return;
-  const int L = a.kv_lens[s];
-  if (L <= 0) return;
+  const int q1 = a.q_offsets[s + 1];
+  const int L = a.kv_lens[s];                 // requested with the offsets
+  if (q1 - q0 != 1 || L <= 0) return;
   const int hi = L - 1;
   const int lo = a.window_left < 0 ? 0 : max(0, hi - a.window_left);
   const int c0 = (lo / 32) * 32;              // the decode kernel's chunk origin
