@@ -19,10 +19,11 @@ read (outside the step's events) so that the 256 MB Infinity Cache and the
 L2s hold none of the step's inputs -- a read, not a write, so that the step
 does not pay for writing back someone else's dirty lines; each step is timed
 with HIP events on the step's stream and ms_per_step is the median.  Kernel
-durations come from the library's own event pairs around each launch
-(nk_profile_*): inside the timed region only the workload's dominant kernels
-carry them (every pair costs the stream a few microseconds); a second pass
-of the same number of steps times all kernels for the per-kernel table.
+durations come from the library's own events, attached to the kernels'
+dispatches (nk_profile_*): inside the timed region only the workload's
+dominant kernels carry them (a timestamped dispatch still costs the stream
+about a microsecond); a second pass of the same number of steps times all
+kernels for the per-kernel table.
 """
 
 import argparse
@@ -50,7 +51,7 @@ DESCR = {
     "mixed_window_bf16": "sliding-window mixed batch, bf16: 4 prefill 1024-4096 + 60 decode 2048-8192, Hq16/Hkv8, D256, window 1024",
     "tiny_prefill_f32": "tiny ragged prefill, fp32: segments 5 and 12, Hq4/Hkv2, D64",
 }
-# kernels whose launches carry event pairs inside the timed region
+# kernels whose launches carry timing events inside the timed region
 DOMINANT = {
     "decode_bf16": ("attn_decode",),
     "prefill_bf16": ("attn_prefill",),

@@ -238,9 +238,11 @@ int nk_version(void);
  * ("attn_decode"), NK_PROF_ATTN_PREFILL ("attn_prefill", which includes its
  * scheduling kernel), NK_PROF_ATTN_F32 ("attn_f32"), NK_PROF_LSE_MERGE
  * ("lse_merge"); NK_PROF_ALL selects every family and 0 turns timing off.
- * Every launch of a selected family is bracketed by two HIP events recorded
- * on the call's stream.  The events themselves cost the stream a few
- * microseconds, so a caller timing whole steps selects only the family it
+ * The kernels of a selected family are launched with a pair of HIP events
+ * (hipExtLaunchKernel) that take the first kernel's dispatch start time and
+ * the last one's end time on the call's stream; no marker packets are added
+ * between kernels, but timestamped dispatches still cost the stream about a
+ * microsecond, so a caller timing whole steps selects only the family it
  * needs.  nk_profile_read waits for the recorded events and returns the
  * summed milliseconds and the launch count of one family since the last
  * reset.  Events are created on first use and reused; this is the only state

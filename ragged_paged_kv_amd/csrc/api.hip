@@ -136,7 +136,15 @@ static int family_bit(const char *family) {
   return 0;
 }
 
-ProfileScope::ProfileScope(const char *family, hipStream_t s) : slot(-1), stream(s) {
+namespace {
+ProfileScope *&current_scope() {
+  static thread_local ProfileScope *cur = nullptr;
+  return cur;
+}
+}  // namespace
+
+ProfileScope::ProfileScope(const char *family, hipStream_t) : slot(-1), outer(current_scope()) {
+  current_scope() = this;
   ProfileState &p = prof();
   if (!(p.mask & family_bit(family))) return;
   std::lock_guard<std::mutex> lock(p.mu);
@@ -156,15 +164,25 @@ ProfileScope::ProfileScope(const char *family, hipStream_t s) : slot(-1), stream
   }
   p.recs[idx].family = family;
   p.recs[idx].pending = true;
-  hipEventRecord(p.recs[idx].a, stream);
   slot = idx;
 }
 
-ProfileScope::~ProfileScope() {
-  if (slot < 0) return;
+void ProfileScope::launch_events(hipEvent_t *start, hipEvent_t *stop) {
+  ProfileScope *ps = current_scope();
+  if (!ps || ps->slot < 0) return;
   ProfileState &p = prof();
   std::lock_guard<std::mutex> lock(p.mu);
-  hipEventRecord(p.recs[slot].b, stream);
+  if (!ps->started) *start = p.recs[ps->slot].a;
+  *stop = p.recs[ps->slot].b;
+  ps->started = ps->stopped = true;
+}
+
+ProfileScope::~ProfileScope() {
+  current_scope() = outer;
+  if (slot < 0 || (started && stopped)) return;
+  ProfileState &p = prof();                  // nothing was launched: no record
+  std::lock_guard<std::mutex> lock(p.mu);
+  p.recs[slot].pending = false;
 }
 
 }  // namespace nk

@@ -412,11 +412,8 @@ hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
   const int G = a.hq / hkv;
   dim3 grid((unsigned)(a.num_seqs * a.max_chunks * hkv), (unsigned)((G + 15) / 16), 1);
   // sub-chunks of 32 steps (512 keys) when the chunk size allows, else 16
-  if (a.split_tokens % 512 == 0)
-    attn_decode_kernel<D, P, FP8, NPF, 32><<<grid, 64, 0, stream>>>(a);
-  else
-    attn_decode_kernel<D, P, FP8, NPF, 16><<<grid, 64, 0, stream>>>(a);
-  return hipGetLastError();
+  if (a.split_tokens % 512 == 0) return launch(attn_decode_kernel<D, P, FP8, NPF, 32>, grid, dim3(64), 0, stream, a);
+  return launch(attn_decode_kernel<D, P, FP8, NPF, 16>, grid, dim3(64), 0, stream, a);
 }
 
 template <int D, int P>

@@ -101,8 +101,7 @@ hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream) {
   if (a.total_q == 0) return hipSuccess;
   ProfileScope prof("attn_f32", stream);
   dim3 grid((unsigned)a.total_q, (unsigned)a.hq);
-  attn_f32_kernel<<<grid, kWave, 0, stream>>>(a);
-  return hipGetLastError();
+  return launch(attn_f32_kernel, grid, dim3(kWave), 0, stream, a);
 }
 
 }  // namespace nk

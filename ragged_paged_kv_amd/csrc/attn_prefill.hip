@@ -717,9 +717,9 @@ hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
   // enough work-groups to fill every CU, at least one per queue
   int grid = ds.cus * res;
   grid = (grid + NQ - 1) / NQ * NQ;
-  prefill_plan_kernel<<<1, kPlanThreads, 0, stream>>>(a, BM);
-  kern<<<grid, NW * 64, C::LDS, stream>>>(a, GW, NQ);
-  return hipGetLastError();
+  e = launch(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, BM);
+  if (e != hipSuccess) return e;
+  return launch(kern, dim3(grid), dim3(NW * 64), C::LDS, stream, a, GW, NQ);
 }
 
 template <int D, int P>

@@ -3,6 +3,7 @@
 // list, and the launcher prototypes.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -69,12 +70,34 @@ hipError_t launch_lse_merge(const float *po, const float *pl, const int32_t *off
                             int32_t rows, int32_t heads, int32_t head_dim, void *out,
                             int32_t out_dtype, float *lse_out, hipStream_t stream);
 
-// Kernel timing (diagnostics): bracket a launch with events when enabled.
+// Kernel timing (diagnostics, nk_profile_enable).  While enabled for its
+// family, a scope owns a pair of events, and the kernels launched inside it
+// through launch() carry them: the scope's first launch the start event,
+// every launch the stop event (the last one recorded counts).  The events
+// then take the kernels' own dispatch start and end times, with no marker
+// packets of their own on the stream.
 struct ProfileScope {
   ProfileScope(const char *family, hipStream_t stream);
   ~ProfileScope();
+  ProfileScope(const ProfileScope &) = delete;
+  ProfileScope &operator=(const ProfileScope &) = delete;
+  // events for the next launch in the innermost scope of this thread (null
+  // when none is enabled)
+  static void launch_events(hipEvent_t *start, hipEvent_t *stop);
   int slot;
-  hipStream_t stream;
+  bool started = false, stopped = false;
+  ProfileScope *outer;
 };
+
+// Every kernel launch of the library: hipExtLaunchKernel with the current
+// scope's events (plain launch when timing is off).
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                  Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  ProfileScope::launch_events(&start, &stop);
+  hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)shmem, stream, start, stop, 0u, args...);
+  return hipGetLastError();
+}
 
 }  // namespace nk

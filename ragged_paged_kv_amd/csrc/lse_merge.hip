@@ -155,12 +155,11 @@ hipError_t launch_lse_merge(const float *po, const float *pl, const int32_t *off
   auto go = [&](auto tag) {
     using TOut = decltype(tag);
     TOut *o = (TOut *)out;
-    if (head_dim <= 128) lse_merge_kernel<TOut, 4><<<grid, kWave, 0, stream>>>(po, pl, offsets, heads, head_dim, o, lse_out);
-    else if (head_dim <= 256) lse_merge_kernel<TOut, 8><<<grid, kWave, 0, stream>>>(po, pl, offsets, heads, head_dim, o, lse_out);
-    else lse_merge_kernel<TOut, 16><<<grid, kWave, 0, stream>>>(po, pl, offsets, heads, head_dim, o, lse_out);
+    auto k = head_dim <= 128 ? lse_merge_kernel<TOut, 4> : head_dim <= 256 ? lse_merge_kernel<TOut, 8>
+                                                                          : lse_merge_kernel<TOut, 16>;
+    return launch(k, dim3(grid), dim3(kWave), 0, stream, po, pl, offsets, heads, head_dim, o, lse_out);
   };
-  if (out_dtype == NK_F32) go(float{}); else go(bf16_t{});
-  return hipGetLastError();
+  return out_dtype == NK_F32 ? go(float{}) : go(bf16_t{});
 }
 
 hipError_t launch_decode_merge(const AttnArgs &a, hipStream_t stream) {
@@ -171,12 +170,10 @@ hipError_t launch_decode_merge(const AttnArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)n;
   auto go = [&](auto tag) {
     using TOut = decltype(tag);
-    const int D = a.cache.head_dim;
-    if (D <= 128) decode_merge_kernel<TOut, 4><<<grid, kWave, 0, stream>>>(a);
-    else decode_merge_kernel<TOut, 8><<<grid, kWave, 0, stream>>>(a);
+    auto k = a.cache.head_dim <= 128 ? decode_merge_kernel<TOut, 4> : decode_merge_kernel<TOut, 8>;
+    return launch(k, dim3(grid), dim3(kWave), 0, stream, a);
   };
-  if (a.q_dtype == NK_F32) go(float{}); else go(bf16_t{});
-  return hipGetLastError();
+  return a.q_dtype == NK_F32 ? go(float{}) : go(bf16_t{});
 }
 
 }  // namespace nk

@@ -366,11 +366,8 @@ hipError_t launch_layout(const RopeArgs &a, hipStream_t stream) {
   if (qk_blocks + v_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const unsigned grid = (unsigned)(qk_blocks + v_blocks);
   const size_t lds = (size_t)(block / 64) * 4 * D * esz;
-  if (a.layout == NK_ROPE_INTERLEAVED)
-    rope_write_kernel<TIn, CACHE, true><<<grid, block, lds, stream>>>(a, upt, bpt, (int)v_blocks, v_group);
-  else
-    rope_write_kernel<TIn, CACHE, false><<<grid, block, lds, stream>>>(a, upt, bpt, (int)v_blocks, v_group);
-  return hipGetLastError();
+  auto k = a.layout == NK_ROPE_INTERLEAVED ? rope_write_kernel<TIn, CACHE, true> : rope_write_kernel<TIn, CACHE, false>;
+  return launch(k, dim3(grid), dim3(block), lds, stream, a, upt, bpt, (int)v_blocks, v_group);
 }
 
 }  // namespace
