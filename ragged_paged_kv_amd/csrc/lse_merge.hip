@@ -11,8 +11,9 @@
 // Design: one wave per (row, head), the heads of a row on consecutive
 // work-groups (their partials are adjacent); four 16-lane groups take every
 // fourth chunk, lanes over head dimensions.  A call moves little data, so
-// its time is the chain of dependent memory accesses, kept to: row bounds,
-// then the partials and their lse values together, then the output.  Two
+// its time is the chain of dependent memory accesses, kept short: a row's
+// partials and lse values are requested together (for a decode row, before
+// its chunk count is read), then the output is written.  Two
 // row->partials maps: explicit merge offsets (the public entry point) and
 // the split-KV decode layout (chunks of a decode row at row*max_chunks).
 
@@ -30,24 +31,33 @@ template <> NK_DEVICE void store2<bf16_t>(bf16_t *p, float a, float b) {
   *(bf16x2_t *)p = bf16x2_t{(bf16_t)a, (bf16_t)b};
 }
 
-// Merge `n` partials starting at `first` (stride `heads` between chunks) for
-// head `h`; write row `out_row`.  The wave splits into four 16-lane groups
-// that take every fourth chunk, each lane holding MAXP pairs of dimensions
-// 2(l + 16 r), r < MAXP; the groups' sums are added across lanes at the end.
-// Latency-bound: the first batch of partial outputs (4 chunks per group) is
-// requested together with the chunks' lse values, so a row of up to 16
-// chunks costs one memory round trip after its chunk count is known.  Lane
-// i holds chunk i's lse and weight; a group reads its chunks' weights from
-// those lanes.
-template <typename TOut, int MAXP>
+// Where a merged row goes: its chunk count (negative: nothing to write) and
+// output locations.
+template <typename TOut> struct RowTarget {
+  int n;
+  TOut *out_row;
+  float *lse_out;
+};
+
+// Merge the partials of one row for head `h`: chunk c's state sits at
+// `first + c` (stride `heads` between chunks).  `target()` reads the row's
+// chunk count and output locations; at most `n_issue` chunks are requested
+// before it returns (an upper bound on the count, within the row's slots),
+// so that those requests and its own are in flight together.  The wave
+// splits into four 16-lane groups that take every fourth chunk, each lane
+// holding MAXP pairs of dimensions 2(l + 16 r), r < MAXP; the groups' sums
+// are added across lanes at the end.  Latency-bound: the first batch of
+// partial outputs (4 chunks per group) is requested together with the
+// chunks' lse values.  Lane i holds chunk i's lse and weight; a group reads
+// its chunks' weights from those lanes.
+template <typename TOut, int MAXP, typename Target>
 NK_DEVICE void merge_row(const float *__restrict__ po, const float *__restrict__ pl, long long first,
-                         int n, int heads, int h, int D, TOut *__restrict__ out_row,
-                         float *__restrict__ lse_out) {
+                         int n_issue, int heads, int h, int D, Target &&target) {
   constexpr int CB = 4;                       // chunks per group and batch
   const int lane = threadIdx.x;
   const int grp = lane >> 4, l16 = lane & 15;
   f32x2_t v[CB][MAXP];
-  auto load_batch = [&](int c0) {
+  auto load_batch = [&](int c0, int n) {
 #pragma unroll
     for (int k = 0; k < CB; ++k) {
       const int c = c0 + grp + 4 * k;
@@ -60,8 +70,12 @@ NK_DEVICE void merge_row(const float *__restrict__ po, const float *__restrict__
     }
   };
   auto lse_of = [&](int c) { return pl[(first + c) * heads + h]; };
-  load_batch(0);
-  const float l0 = lane < n ? lse_of(lane) : -INFINITY;
+  load_batch(0, n_issue);
+  const float l_issued = lane < n_issue ? lse_of(lane) : -INFINITY;
+  const RowTarget<TOut> t = target();
+  if (t.n < 0) return;
+  const int n = t.n;
+  const float l0 = lane < n ? l_issued : -INFINITY;
   float M = l0;
   for (int b = kWave; b < n; b += kWave)
     if (b + lane < n) M = fmaxf(M, lse_of(b + lane));
@@ -82,16 +96,18 @@ NK_DEVICE void merge_row(const float *__restrict__ po, const float *__restrict__
       for (int k = 0; k < CB; ++k) {
         const int c = c0 + grp + 4 * k;
         const float wl = __shfl(w0, c & (kWave - 1), kWave);          // every lane takes part
-        const float w = c >= n ? 0.f : (c < kWave ? wl : weight_of(lse_of(c)));
+        if (c < n) {                          // (requested chunks past n hold anything)
+          const float w = c < kWave ? wl : weight_of(lse_of(c));
 #pragma unroll
-        for (int r = 0; r < MAXP; ++r) {
-          acc[r][0] = fmaf(w, v[k][r][0], acc[r][0]);
-          acc[r][1] = fmaf(w, v[k][r][1], acc[r][1]);
+          for (int r = 0; r < MAXP; ++r) {
+            acc[r][0] = fmaf(w, v[k][r][0], acc[r][0]);
+            acc[r][1] = fmaf(w, v[k][r][1], acc[r][1]);
+          }
         }
       }
       c0 += 4 * CB;
       if (c0 >= n) break;
-      load_batch(c0);
+      load_batch(c0, n);
     }
     // the four groups hold the same dimensions: lanes l, l^16, l^32, l^48
 #pragma unroll
@@ -107,10 +123,10 @@ NK_DEVICE void merge_row(const float *__restrict__ po, const float *__restrict__
 #pragma unroll
     for (int r = 0; r < MAXP; ++r) {
       const int d = 2 * (l16 + 16 * r);
-      if (d < D) store2<TOut>(out_row + d, acc[r][0] * inv, acc[r][1] * inv);
+      if (d < D) store2<TOut>(t.out_row + d, acc[r][0] * inv, acc[r][1] * inv);
     }
   }
-  if (lse_out && lane == 0) *lse_out = tot > 0.f ? M + logf(tot) : -INFINITY;
+  if (t.lse_out && lane == 0) *t.lse_out = tot > 0.f ? M + logf(tot) : -INFINITY;
 }
 
 template <typename TOut, int MAXP>
@@ -119,27 +135,35 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(const float *po, const fl
                                                        TOut *out, float *lse_out) {
   const int h = (int)(blockIdx.x % (unsigned)heads), r = (int)(blockIdx.x / (unsigned)heads);   // heads fastest
   const int a = offsets[r], b = offsets[r + 1];
-  merge_row<TOut, MAXP>(po, pl, a, b - a, heads, h, D, out + ((size_t)r * heads + h) * D,
-                        lse_out ? lse_out + (size_t)r * heads + h : nullptr);
+  merge_row<TOut, MAXP>(po, pl, a, b - a, heads, h, D, [&]() {
+    return RowTarget<TOut>{b - a, out + ((size_t)r * heads + h) * D, lse_out ? lse_out + (size_t)r * heads + h : nullptr};
+  });
 }
 
 // Split-KV decode rows: sequence s (a single query row) has its chunks at
 // s*max_chunks ... ; rows with one chunk were finished by the decode kernel.
+// The row's slots are known before its chunk count, so they are requested
+// first.
 template <typename TOut, int MAXP>
 __global__ void __launch_bounds__(64) decode_merge_kernel(AttnArgs a) {
   const int h = (int)(blockIdx.x % (unsigned)a.hq), s = (int)(blockIdx.x / (unsigned)a.hq);     // heads fastest
-  const int q0 = a.q_offsets[s];
-  const int q1 = a.q_offsets[s + 1];
-  const int L = a.kv_lens[s];                 // requested with the offsets
-  if (q1 - q0 != 1 || L <= 0) return;
-  const int hi = L - 1;
-  const int lo = a.window_left < 0 ? 0 : max(0, hi - a.window_left);
-  const int c0 = (lo / 32) * 32;              // the decode kernel's chunk origin
-  const int n = min((hi + 1 - c0 + a.split_tokens - 1) / a.split_tokens, a.max_chunks);
-  if (n <= 1) return;
-  merge_row<TOut, MAXP>(a.part_out, a.part_lse, (long long)s * a.max_chunks, n, a.hq, h,
-                  a.cache.head_dim, (TOut *)a.out + ((size_t)q0 * a.hq + h) * a.cache.head_dim,
-                  a.lse ? a.lse + (size_t)q0 * a.hq + h : nullptr);
+  merge_row<TOut, MAXP>(a.part_out, a.part_lse, (long long)s * a.max_chunks, a.max_chunks, a.hq, h,
+                        a.cache.head_dim, [&]() {
+    const int q0 = a.q_offsets[s];
+    const int q1 = a.q_offsets[s + 1];
+    const int L = a.kv_lens[s];
+    RowTarget<TOut> t{-1, nullptr, nullptr};
+    if (q1 - q0 != 1 || L <= 0) return t;
+    const int hi = L - 1;
+    const int lo = a.window_left < 0 ? 0 : max(0, hi - a.window_left);
+    const int c0 = (lo / 32) * 32;            // the decode kernel's chunk origin
+    const int n = min((hi + 1 - c0 + a.split_tokens - 1) / a.split_tokens, a.max_chunks);
+    if (n <= 1) return t;
+    t.n = n;
+    t.out_row = (TOut *)a.out + ((size_t)q0 * a.hq + h) * a.cache.head_dim;
+    t.lse_out = a.lse ? a.lse + (size_t)q0 * a.hq + h : nullptr;
+    return t;
+  });
 }
 
 }  // namespace
