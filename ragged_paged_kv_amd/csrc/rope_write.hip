@@ -123,6 +123,19 @@ template <int CACHE> NK_DEVICE size_t v_index(int d, int t, int D) {
          (size_t)(16 * ((t & 15) >> 2) + (d & 15)) * (4 * NV) + ((d >> 4) % NV) * 4 + (t & 3);
 }
 
+// Segment of token t with its row range and key count.  In a batch of
+// single-token rows (decode steps) token t is segment t: that guess is read
+// first, with no lookup before it, and kept when its rows hold t (then it
+// is the segment a search would find); otherwise the offsets are searched.
+struct Seg { int s, q0, q_end, kv; };
+NK_DEVICE Seg segment_of(const RopeArgs &a, int t) {
+  const int g = min(t, a.num_seqs - 1);
+  const int g0 = a.q_offsets[g], g1 = a.q_offsets[g + 1], gk = a.kv_lens[g];
+  if (g0 <= t && t < g1) return Seg{g, g0, g1, gk};
+  const int s = find_segment(a.q_offsets, a.num_seqs, t);
+  return Seg{s, a.q_offsets[s], a.q_offsets[s + 1], a.kv_lens[s]};
+}
+
 // V append, one wave per (group of consecutive tokens, kv head).  A 16-byte
 // run of a V page holds 4 consecutive slots (a "quad") of NV dims (v_index):
 // one token alone can only fill esz bytes of each run.  The wave therefore
@@ -139,12 +152,12 @@ NK_DEVICE void append_v_quads(const RopeArgs &a, int t0, int ntok, int head, uin
   constexpr int NR = D / NV;       // 16-byte runs per quad and head
   const int P = a.cache.page_size, hkv = a.cache.num_kv_heads;
   const int lane = threadIdx.x & 63, b = lane >> 4, chunk = lane & 15;
-  int s = find_segment(a.q_offsets, a.num_seqs, t0);
-  int q0 = a.q_offsets[s], q_end = a.q_offsets[s + 1], kv = a.kv_lens[s];
+  Seg sg = segment_of(a, t0);
+  int s = sg.s, q0 = sg.q0, q_end = sg.q_end, kv = sg.kv;
   for (int t = t0; t < t0 + ntok; ++t) {
     if (t >= q_end) {        // next non-empty segment
-      s = find_segment(a.q_offsets, a.num_seqs, t);
-      q0 = a.q_offsets[s]; q_end = a.q_offsets[s + 1]; kv = a.kv_lens[s];
+      sg = segment_of(a, t);
+      s = sg.s; q0 = sg.q0; q_end = sg.q_end; kv = sg.kv;
     }
     const int slot = kv - (q_end - q0) + (t - q0);
     // only the first new slot of a quad starts one; slot < 0 violates the
@@ -279,10 +292,9 @@ __global__ void __launch_bounds__(1024) rope_write_kernel(RopeArgs a, int units_
   InTraits<TIn>::load8(src + a0, xa);
   InTraits<TIn>::load8(src + b0, xb);
 
-  const int s = find_segment(a.q_offsets, a.num_seqs, t);
-  const int q0 = a.q_offsets[s];
-  const int q_len = a.q_offsets[s + 1] - q0;
-  const int slot = a.kv_lens[s] - q_len + (t - q0);
+  const Seg sg = segment_of(a, t);
+  const int s = sg.s, q0 = sg.q0;
+  const int slot = sg.kv - (sg.q_end - q0) + (t - q0);
 
   if (rotates) {
     // out-of-range positions (a precondition violation) are clamped so that
