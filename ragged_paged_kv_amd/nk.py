@@ -248,8 +248,8 @@ PROFILE_FAMILIES = ("rope_write", "attn_decode", "attn_prefill", "attn_f32", "ls
 
 
 def profile_enable(on=True, families=None):
-    """Bracket the launches of `families` (default: all) with HIP events;
-    on=False turns timing off."""
+    """Time the kernels of `families` (default: all) with HIP events attached
+    to their dispatches; on=False turns timing off."""
     fams = PROFILE_FAMILIES if families is None else families
     mask = 0
     for f in fams:
