@@ -28,9 +28,10 @@
  *     is the cache descriptor itself (a host struct holding device pointers).
  *     Integer arrays are int32.
  *   - The caller owns every buffer, the workspace and the cache.  The library
- *     never allocates device memory, keeps no state between calls (apart from
- *     the optional profiling events below) and may be called from several
- *     host threads at once.
+ *     never allocates device memory, keeps no state between calls apart from
+ *     per-device properties it caches (CU count, resident work-groups of the
+ *     prefill kernel) and the optional profiling events below, and may be
+ *     called from several host threads at once (profiling excepted).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work; they never synchronise.
  *   - Errors are returned as nk_status_t values, detected on the host before
