@@ -309,6 +309,19 @@ def load_traffic(kernel_key):
     return rec.get("bytes_per_launch")
 
 
+def load_mfma(workload):
+    """MFMA counter summary of a workload's prefill kernel from profiles/,
+    if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(family_sources(rec.get("kernel", ""))):
+        return None
+    return {k: rec.get(k) for k in ("executed_over_algorithmic", "mfma_busy_frac")}
+
+
 def _short(name):
     """Kernel name without namespaces / argument lists, template arguments kept."""
     n = name.replace("nk::(anonymous namespace)::", "").replace("void ", "")
@@ -342,6 +355,32 @@ def rocpd_counter(db_path, kernel_match, counter):
     vals = [v for name, cn, v in con.execute("select kernel_name, counter_name, value from counters_collection")
             if kernel_match in name and cn == counter]
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def rocpd_mfma(db_path, kernel_match, simds, gui_instances, flops_per_launch):
+    """MFMA work and utilisation of the matching kernel from one rocprofv3
+    --pmc pass over MFMA_COUNTERS: bf16 MFMA flops executed per dispatch
+    (512 per MOPS unit), and the busy cycles of the matrix units over the
+    dispatch's active GPU cycles times the SIMD count (GRBM_GUI_ACTIVE is read
+    once per XCD, hence `gui_instances`)."""
+    vals = {c: rocpd_counter(db_path, kernel_match, c) for c in MFMA_COUNTERS}
+    mops, n = vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+    busy, _ = vals["SQ_VALU_MFMA_BUSY_CYCLES"]
+    gui, _ = vals["GRBM_GUI_ACTIVE"]
+    rec = {"kernel": kernel_match, "dispatches": n, "counters_per_dispatch": {c: v[0] for c, v in vals.items()},
+           "simds": simds, "gui_instances": gui_instances, "algorithmic_flops_per_launch": flops_per_launch}
+    if mops is not None:
+        rec["mfma_flops_per_dispatch"] = 512.0 * mops
+        if flops_per_launch:
+            rec["executed_over_algorithmic"] = 512.0 * mops / flops_per_launch
+    if busy is not None and gui:
+        rec["active_cycles"] = gui / gui_instances
+        rec["mfma_busy_frac"] = busy / (gui / gui_instances * simds)
+    rec["source_hash"] = source_hash(family_sources(kernel_match))
+    return rec
 
 
 def _pmc_rows(d):
@@ -393,6 +432,12 @@ def main():
     ap.add_argument("--copy-only", action="store_true", help="run one plain 1 GiB copy (counter calibration)")
     ap.add_argument("--rocpd-summary", nargs=3, metavar=("DB", "OUT", "COMMAND"),
                     help="write the per-kernel table of a rocprofv3 kernel-trace database")
+    ap.add_argument("--rocpd-mfma", nargs=2, metavar=("DB", "OUT"),
+                    help="MFMA flops and busy fraction of --pmc-kernel from a pass over MFMA_COUNTERS")
+    ap.add_argument("--mfma-workload", default="prefill_bf16",
+                    help="workload whose algorithmic prefill flops --rocpd-mfma compares with")
+    ap.add_argument("--simds", type=int, default=1024, help="SIMDs of the GPU (MI355X: 256 CUs x 4)")
+    ap.add_argument("--gui-instances", type=int, default=8, help="GRBM_GUI_ACTIVE readings summed per dispatch (XCDs)")
     ap.add_argument("--rocpd-traffic", nargs=5, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB", "OUT"),
                     help="HBM bytes per launch of --pmc-kernel from FETCH_SIZE / WRITE_SIZE databases")
     args = ap.parse_args()
@@ -403,6 +448,16 @@ def main():
         with open(out, "w") as f:
             f.write(text)
         print(text)
+        return 0
+    if args.rocpd_mfma:
+        import synth
+        from synth import work
+        db, out = args.rocpd_mfma
+        rec = rocpd_mfma(db, args.pmc_kernel, args.simds, args.gui_instances,
+                         work.prefill_flops(synth.make(args.mfma_workload)))
+        with open(out, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec, indent=1))
         return 0
     if args.rocpd_traffic:
         fdb, wdb, cfdb, cwdb, out = args.rocpd_traffic
@@ -484,6 +539,7 @@ def main():
         if r.get("prefill_TFLOPs_kernel"):
             e["prefill_TFLOPs_kernel"] = r["prefill_TFLOPs_kernel"]
             e["prefill_mfma_frac"] = r["prefill_TFLOPs_kernel"] / BF16_PEAK_TFLOPS
+            e["prefill_mfma_counters"] = load_mfma(n)
         if r.get("rope_GBps_kernel"):
             e["rope_GBps_kernel"] = r["rope_GBps_kernel"]
         extra[n] = e

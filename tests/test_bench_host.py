@@ -86,3 +86,18 @@ def test_traffic_is_used_only_for_unchanged_sources(tmp_path, monkeypatch):
     (csrc / "attn_decode.hip").write_text("// the decode kernel changed")
     assert bench.load_traffic("decode_bf16") is None
     assert bench.load_traffic("no_such_key") is None
+
+
+def test_mfma_summary(tmp_path):
+    db = str(tmp_path / "mfma.db")
+    k = "attn_prefill_kernel<128, 16, false, 8>"
+    _counter_db(db, [(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1000.0), (k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 3000.0),
+                     (k, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0), (k, "GRBM_GUI_ACTIVE", 80.0),
+                     (k, "SQ_BUSY_CYCLES", 5.0), ("prefill_plan_kernel", "GRBM_GUI_ACTIVE", 1e9)])
+    rec = bench.rocpd_mfma(db, "attn_prefill_kernel<128, 16, false", simds=64, gui_instances=8,
+                           flops_per_launch=512.0 * 1000)
+    assert rec["dispatches"] == 2
+    assert rec["mfma_flops_per_dispatch"] == pytest.approx(512.0 * 2000)     # 512 flops per MOPS unit
+    assert rec["executed_over_algorithmic"] == pytest.approx(2.0)
+    assert rec["active_cycles"] == pytest.approx(10.0)                       # one XCD's share
+    assert rec["mfma_busy_frac"] == pytest.approx(1024.0 / (10.0 * 64))
