@@ -554,6 +554,14 @@ def main():
             e["prefill_mfma_counters"] = load_mfma(n)
         if r.get("rope_GBps_kernel"):
             e["rope_GBps_kernel"] = r["rope_GBps_kernel"]
+        if r.get("decode_bytes") and r.get("prefill_flops"):
+            # one ragged call, two launches: the time each would take at its
+            # roofline over the time the attention kernels took together
+            ks = r["kernels"]
+            t_attn = sum(ks[f]["avg_ms"] for f in ("attn_decode", "attn_prefill", "lse_merge") if f in ks) / 1e3
+            if t_attn > 0:
+                ideal = r["decode_bytes"] / (HBM_PEAK_GBS * 1e9) + r["prefill_flops"] / (BF16_PEAK_TFLOPS * 1e12)
+                e["combined_roofline_frac"] = ideal / t_attn
         extra[n] = e
     line["workloads"] = extra
     print(json.dumps(line), flush=True)
