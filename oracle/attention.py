@@ -21,9 +21,10 @@ Definitions followed:
   Hq / Hkv query heads.
 
 Readings taken where the pages leave a step open: query head h reads KV head
-floor(h / G) with G = Hq / Hkv; only the causal band (keys_after = 0) is
-computed; ``window_left`` = keys_before (-1 = unbounded); the log-sum-exp is
-the natural log of sum_j exp(scale * q.k_j); an empty row has lse = -inf.
+floor(h / G) with G = Hq / Hkv; ``window_left`` = keys_before and
+``window_right`` = keys_after, -1 standing for the pages' None (unbounded),
+window_right 0 (the default) being causal; the log-sum-exp is the natural
+log of sum_j exp(scale * q.k_j); an empty row has lse = -inf.
 
 This is the plain definition: full score rows, one max, one exponent, one
 sum, one division -- no tiling, no online softmax, no split.
@@ -32,16 +33,18 @@ sum, one division -- no tiling, no online softmax, no split.
 import numpy as np
 
 
-def visible_range(row, q_len, kv_len, window_left):
+def visible_range(row, q_len, kv_len, window_left, window_right=0):
     """Inclusive key range [lo, hi] visible to query row ``row`` of a segment
-    with ``q_len`` query rows over ``kv_len`` keys (empty when lo > hi)."""
+    with ``q_len`` query rows over ``kv_len`` keys (empty when lo > hi): from
+    the row's position minus keys_before through the position plus
+    keys_after, clipped to the segment's keys."""
     p = row + kv_len - q_len                    # end-aligned query position
-    hi = min(p, kv_len - 1)
+    hi = kv_len - 1 if window_right < 0 else min(p + window_right, kv_len - 1)
     lo = 0 if window_left < 0 else max(0, p - window_left)
     return lo, hi
 
 
-def attend_rows(q_rows, K, V, row_ids, q_len, kv_len, softmax_scale, window_left):
+def attend_rows(q_rows, K, V, row_ids, q_len, kv_len, softmax_scale, window_left, window_right=0):
     """Attention for selected query rows of one segment and one KV head.
 
     q_rows [n, D] float64, K/V [kv_len, D] float64, row_ids [n] local rows.
@@ -52,7 +55,7 @@ def attend_rows(q_rows, K, V, row_ids, q_len, kv_len, softmax_scale, window_left
     lse = np.full(n, -np.inf)
     scores = softmax_scale * (q_rows @ K.T)     # [n, kv_len]
     for r in range(n):
-        lo, hi = visible_range(int(row_ids[r]), q_len, kv_len, window_left)
+        lo, hi = visible_range(int(row_ids[r]), q_len, kv_len, window_left, window_right)
         if lo > hi:
             continue
         s = scores[r, lo:hi + 1]
@@ -65,7 +68,7 @@ def attend_rows(q_rows, K, V, row_ids, q_len, kv_len, softmax_scale, window_left
 
 
 def ragged_paged_attention(q, q_offsets, kv_lens, cache, page_table, softmax_scale,
-                           window_left=-1, rows=None):
+                           window_left=-1, rows=None, window_right=0):
     """Attention of every (or the selected) query row of a ragged batch.
 
     q [T, Hq, D]: float64 values of the stored queries.  ``cache`` is an
@@ -98,16 +101,17 @@ def ragged_paged_attention(q, q_offsets, kv_lens, cache, page_table, softmax_sca
         for h in range(hq):
             g = h // group
             o, l = attend_rows(q[a + local, h, :], K[:, g, :], V[:, g, :], local,
-                               q_len, kv_len, softmax_scale, window_left)
+                               q_len, kv_len, softmax_scale, window_left, window_right)
             out[a + local, h, :] = o
             lse[a + local, h] = l
     return out, lse
 
 
-def dense_attention(q, k, v, softmax_scale, window_left=-1):
+def dense_attention(q, k, v, softmax_scale, window_left=-1, window_right=0):
     """Single-segment attention on contiguous arrays (no pages).
 
-    q [n_q, Hq, D], k/v [n_kv, Hkv, D] float64; end-aligned causal band.
+    q [n_q, Hq, D], k/v [n_kv, Hkv, D] float64; end-aligned band (causal by
+    default).
     """
     q = np.asarray(q, dtype=np.float64)
     n_q, hq, d = q.shape
@@ -118,7 +122,7 @@ def dense_attention(q, k, v, softmax_scale, window_left=-1):
     for h in range(hq):
         g = h // group
         o, l = attend_rows(q[:, h, :], k[:, g, :], v[:, g, :], np.arange(n_q),
-                           n_q, n_kv, softmax_scale, window_left)
+                           n_q, n_kv, softmax_scale, window_left, window_right)
         out[:, h, :] = o
         lse[:, h] = l
     return out, lse

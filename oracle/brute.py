@@ -36,7 +36,7 @@ def attention_row(q, keys, values, scale):
     return out, m + math.log(l)
 
 
-def ragged_attention(q, q_offsets, kv_lens, keys, values, scale, window_left=-1):
+def ragged_attention(q, q_offsets, kv_lens, keys, values, scale, window_left=-1, window_right=0):
     """q: list over tokens of list over heads of vectors; keys/values: list
     over sequences of list over slots of list over kv heads of vectors.
     Returns (out, lse) nested lists [T][Hq][D], [T][Hq]."""
@@ -50,7 +50,7 @@ def ragged_attention(q, q_offsets, kv_lens, keys, values, scale, window_left=-1)
         for r in range(q_len):
             p = r + kv_len - q_len
             lo = 0 if window_left < 0 else max(0, p - window_left)
-            hi = min(p, kv_len - 1)
+            hi = kv_len - 1 if window_right < 0 else min(p + window_right, kv_len - 1)
             row_out, row_lse = [], []
             for h in range(hq):
                 g = h // group

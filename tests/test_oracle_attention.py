@@ -161,16 +161,22 @@ def test_p8_gqa_equals_repeated_heads(golden):
     np.testing.assert_array_equal(lse, l2)
 
 
-@pytest.mark.parametrize("n_q,n_kv,window", [(7, 7, -1), (3, 10, -1), (1, 13, -1), (6, 9, 2), (9, 9, 0)])
-def test_p9_matches_torch_sdpa(n_q, n_kv, window):
+@pytest.mark.parametrize("n_q,n_kv,window,after", [(7, 7, -1, 0), (3, 10, -1, 0), (1, 13, -1, 0), (6, 9, 2, 0),
+                                                   (9, 9, 0, 0), (7, 7, -1, -1), (6, 9, 2, 3), (5, 12, -1, 4),
+                                                   (9, 9, 0, 2), (3, 10, 1, -1)])
+def test_p9_matches_torch_sdpa(n_q, n_kv, window, after):
+    """The band of attention_packed (NumKong matrix-kernels page): row r of
+    n_q queries over n_kv keys sees keys r + n_kv - n_q - keys_before through
+    r + n_kv - n_q + keys_after, each side unbounded at None (-1 here)."""
     rng = np.random.default_rng(9)
     hq, hkv, d = 4, 2, 16
     q = rng.standard_normal((n_q, hq, d)); k = rng.standard_normal((n_kv, hkv, d)); v = rng.standard_normal((n_kv, hkv, d))
     scale = 0.37
-    out, lse = attention.dense_attention(q, k, v, scale, window)
+    out, lse = attention.dense_attention(q, k, v, scale, window, after)
     i = np.arange(n_q)[:, None] + n_kv - n_q
     j = np.arange(n_kv)[None, :]
-    mask = (j <= i) & ((j >= i - window) if window >= 0 else True)
+    mask = ((j <= i + after) if after >= 0 else True) & ((j >= i - window) if window >= 0 else True)
+    mask = np.broadcast_to(mask, (n_q, n_kv)).copy()
     tq = torch.from_numpy(q).permute(1, 0, 2)
     tk = torch.from_numpy(np.repeat(k, hq // hkv, axis=1)).permute(1, 0, 2).contiguous()
     tv = torch.from_numpy(np.repeat(v, hq // hkv, axis=1)).permute(1, 0, 2).contiguous()
@@ -207,6 +213,49 @@ def test_p10_window_band(golden):
     o_w, l_w = attention.ragged_paged_attention(q, offs, lens, cache, pt, scale, max(lens) - 1)
     np.testing.assert_array_equal(o_full, o_w)
     np.testing.assert_array_equal(l_full, l_w)
+
+
+def test_p10b_band_after_the_row(golden):
+    """keys_after > 0 (attention_packed's band): brute force on the
+    two-segment example, the band's edges, and the special cases -- a
+    single-token row is its segment's last position, so keys after it do not
+    exist; a keys_after that reaches every segment's end is unbounded."""
+    g = golden("numkong_band_example.json")
+    rng = np.random.default_rng(12)
+    lens, offs = g["lengths"], g["offsets"]
+    T = offs[-1]
+    q = rng.standard_normal((T, 2, 8)); k = rng.standard_normal((T, 2, 8)); v = rng.standard_normal((T, 2, 8))
+    cache, pt = _pack_contiguous(k, v, offs, 16)
+    ks = [k[offs[s]:offs[s + 1]].tolist() for s in range(2)]
+    vs = [v[offs[s]:offs[s + 1]].tolist() for s in range(2)]
+    for before, after in ((3, 2), (-1, 1), (0, -1), (-1, -1), (2, 5)):
+        for L in lens:
+            for r in range(L):
+                lo, hi = attention.visible_range(r, L, L, before, after)
+                assert hi == (L - 1 if after < 0 else min(r + after, L - 1))
+                assert lo == (0 if before < 0 else max(0, r - before))
+        out, lse = attention.ragged_paged_attention(q, offs, lens, cache, pt, 0.3, before, window_right=after)
+        bo, bl = brute.ragged_attention(q.tolist(), offs, lens, ks, vs, 0.3, before, after)
+        np.testing.assert_allclose(out, np.array(bo), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, np.array(bl), rtol=0, atol=1e-13)
+    o_u, l_u = attention.ragged_paged_attention(q, offs, lens, cache, pt, 0.3, -1, window_right=-1)
+    o_m, l_m = attention.ragged_paged_attention(q, offs, lens, cache, pt, 0.3, -1, window_right=max(lens) - 1)
+    np.testing.assert_array_equal(o_u, o_m)
+    np.testing.assert_array_equal(l_u, l_m)
+    # unbounded on both sides: every row is the plain softmax over all its segment's keys
+    for s in range(2):
+        a, b = offs[s], offs[s + 1]
+        sc = 0.3 * np.einsum("qhd,khd->hqk", q[a:b], k[a:b])
+        w = np.exp(sc - sc.max(-1, keepdims=True))
+        ref = np.einsum("hqk,khd->qhd", w / w.sum(-1, keepdims=True), v[a:b])
+        np.testing.assert_allclose(o_u[a:b], ref, rtol=0, atol=1e-13)
+    # one query row over 9 keys: keys after its position do not exist
+    q1 = rng.standard_normal((1, 2, 8)); k9 = rng.standard_normal((9, 2, 8)); v9 = rng.standard_normal((9, 2, 8))
+    o0, l0 = attention.dense_attention(q1, k9, v9, 0.5, 4, 0)
+    for after in (1, 7, -1):
+        o1, l1 = attention.dense_attention(q1, k9, v9, 0.5, 4, after)
+        np.testing.assert_array_equal(o0, o1)
+        np.testing.assert_array_equal(l0, l1)
 
 
 def test_rows_with_no_key_are_zero():
