@@ -187,6 +187,29 @@ int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_o
                               int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * nk_ragged_paged_attention_band -- the same over a general band of keys.
+ *
+ * NumKong matrix-kernels page, attention_packed: the row at position p sees
+ * the keys from p - keys_before through p + keys_after, each side unbounded
+ * at None.  Here window_left = keys_before and window_right = keys_after,
+ * -1 standing for None:
+ *   hi = kv_len-1 if window_right < 0 else min(p + window_right, kv_len-1),
+ *   lo as above.
+ * window_right = 0 is causal (nk_ragged_paged_attention is this call with
+ * window_right 0); window_right < -1 returns NK_ERR_INVALID_ARG.  A
+ * single-token row sits at its segment's last key, so window_right does not
+ * change it.  Every other argument, the workspace and the errors are those
+ * of nk_ragged_paged_attention.
+ */
+int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t *q_offsets,
+                                   const int32_t *kv_lens, const nk_paged_kv_t *cache,
+                                   float softmax_scale, int32_t window_left, int32_t window_right,
+                                   void *out, float *lse, int32_t num_seqs, int32_t total_q,
+                                   int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
+                                   int32_t kv_split_tokens, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace nk_ragged_paged_attention needs for these scalars
  * (0 if none).  Pure host computation. */
 size_t nk_ragged_paged_attention_workspace_size(int32_t q_dtype, int32_t cache_dtype,

@@ -257,9 +257,21 @@ int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_o
                               int32_t num_seqs, int32_t total_q, int32_t max_q_len,
                               int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens,
                               void *workspace, size_t workspace_bytes_given, void *stream) {
+  return nk_ragged_paged_attention_band(q, q_dtype, q_offsets, kv_lens, cache, softmax_scale, window_left, 0,
+                                        out, lse, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads,
+                                        kv_split_tokens, workspace, workspace_bytes_given, stream);
+}
+
+int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t *q_offsets,
+                                   const int32_t *kv_lens, const nk_paged_kv_t *cache,
+                                   float softmax_scale, int32_t window_left, int32_t window_right,
+                                   void *out, float *lse, int32_t num_seqs, int32_t total_q,
+                                   int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
+                                   int32_t kv_split_tokens, void *workspace,
+                                   size_t workspace_bytes_given, void *stream) {
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0 || num_q_heads <= 0)
     return NK_ERR_INVALID_ARG;
-  if (window_left < -1) return NK_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1) return NK_ERR_INVALID_ARG;
   if (kv_split_tokens < 0 || kv_split_tokens % 32) return NK_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return NK_ERR_INVALID_ARG;
   int st = check_cache(cache);
@@ -275,7 +287,8 @@ int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_o
 
   AttnArgs a{};
   a.q = q; a.q_dtype = q_dtype; a.q_offsets = q_offsets; a.kv_lens = kv_lens;
-  a.cache = *cache; a.softmax_scale = softmax_scale; a.window_left = window_left;
+  a.cache = *cache; a.softmax_scale = softmax_scale;
+  a.window_left = window_left; a.window_right = window_right;
   a.out = out; a.lse = lse;
   a.num_seqs = num_seqs; a.total_q = total_q; a.max_q_len = max_q_len; a.max_kv_len = max_kv_len;
   a.hq = num_q_heads;

@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
   const int q_len = a.q_offsets[s + 1] - q0;
   const int L = a.kv_lens[s];
   const int p = (t - q0) + L - q_len;
-  const int hi = min(p, L - 1);
+  const int hi = band_hi(p, L, a.window_right);
   const int lo = a.window_left < 0 ? 0 : max(0, p - a.window_left);
 
   const float *q = (const float *)a.q + ((size_t)t * a.hq + h) * D;

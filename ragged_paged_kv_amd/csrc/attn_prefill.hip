@@ -164,7 +164,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const int r0 = qb * BM;
   const int shift = L - q_len;                // row r sits at position r + shift
   const int r_last = min(r0 + BM, q_len) - 1;
-  const int kmax_wg = min(r_last + shift, L - 1);
+  const int kmax_wg = band_hi(r_last + shift, L, a.window_right);
   const int kmin_wg = a.window_left < 0 ? 0 : max(0, r0 + shift - a.window_left);
   if (kmax_wg < kmin_wg || L <= 0) {
     // no row of the group sees a key (q_len > kv_len): zeros, -inf
@@ -191,11 +191,11 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const bool row_valid = my_row < q_len;
   const int my_pos = my_row + shift;
   const int my_lo = a.window_left < 0 ? 0 : max(0, my_pos - a.window_left);
-  const int my_hi = min(my_pos, L - 1);
+  const int my_hi = band_hi(my_pos, L, a.window_right);
   // the wave's key range (over its valid rows)
   const bool wave_active = rw < q_len;
   const int w_rows_last = min(rw + 31, q_len - 1);
-  const int wk_hi = min(w_rows_last + shift, L - 1);
+  const int wk_hi = band_hi(w_rows_last + shift, L, a.window_right);
   const int wk_lo = a.window_left < 0 ? 0 : max(0, rw + shift - a.window_left);
 
   // ---- Q operand (B of the score product): lane holds Q[row][16kk + 8*half .. +8].
@@ -399,7 +399,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
           for (int r = 0; r < 4; ++r) sc[st][4 * j + r] *= k4[r];
         }
     }
-    const bool mask = tile_base + BN - 1 > rw + shift ||
+    const bool mask = tile_base + BN - 1 > band_hi(rw + shift, L, a.window_right) ||
                       (a.window_left >= 0 && tile_base < w_rows_last + shift - a.window_left);
     if (mask) {
       const int rel_hi = row_valid ? my_hi - tile_base - 8 * half : -1000000;
@@ -530,7 +530,7 @@ NK_DEVICE int item_tiles(const AttnArgs &a, int BM, int s, int qb) {
   const int shift = L - q_len;
   const int r0 = qb * BM;
   const int r_last = min(r0 + BM, q_len) - 1;
-  const int kmax = min(r_last + shift, L - 1);
+  const int kmax = band_hi(r_last + shift, L, a.window_right);
   const int kmin = a.window_left < 0 ? 0 : max(0, r0 + shift - a.window_left);
   return (kmax < kmin || L <= 0) ? 0 : kmax / BN - kmin / BN + 1;
 }

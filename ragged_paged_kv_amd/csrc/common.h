@@ -72,6 +72,13 @@ NK_DEVICE float wave_sum(float v) {
 NK_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 NK_DEVICE float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Last key visible to a query at position p of a segment with L keys: p plus
+// the keys after it, or the segment's last key when those are unbounded
+// (-1) or reach past it.
+NK_DEVICE int band_hi(int p, int L, int window_right) {
+  return (window_right < 0 || window_right >= L) ? L - 1 : min(p + window_right, L - 1);
+}
+
 // Index of the first segment s with q_offsets[s+1] > t (binary search).
 NK_DEVICE int find_segment(const int32_t *__restrict__ q_offsets, int num_seqs, int t) {
   int lo = 0, hi = num_seqs - 1;

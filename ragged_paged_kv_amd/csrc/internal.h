@@ -28,7 +28,8 @@ struct AttnArgs {
   const int32_t *q_offsets, *kv_lens;
   nk_paged_kv_t cache;
   float softmax_scale;
-  int32_t window_left;
+  int32_t window_left;      // keys before a row's position it sees (-1: all)
+  int32_t window_right;     // keys after it (0: causal; -1: all)
   void *out;
   float *lse;
   int32_t num_seqs, total_q, max_q_len, max_kv_len, hq;

@@ -19,7 +19,7 @@ NK_F32, NK_BF16, NK_E4M3 = 0, 1, 2
 NK_ROPE_HALF, NK_ROPE_INTERLEAVED = 0, 1
 NK_OK, NK_ERR_INVALID_ARG, NK_ERR_UNSUPPORTED, NK_ERR_WORKSPACE, NK_ERR_DEVICE = 0, 1, 2, 3, 4
 
-EXPORTS = ("nk_rope_qk_write_paged", "nk_ragged_paged_attention",
+EXPORTS = ("nk_rope_qk_write_paged", "nk_ragged_paged_attention", "nk_ragged_paged_attention_band",
            "nk_ragged_paged_attention_workspace_size", "nk_ragged_paged_attention_split_tokens",
            "nk_attention_lse_merge", "nk_status_string", "nk_version", "nk_profile_enable",
            "nk_profile_reset", "nk_profile_read")
@@ -58,6 +58,9 @@ def lib():
         L.nk_ragged_paged_attention.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, vp, vp, i32,
                                                 i32, i32, i32, i32, i32, vp, sz, vp]
         L.nk_ragged_paged_attention.restype = ctypes.c_int
+        L.nk_ragged_paged_attention_band.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, i32, vp, vp, i32,
+                                                     i32, i32, i32, i32, i32, vp, sz, vp]
+        L.nk_ragged_paged_attention_band.restype = ctypes.c_int
         L.nk_ragged_paged_attention_workspace_size.argtypes = [i32] * 11
         L.nk_ragged_paged_attention_workspace_size.restype = sz
         L.nk_ragged_paged_attention_split_tokens.argtypes = [i32] * 7
@@ -202,10 +205,12 @@ def split_tokens(cache, num_seqs, max_kv_len, num_q_heads, window_left=-1, kv_sp
 
 def ragged_paged_attention(q, q_offsets, kv_lens, cache, softmax_scale, max_q_len, max_kv_len,
                            window_left=-1, out=None, lse=None, kv_split_tokens=0, workspace=None,
-                           stream=None):
-    """Causal (optionally windowed) GQA attention of q [T, Hq, D] over the
-    cache; returns (out, lse).  ``lse`` is filled when given (float32
-    [T, Hq]); ``workspace`` is allocated here when not given."""
+                           stream=None, window_right=0):
+    """GQA attention of q [T, Hq, D] over the cache under the band
+    [position - window_left, position + window_right] (-1 = unbounded side;
+    window_right 0, the default, is causal); returns (out, lse).  ``lse`` is
+    filled when given (float32 [T, Hq]); ``workspace`` is allocated here when
+    not given."""
     T, hq, d = q.shape
     B = kv_lens.shape[0]
     if out is None:
@@ -221,11 +226,12 @@ def ragged_paged_attention(q, q_offsets, kv_lens, cache, softmax_scale, max_q_le
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = cache.struct()
-    st = lib().nk_ragged_paged_attention(_ptr(q), _dtype_code(q.dtype), _ptr(q_offsets), _ptr(kv_lens),
-                                         ctypes.byref(c), float(softmax_scale), int(window_left),
-                                         _ptr(out), _ptr(lse), B, T, int(max_q_len), int(max_kv_len), hq,
-                                         int(kv_split_tokens), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "nk_ragged_paged_attention")
+    st = lib().nk_ragged_paged_attention_band(_ptr(q), _dtype_code(q.dtype), _ptr(q_offsets), _ptr(kv_lens),
+                                              ctypes.byref(c), float(softmax_scale), int(window_left),
+                                              int(window_right), _ptr(out), _ptr(lse), B, T, int(max_q_len),
+                                              int(max_kv_len), hq, int(kv_split_tokens), _ptr(workspace),
+                                              ws_bytes, _stream(stream))
+    _check(st, "nk_ragged_paged_attention_band")
     return out, lse
 
 

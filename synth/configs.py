@@ -57,6 +57,7 @@ class Workload:
     seq_ids: np.ndarray = field(default=None)   # original sequence ids (RNG identity)
     token_ids: np.ndarray = field(default=None)  # original token ids
     full_total_q: int = 0       # tokens of the original batch (RNG identity)
+    window_right: int = 0       # keys after a row's position it sees: 0 causal, -1 unbounded
 
     @property
     def num_seqs(self):
@@ -333,7 +334,7 @@ def build_cache(w, threads=8):
 def custom(q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, *, rotary_dim=None,
            rope_layout="half", rope_theta=1e4, page_size=16, in_dtype="bf16", cache_dtype="bf16",
            softmax_scale=None, window_left=-1, qk_norm=False, explicit_positions=True,
-           page_order="permuted", seed=1000, split_tokens=0, name="custom"):
+           page_order="permuted", seed=1000, split_tokens=0, name="custom", window_right=0):
     """A workload of given shapes (for tests); pages drawn from
     ``default_rng(seed)``, values from the same per-token/per-sequence streams
     as the named workloads."""
@@ -348,4 +349,5 @@ def custom(q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, *, rotary_dim=N
     w.seq_ids = np.arange(w.num_seqs)
     w.token_ids = np.arange(w.total_q)
     w.full_total_q = w.total_q
+    w.window_right = window_right
     return w

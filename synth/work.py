@@ -25,7 +25,7 @@ def visible_keys(w):
     for s in range(w.num_seqs):
         ql, L = int(w.q_lens[s]), int(w.kv_lens[s])
         p = np.arange(ql) + L - ql
-        hi = np.minimum(p, L - 1)
+        hi = np.full_like(p, L - 1) if w.window_right < 0 else np.minimum(p + w.window_right, L - 1)
         lo = np.zeros_like(p) if w.window_left < 0 else np.maximum(0, p - w.window_left)
         out[offs[s]:offs[s] + ql] = np.maximum(hi - lo + 1, 0)
     return out

@@ -102,6 +102,25 @@ def test_attention_validation(L):
     assert attn(L, c, total=0) == nk.NK_OK
 
 
+def attn_band(L, cache, window_right, **kw):
+    a = dict(q=1, q_dtype=nk.NK_BF16, q_offsets=1, kv_lens=1, scale=0.1, window=-1, out=1, lse=None, num_seqs=1,
+             total=4, max_q=4, max_kv=64, hq=4, split=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return L.nk_ragged_paged_attention_band(a["q"], a["q_dtype"], a["q_offsets"], a["kv_lens"],
+                                            None if cache is None else ctypes.byref(cache), a["scale"], a["window"],
+                                            window_right, a["out"], a["lse"], a["num_seqs"], a["total"], a["max_q"],
+                                            a["max_kv"], a["hq"], a["split"], a["ws"], a["ws_bytes"], None)
+
+
+def test_band_validation(L):
+    c = _cache()
+    assert attn_band(L, c, -2) == nk.NK_ERR_INVALID_ARG               # only -1 stands for unbounded
+    assert attn_band(L, c, 3, window=-2) == nk.NK_ERR_INVALID_ARG
+    assert attn_band(L, None, 0) == nk.NK_ERR_INVALID_ARG
+    assert attn_band(L, c, 5, q_dtype=nk.NK_F32) == nk.NK_ERR_UNSUPPORTED
+    assert attn_band(L, c, -1, total=0) == nk.NK_OK                   # empty batch: nothing launched
+
+
 def test_workspace_and_split_queries(L):
     # no workspace when every decode row fits in one chunk, or without decode-capable dtypes
     assert L.nk_ragged_paged_attention_workspace_size(nk.NK_BF16, nk.NK_BF16, 4, 4, 1, 100, 8, 2, 128, -1, 0) == 0
