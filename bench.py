@@ -50,6 +50,7 @@ DESCR = {
     "decode_fp8": "long-context decode, e4m3 KV + f32 scales: 128 seqs, KV 4096-32768 log-uniform, Hq64/Hkv8, D128, split 512",
     "mixed_window_bf16": "sliding-window mixed batch, bf16: 4 prefill 1024-4096 + 60 decode 2048-8192, Hq16/Hkv8, D256, window 1024",
     "tiny_prefill_f32": "tiny ragged prefill, fp32: segments 5 and 12, Hq4/Hkv2, D64",
+    "prefill_bidir_bf16": "the ragged prefill batch with every row seeing its whole segment (band unbounded on both sides)",
 }
 # kernels whose launches carry timing events inside the timed region
 DOMINANT = {
@@ -58,6 +59,7 @@ DOMINANT = {
     "decode_fp8": ("attn_decode",),
     "mixed_window_bf16": ("attn_prefill", "attn_decode"),
     "tiny_prefill_f32": ("attn_f32",),
+    "prefill_bidir_bf16": ("attn_prefill",),
 }
 KERNEL_SOURCES = ["attn_decode.hip", "attn_prefill.hip", "rope_write.hip", "lse_merge.hip", "common.h", "internal.h"]
 # the sources a kernel family is built from: a counter summary stays valid
@@ -188,7 +190,7 @@ def measure(st, steps, warmup, flush, split=None):
                                w.rope_layout, position_ids=st.pos, q_out=st.q_out)
         nk.ragged_paged_attention(st.q_out, st.q_offsets, st.kv_lens, st.cache, w.softmax_scale, w.max_q_len,
                                   w.max_kv_len, w.window_left, out=st.out, lse=st.lse, kv_split_tokens=split_req,
-                                  workspace=ws)
+                                  workspace=ws, window_right=w.window_right)
 
     scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
     sink = torch.empty((), dtype=torch.float32, device="cuda")
@@ -434,7 +436,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="decode_bf16,prefill_bf16,decode_fp8,mixed_window_bf16")
+    ap.add_argument("--only", default="decode_bf16,prefill_bf16,decode_fp8,mixed_window_bf16,prefill_bidir_bf16")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))

@@ -26,6 +26,9 @@ import numpy as np
 import torch
 
 NAMES = ("tiny_prefill_f32", "decode_bf16", "prefill_bf16", "mixed_window_bf16", "decode_fp8")
+# beyond the five: the prefill batch under a band unbounded on both sides
+# (every row sees its whole segment), for the band entry point
+EXTRA = ("prefill_bidir_bf16",)
 
 
 def names():
@@ -135,6 +138,10 @@ def _pages(rng, kv_lens, page_size, order):
 
 def make(which):
     """Workload by number (1..5) or name."""
+    if which in EXTRA:
+        w = replace(make("prefill_bf16"), name=which)
+        w.window_right = -1
+        return w
     k = NAMES.index(which) + 1 if isinstance(which, str) else int(which)
     seed = k - 1
     rng = np.random.default_rng(seed)
