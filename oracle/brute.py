@@ -16,7 +16,12 @@ def rope_row(x, cos_row, sin_row, rotary_dim, layout):
     out = list(x)
     half = rotary_dim // 2
     for i in range(half):
-        a, b = (i, i + half) if layout == "half" else (2 * i, 2 * i + 1)
+        if layout == "half":
+            a, b = i, i + half
+        elif layout == "half_proportional":          # pairs span the whole head
+            a, b = i, i + len(x) // 2
+        else:
+            a, b = 2 * i, 2 * i + 1
         c, s = cos_row[i], sin_row[i]
         out[a] = x[a] * c - x[b] * s
         out[b] = x[a] * s + x[b] * c

@@ -10,8 +10,11 @@ What is computed, per the pages:
   ``freqs_cis`` table; ``interleaved`` pairs adjacent (real, imaginary)
   components instead of splitting the head into halves.
 * aria_kernel crate, ``rope`` (interleaved pairs), ``rope_half`` (rotate-half:
-  a contiguous half of the dims pairs with the other half) and
-  ``rope_half_partial`` (only the first ``rotary_dim`` dims rotate).
+  a contiguous half of the dims pairs with the other half),
+  ``rope_half_partial`` (only the first ``rotary_dim`` dims rotate) and
+  ``rope_half_proportional`` (p-RoPE: the rotate-half pairing over the whole
+  head, only its first pairs rotate, the others stay identity; their
+  frequencies use the full head_dim denominator).
 * NumKong matrix-kernels page, ``attention_rope``: every channel pair of each
   head is rotated by per-token cos/sin grids shared across heads.
 
@@ -21,7 +24,9 @@ Readings taken where the pages leave a step open:
   cos + i sin, so x' = x cos - y sin and y' = x sin + y cos;
 * the table is ``freqs[pos][i] = (cos, sin)`` of pair i at position pos,
   float32, shape ``[max_pos, rotary_dim/2, 2]``; pairs are
-  half: (i, i + R/2), interleaved: (2i, 2i+1), for i < R/2; dims >= R pass;
+  half: (i, i + R/2), interleaved: (2i, 2i+1), for i < R/2, dims >= R pass;
+  half_proportional: (i, i + D/2) for i < R/2 (R = 2 x the rotated pairs),
+  every other dim passes; the table's frequencies are the caller's;
 * token i of segment s goes to logical slot ``kv_len[s] - q_len[s] + i``
   (``kv_len`` counts keys after the append); without position ids the
   position is that slot;
@@ -39,7 +44,7 @@ from . import formats
 from .paged import PagedCache
 
 
-def pair_indices(rotary_dim, layout):
+def pair_indices(rotary_dim, layout, head_dim=None):
     """Index arrays (first, second) of the rotated pairs."""
     if rotary_dim % 2:
         raise ValueError("rotary_dim must be even")
@@ -49,6 +54,10 @@ def pair_indices(rotary_dim, layout):
         return i, i + half
     if layout == "interleaved":
         return 2 * i, 2 * i + 1
+    if layout == "half_proportional":
+        if head_dim is None or head_dim % 2 or rotary_dim > head_dim:
+            raise ValueError("half_proportional needs an even head_dim >= rotary_dim")
+        return i, i + head_dim // 2
     raise ValueError(layout)
 
 
@@ -59,7 +68,7 @@ def rotate(x, cos, sin, rotary_dim, layout):
     dims; dims >= R are returned unchanged.
     """
     x = np.asarray(x, dtype=np.float64)
-    a_idx, b_idx = pair_indices(rotary_dim, layout)
+    a_idx, b_idx = pair_indices(rotary_dim, layout, x.shape[-1])
     out = x.copy()
     a = x[..., a_idx]
     b = x[..., b_idx]

@@ -242,12 +242,14 @@ def new_tokens(w):
 
 def freqs_table(w, max_pos=None):
     """RoPE table [max_pos, R/2, 2] float32 of (cos, sin) at angle
-    pos * theta**(-2i/R) for pair i (the RoPE rotation angle of the Algenta
-    page's ``rope_rotation_angle`` with d = rotary_dim), computed in float64
-    and rounded to float32."""
+    pos * theta**(-2i/d) for pair i (the RoPE rotation angle of the Algenta
+    page's ``rope_rotation_angle``) with d = rotary_dim, or d = head_dim for
+    the proportional layout (aria_kernel ``rope_half_proportional``: the full
+    head_dim denominator), computed in float64 and rounded to float32."""
     n = w.max_pos if max_pos is None else max_pos
     half = w.rotary_dim // 2
-    inv = w.rope_theta ** (-2.0 * np.arange(half, dtype=np.float64) / w.rotary_dim)
+    denom = w.head_dim if w.rope_layout == "half_proportional" else w.rotary_dim
+    inv = w.rope_theta ** (-2.0 * np.arange(half, dtype=np.float64) / denom)
     ang = np.arange(n, dtype=np.float64)[:, None] * inv[None, :]
     return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
 

@@ -7,8 +7,10 @@ position 0, and makes q.k depend only on the position difference; the
 interleaved layout pairs adjacent components and the half layout pairs the
 two halves (Mojo page, ``interleaved`` parameter; aria_kernel ``rope`` /
 ``rope_half``); partial rotary leaves the dims past ``rotary_dim`` alone
-(aria_kernel ``rope_half_partial``); the RoPE angle of pair i at position p
-is p * base**(-2i/d) (Algenta, "Five ways to inject position").
+(aria_kernel ``rope_half_partial``); p-RoPE pairs (i, i + D/2) and rotates
+only the first pairs, with the full head_dim denominator (aria_kernel
+``rope_half_proportional``); the RoPE angle of pair i at position p is
+p * base**(-2i/d) (Algenta, "Five ways to inject position").
 """
 
 import math
@@ -82,6 +84,48 @@ def test_partial_rotary_leaves_tail(layout):
     y = rope.rotate(x, t[8, :, 0], t[8, :, 1], 128, layout)
     np.testing.assert_array_equal(y[:, 128:], x[:, 128:])
     assert not np.allclose(y[:, :128], x[:, :128])
+
+
+def test_proportional_layout():
+    """aria_kernel rope_half_proportional (p-RoPE): the rotate-half pairing
+    over the whole head, (i, i + D/2); only the first pairs rotate, the rest
+    stay identity; with every pair rotated it is plain rope_half; frequencies
+    use the full head_dim denominator."""
+    rng = np.random.default_rng(4)
+    D, R = 64, 32                                    # 16 of 32 pairs rotate
+    t = _table(50, D, 1e4)[:, :R // 2]               # full-head denominator, first R/2 pairs
+    x = rng.standard_normal((3, D))
+    y = rope.rotate(x, t[7, :, 0], t[7, :, 1], R, "half_proportional")
+    rot = np.r_[0:R // 2, D // 2:D // 2 + R // 2]
+    keep = np.setdiff1d(np.arange(D), rot)
+    np.testing.assert_array_equal(y[:, keep], x[:, keep])              # the other pairs are identity
+    assert not np.allclose(y[:, rot], x[:, rot])
+    # pairing: dim 0 goes with dim D/2 (not R/2 as in the partial layout)
+    e0 = np.zeros(D); e0[0] = 1.0
+    z = rope.rotate(e0, t[3, :, 0], t[3, :, 1], R, "half_proportional")
+    assert z[0] == math.cos(3) and z[D // 2] == math.sin(3) and z[R // 2] == 0.0
+    # every pair rotated: the plain rotate-half layout
+    tf = _table(50, D, 1e4)
+    np.testing.assert_array_equal(rope.rotate(x, tf[9, :, 0], tf[9, :, 1], D, "half_proportional"),
+                                  rope.rotate(x, tf[9, :, 0], tf[9, :, 1], D, "half"))
+    # identity at 0, norms kept, q.k a function of the position difference
+    np.testing.assert_array_equal(rope.rotate(x, t[0, :, 0], t[0, :, 1], R, "half_proportional"), x)
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    assert abs(np.linalg.norm(rope.rotate(q, t[40, :, 0], t[40, :, 1], R, "half_proportional")) -
+               np.linalg.norm(q)) < 1e-12
+    def dot(m, n):
+        return (rope.rotate(q, t[m, :, 0], t[m, :, 1], R, "half_proportional") @
+                rope.rotate(k, t[n, :, 0], t[n, :, 1], R, "half_proportional"))
+    assert abs(dot(12, 19) - dot(2, 9)) < 1e-12
+    # brute force agrees
+    for p in (0, 5, 31):
+        b = brute.rope_row(list(x[1]), list(t[p, :, 0]), list(t[p, :, 1]), R, "half_proportional")
+        np.testing.assert_allclose(rope.rotate(x[1], t[p, :, 0], t[p, :, 1], R, "half_proportional"),
+                                   np.array(b), rtol=0, atol=1e-15)
+    # the synthetic table of a proportional workload uses the full head_dim denominator
+    w = synth.custom(q_lens=[3], kv_lens=[3], num_q_heads=2, num_kv_heads=1, head_dim=D, rotary_dim=R,
+                     rope_layout="half_proportional", rope_theta=1e4)
+    np.testing.assert_array_equal(synth.freqs_table(w), _table(w.max_pos, D, 1e4)[:, :R // 2].astype(np.float32))
 
 
 def test_slots_follow_the_append():
