@@ -89,8 +89,16 @@ typedef enum { NK_F32 = 0, NK_BF16 = 1, NK_E4M3 = 2 } nk_dtype_t;
 
 /* NK_ROPE_HALF pairs dim i with dim i + rotary_dim/2 (rotate-half);
  * NK_ROPE_INTERLEAVED pairs dims 2i and 2i+1 (Mojo `interleaved`;
- * aria_kernel `rope` / `rope_half`). */
-typedef enum { NK_ROPE_HALF = 0, NK_ROPE_INTERLEAVED = 1 } nk_rope_layout_t;
+ * aria_kernel `rope` / `rope_half`); NK_ROPE_HALF_PROPORTIONAL pairs dim i
+ * with dim i + head_dim/2 and rotates only the pairs i < rotary_dim/2, the
+ * others passing unchanged (aria_kernel `rope_half_proportional`, p-RoPE;
+ * the caller builds its table with the head_dim denominator).  In every
+ * layout pair i reads table entry i. */
+typedef enum {
+  NK_ROPE_HALF = 0,
+  NK_ROPE_INTERLEAVED = 1,
+  NK_ROPE_HALF_PROPORTIONAL = 2
+} nk_rope_layout_t;
 
 typedef enum {
   NK_OK = 0,

@@ -212,7 +212,8 @@ int nk_rope_qk_write_paged(const void *q, const void *k, const void *v, int32_t 
   int st = check_cache(cache);
   if (st != NK_OK) return st;
   if (num_q_heads % cache->num_kv_heads) return NK_ERR_INVALID_ARG;
-  if (layout != NK_ROPE_HALF && layout != NK_ROPE_INTERLEAVED) return NK_ERR_INVALID_ARG;
+  if (layout != NK_ROPE_HALF && layout != NK_ROPE_INTERLEAVED && layout != NK_ROPE_HALF_PROPORTIONAL)
+    return NK_ERR_INVALID_ARG;
   if (rotary_dim <= 0 || rotary_dim > cache->head_dim || rotary_dim % 16) return NK_ERR_UNSUPPORTED;
   const bool ok_types = (in_dtype == NK_F32 && cache->dtype == NK_F32) ||
                         (in_dtype == NK_BF16 && (cache->dtype == NK_BF16 || cache->dtype == NK_E4M3));

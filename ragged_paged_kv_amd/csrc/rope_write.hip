@@ -5,8 +5,9 @@
 // write rotated Q to the output, update the keys of the paged cache in
 // place), with V appended unrotated to the same slot; pair layouts of the
 // aria_kernel crate (`rope`: interleaved, `rope_half`: rotate-half,
-// `rope_half_partial`: only the first rotary_dim dims).  float8 caches store
-// one scale per (token, kv head), absmax / 448.
+// `rope_half_partial`: only the first rotary_dim dims, `rope_half_proportional`:
+// rotate-half pairs over the whole head, only the first rotary_dim/2
+// rotated).  float8 caches store one scale per (token, kv head), absmax / 448.
 //
 // Rounding: the rotation runs in float64 and every stored element is rounded
 // once from it (see round_odd_f32), so q_out and the appended cache rows are
@@ -16,12 +17,14 @@
 // units exceed 1024 threads).  One thread owns a "unit" of 16
 // elements of one head of one token: for the rotate-half layout the 8
 // elements [8j, 8j+8) and their partners [R/2+8j, R/2+8j+8); for the
-// interleaved layout and for pass-through dims, 16 consecutive elements.
+// proportional layout [8j, 8j+8) and [D/2+8j, D/2+8j+8); for the interleaved
+// layout and for pass-through dims, 16 consecutive elements.
 // Consecutive threads own consecutive units of a head, so every load and
 // K-store is a coalesced 16/32-byte vector access.  The D/16 units of a head
 // are consecutive lanes of one wave, so the float8 absmax is a lane-group
-// reduction.  V is stored dimension-major inside a page: its stores are
-// per-element (stride page_size).
+// reduction.  V goes to the page's 16-byte runs of 4 consecutive slots:
+// whole runs from LDS where a run's 4 slots are all new, single elements
+// where a segment's new slots start or end inside one (append_v_quads).
 
 #include "common.h"
 #include "internal.h"
@@ -239,7 +242,8 @@ NK_DEVICE void append_v_quads(const RopeArgs &a, int t0, int ntok, int head, uin
   }
 }
 
-template <typename TIn, int CACHE, bool INTERLEAVED>
+// LAYOUT: NK_ROPE_HALF, NK_ROPE_INTERLEAVED or NK_ROPE_HALF_PROPORTIONAL
+template <typename TIn, int CACHE, int LAYOUT>
 __global__ void __launch_bounds__(1024) rope_write_kernel(RopeArgs a, int units_per_token, int blocks_per_token,
                                                           int v_blocks, int v_group) {
   extern __shared__ __attribute__((aligned(16))) uint8_t v_stage[];
@@ -279,10 +283,15 @@ __global__ void __launch_bounds__(1024) rope_write_kernel(RopeArgs a, int units_
   const TIn *src = (const TIn *)(kind == 0 ? a.q : a.k) + ((size_t)t * hn + head) * D;
 
   // run A / run B of this unit and whether it rotates
+  constexpr bool INTERLEAVED = LAYOUT == NK_ROPE_INTERLEAVED;
   const bool rotates = INTERLEAVED ? 16 * j < R : j < (R >> 4);
   int a0, b0;
   if (INTERLEAVED) {
     a0 = 16 * j; b0 = a0 + 8;
+  } else if (LAYOUT == NK_ROPE_HALF_PROPORTIONAL) {
+    // pairs span the whole head: unit j holds dims 8j.. and D/2 + 8j..,
+    // rotated when its pairs are among the first R/2
+    a0 = 8 * j; b0 = (D >> 1) + 8 * j;
   } else if (rotates) {
     a0 = 8 * j; b0 = (R >> 1) + 8 * j;
   } else {
@@ -378,7 +387,9 @@ hipError_t launch_layout(const RopeArgs &a, hipStream_t stream) {
   if (qk_blocks + v_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const unsigned grid = (unsigned)(qk_blocks + v_blocks);
   const size_t lds = (size_t)(block / 64) * 4 * D * esz;
-  auto k = a.layout == NK_ROPE_INTERLEAVED ? rope_write_kernel<TIn, CACHE, true> : rope_write_kernel<TIn, CACHE, false>;
+  auto k = a.layout == NK_ROPE_INTERLEAVED ? rope_write_kernel<TIn, CACHE, NK_ROPE_INTERLEAVED>
+           : a.layout == NK_ROPE_HALF_PROPORTIONAL ? rope_write_kernel<TIn, CACHE, NK_ROPE_HALF_PROPORTIONAL>
+                                                  : rope_write_kernel<TIn, CACHE, NK_ROPE_HALF>;
   return launch(k, dim3(grid), dim3(block), lds, stream, a, upt, bpt, (int)v_blocks, v_group);
 }
 

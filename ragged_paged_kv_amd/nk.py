@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnk.so")
 
 NK_F32, NK_BF16, NK_E4M3 = 0, 1, 2
-NK_ROPE_HALF, NK_ROPE_INTERLEAVED = 0, 1
+NK_ROPE_HALF, NK_ROPE_INTERLEAVED, NK_ROPE_HALF_PROPORTIONAL = 0, 1, 2
 NK_OK, NK_ERR_INVALID_ARG, NK_ERR_UNSUPPORTED, NK_ERR_WORKSPACE, NK_ERR_DEVICE = 0, 1, 2, 3, 4
 
 EXPORTS = ("nk_rope_qk_write_paged", "nk_ragged_paged_attention", "nk_ragged_paged_attention_band",
@@ -180,7 +180,8 @@ def rope_qk_write_paged(q, k, v, q_offsets, kv_lens, freqs, cache, rotary_dim, l
     if position_ids is not None:
         _i32(position_ids, "position_ids")
     _dev(q, k, v, q_out, q_offsets, kv_lens, position_ids, freqs, cache.k_pages)
-    lay = {"half": NK_ROPE_HALF, "interleaved": NK_ROPE_INTERLEAVED}[layout]
+    lay = {"half": NK_ROPE_HALF, "interleaved": NK_ROPE_INTERLEAVED,
+           "half_proportional": NK_ROPE_HALF_PROPORTIONAL}[layout]
     c = cache.struct()
     st = lib().nk_rope_qk_write_paged(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(q_out),
                                       _ptr(q_offsets), _ptr(kv_lens), _ptr(position_ids), _ptr(freqs),

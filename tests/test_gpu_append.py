@@ -32,6 +32,15 @@ CASES = {
                                       rotary_dim=128),
     "e4m3_d64_p32_decode": dict(q_lens=[1] * 6, kv_lens=[1, 2, 3, 4, 5, 64], num_q_heads=4, num_kv_heads=1,
                                 head_dim=64, page_size=32, cache_dtype="e4m3", explicit_positions=False),
+    # p-RoPE: rotate-half pairs over the whole head, only the first rotated
+    "bf16_d128_p16_proportional": dict(**RAGGED, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                       rope_layout="half_proportional", rotary_dim=64),
+    "e4m3_d256_p32_proportional": dict(q_lens=[5, 9, 2, 1], kv_lens=[9, 9, 70, 33], num_q_heads=4,
+                                       num_kv_heads=2, head_dim=256, page_size=32, cache_dtype="e4m3",
+                                       rope_layout="half_proportional", rotary_dim=64),
+    "f32_d64_p16_proportional_full": dict(q_lens=[7, 3], kv_lens=[20, 3], num_q_heads=2, num_kv_heads=2,
+                                          head_dim=64, in_dtype="f32", cache_dtype="f32",
+                                          rope_layout="half_proportional", rotary_dim=64),
     # 136 heads x 8 units per token: a token's Q/K units span two work-groups
     "bf16_d128_hq128_two_blocks_per_token": dict(q_lens=[3, 6], kv_lens=[10, 6], num_q_heads=128,
                                                  num_kv_heads=8, head_dim=128),

@@ -50,6 +50,11 @@ CASES = {
                                  head_dim=256),
     "prefill_d256_g8_fp8": dict(q_lens=[70, 5], kv_lens=[100, 5], num_q_heads=16, num_kv_heads=2,
                                 head_dim=256, page_size=32, cache_dtype="e4m3"),
+    # p-RoPE (a quarter of the pairs rotated) under a sliding window, decode rows included
+    "proportional_rope_d256_window": dict(q_lens=[90, 1, 1], kv_lens=[90, 700, 40], num_q_heads=8,
+                                          num_kv_heads=2, head_dim=256, page_size=32,
+                                          rope_layout="half_proportional", rotary_dim=64, window_left=200,
+                                          rope_theta=1e6),
 }
 
 
