@@ -17,6 +17,8 @@ What is computed, per the pages:
   frequencies use the full head_dim denominator).
 * NumKong matrix-kernels page, ``attention_rope``: every channel pair of each
   head is rotated by per-token cos/sin grids shared across heads.
+* Mojo page, ``mrope_section``: M-RoPE partitions the head dimension across
+  modalities.
 
 Readings taken where the pages leave a step open:
 
@@ -31,6 +33,10 @@ Readings taken where the pages leave a step open:
   (``kv_len`` counts keys after the append); without position ids the
   position is that slot;
 * V is stored unrotated in the same slot as K;
+* M-RoPE: the sections count rotated pairs (summing to R/2, in pair order);
+  each token carries one position per section, and pair i reads the table
+  row of its section's position (the multimodal RoPE of vision-language
+  models: temporal, height, width);
 * float8 cache: one scale per (token, kv head), ``scale = fl32(absmax/448)``
   of the float64 row to be stored, codes ``e4m3(x / scale)``.
 
@@ -92,21 +98,42 @@ def token_slots(q_offsets, kv_lens, position_ids=None):
     return seq, slot, pos
 
 
+def pair_positions(position_ids, sections, rotary_dim):
+    """Position of every (token, rotated pair) under M-RoPE: position_ids
+    [n_sections, T], sections = rotated pairs per section (sum R/2); pair i
+    takes the position of the section that holds it.  Returns [T, R/2]."""
+    position_ids = np.asarray(position_ids, dtype=np.int64)
+    sections = [int(x) for x in sections]
+    if sum(sections) != rotary_dim // 2 or position_ids.shape[0] != len(sections):
+        raise ValueError("sections must count R/2 pairs, one position stream each")
+    sec_of_pair = np.repeat(np.arange(len(sections)), sections)           # [R/2]
+    return position_ids[sec_of_pair, :].T                                # [T, R/2]
+
+
 def rope_qk_write_paged(q, k, v, in_dtype, q_offsets, kv_lens, position_ids,
-                        freqs, rotary_dim, layout, cache: PagedCache, page_table):
+                        freqs, rotary_dim, layout, cache: PagedCache, page_table, mrope_sections=None):
     """Rotate Q and K, store K/V into the cache.
 
     q [T, Hq, D], k/v [T, Hkv, D]: float64 values of the stored inputs.
     freqs [max_pos, R/2, 2]: the float32 table (values widened).
+    With ``mrope_sections`` (rotated pairs per section), position_ids is
+    [n_sections, T] and pair i rotates by its section's position.
     Returns (q_out as stored, updated copy of the cache).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     freqs = np.asarray(freqs, dtype=np.float64)
-    seq, slot, pos = token_slots(q_offsets, kv_lens, position_ids)
-    cos = freqs[pos, :, 0][:, None, :]          # [T, 1, R/2] shared across heads
-    sin = freqs[pos, :, 1][:, None, :]
+    if mrope_sections is None:
+        seq, slot, pos = token_slots(q_offsets, kv_lens, position_ids)
+        cos = freqs[pos, :, 0][:, None, :]      # [T, 1, R/2] shared across heads
+        sin = freqs[pos, :, 1][:, None, :]
+    else:
+        seq, slot, _ = token_slots(q_offsets, kv_lens)
+        pp = pair_positions(position_ids, mrope_sections, rotary_dim)    # [T, R/2]
+        pair = np.arange(rotary_dim // 2)[None, :]
+        cos = freqs[pp, pair, 0][:, None, :]
+        sin = freqs[pp, pair, 1][:, None, :]
     q_rot = rotate(q, cos, sin, rotary_dim, layout)
     k_rot = rotate(k, cos, sin, rotary_dim, layout)
     q_out = formats.storage_round(q_rot, in_dtype)

@@ -9,8 +9,10 @@ two halves (Mojo page, ``interleaved`` parameter; aria_kernel ``rope`` /
 ``rope_half``); partial rotary leaves the dims past ``rotary_dim`` alone
 (aria_kernel ``rope_half_partial``); p-RoPE pairs (i, i + D/2) and rotates
 only the first pairs, with the full head_dim denominator (aria_kernel
-``rope_half_proportional``); the RoPE angle of pair i at position p is
-p * base**(-2i/d) (Algenta, "Five ways to inject position").
+``rope_half_proportional``); M-RoPE splits the pairs into sections, each
+rotated by its own position stream (Mojo ``mrope_section``); the RoPE angle
+of pair i at position p is p * base**(-2i/d) (Algenta, "Five ways to inject
+position").
 """
 
 import math
@@ -126,6 +128,60 @@ def test_proportional_layout():
     w = synth.custom(q_lens=[3], kv_lens=[3], num_q_heads=2, num_kv_heads=1, head_dim=D, rotary_dim=R,
                      rope_layout="half_proportional", rope_theta=1e4)
     np.testing.assert_array_equal(synth.freqs_table(w), _table(w.max_pos, D, 1e4)[:, :R // 2].astype(np.float32))
+
+
+def _mrope_run(q, k, sections, pos_streams, t, layout="half"):
+    """Rotate [T, 1, D] rows through the oracle's fused step with M-RoPE."""
+    T, _, D = q.shape
+    R = 2 * sum(sections)
+    from oracle.paged import PagedCache as PC
+    cache = PC("f32", 1, 1, 16, D)
+    q_out, c2 = rope.rope_qk_write_paged(q, k, k, "f32", [0, T], [T], np.asarray(pos_streams), t, R, layout,
+                                         cache, np.array([[0]]), mrope_sections=sections)
+    kk = np.array([c2.k[0, 0, j] for j in range(T)])
+    return q_out, kk
+
+
+def test_mrope_sections():
+    """Mojo mrope_section: the head dimension split across modalities; each
+    section of pairs rotates by its own position stream.  One section, or
+    every stream equal, is plain RoPE; a stream moves only its own pairs;
+    q.k depends only on the per-section position differences."""
+    rng = np.random.default_rng(5)
+    D, T = 64, 6
+    sections = [8, 16, 8]                                   # pairs: 32 = R/2 with R = D
+    t = _table(100, D, 1e4)
+    q = rng.standard_normal((T, 1, D)); k = rng.standard_normal((T, 1, D))
+    base = np.array([3, 9, 14, 20, 27, 41])
+    same = np.stack([base, base, base])
+    for layout in ("half", "interleaved"):
+        q_m, k_m = _mrope_run(q, k, sections, same, t, layout)
+        q_p = formats.storage_round(rope.rotate(q, t[base, :, 0][:, None, :], t[base, :, 1][:, None, :], D, layout), "f32")
+        np.testing.assert_array_equal(q_m, q_p)
+        q_1, _ = _mrope_run(q, k, [32], base[None, :], t, layout)
+        np.testing.assert_array_equal(q_1, q_p)
+        # a different stream for section 1 moves only section 1's pairs (and their partners)
+        streams = np.stack([base, base + 7, base])
+        q_d, _ = _mrope_run(q, k, sections, streams, t, layout)
+        a_idx, b_idx = rope.pair_indices(D, layout, D)
+        sec = np.repeat(np.arange(3), sections)
+        moved = np.zeros(D, dtype=bool)
+        moved[a_idx[sec == 1]] = True
+        moved[b_idx[sec == 1]] = True
+        np.testing.assert_array_equal(q_d[:, :, ~moved], q_m[:, :, ~moved])
+        assert not np.allclose(q_d[:, :, moved], q_m[:, :, moved])
+    # pair positions follow the sections in pair order
+    pp = rope.pair_positions(np.stack([base, base + 1, base + 2]), sections, D)
+    assert pp.shape == (T, 32) and (pp[:, :8] == base[:, None]).all() and (pp[:, 8:24] == base[:, None] + 1).all()
+    # relative position per section: shifting every stream by the same amount keeps q.k
+    def dots(streams):
+        qm, km = _mrope_run(q, k, sections, streams, t)
+        return qm[0, 0] @ km[5]
+    s1 = np.stack([base, base + 2, base + 5])
+    assert abs(dots(s1) - dots(s1 + 4)) < 1e-4                # float32 storage rounding
+    assert abs(dots(s1) - dots(np.stack([base, 2 * base, base + 5]))) > 1e-3    # section 1's differences change
+    with pytest.raises(ValueError):
+        rope.pair_positions(same, [8, 8, 8], D)               # must count R/2 pairs
 
 
 def test_slots_follow_the_append():
