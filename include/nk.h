@@ -162,6 +162,29 @@ int nk_rope_qk_write_paged(const void *q, const void *k, const void *v, int32_t 
                            const nk_paged_kv_t *cache, void *stream);
 
 /*
+ * nk_rope_qk_write_paged_mrope -- the same with M-RoPE sections.
+ *
+ * Mojo page, generic_fused_qk_rope_bshd_paged_ragged_kernel_api, parameter
+ * mrope_section (the head dimension partitioned across modalities).  The
+ * rotated pairs are split, in pair order, into num_sections sections of
+ * section_pairs_host[s] pairs (host array; each a positive multiple of 8,
+ * summing to rotary_dim/2); position_ids is [num_sections][total_tokens]
+ * (device) and pair p of token t rotates by row
+ * position_ids[section(p)][t] of the table.  num_sections 0 is
+ * nk_rope_qk_write_paged (position_ids [total_tokens] or NULL); at most 4
+ * sections (NK_ERR_INVALID_ARG beyond, or when the sections do not sum to
+ * rotary_dim/2; NK_ERR_UNSUPPORTED for a section that is not a multiple of
+ * 8 pairs).  Every other argument is as above.
+ */
+int nk_rope_qk_write_paged_mrope(const void *q, const void *k, const void *v, int32_t in_dtype,
+                                 void *q_out, const int32_t *q_offsets, const int32_t *kv_lens,
+                                 const int32_t *position_ids, int32_t num_sections,
+                                 const int32_t *section_pairs_host, const float *freqs, int32_t max_pos,
+                                 int32_t rotary_dim, int32_t layout, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_q_heads,
+                                 const nk_paged_kv_t *cache, void *stream);
+
+/*
  * nk_ragged_paged_attention -- causal (optionally windowed) GQA attention.
  *
  * NumKong matrix-kernels page, attention_packed: query row i of a segment

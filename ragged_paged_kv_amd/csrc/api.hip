@@ -208,7 +208,31 @@ int nk_rope_qk_write_paged(const void *q, const void *k, const void *v, int32_t 
                            int32_t rotary_dim, int32_t layout, int32_t num_seqs,
                            int32_t total_tokens, int32_t num_q_heads,
                            const nk_paged_kv_t *cache, void *stream) {
+  return nk_rope_qk_write_paged_mrope(q, k, v, in_dtype, q_out, q_offsets, kv_lens, position_ids, 0, nullptr,
+                                      freqs, max_pos, rotary_dim, layout, num_seqs, total_tokens,
+                                      num_q_heads, cache, stream);
+}
+
+int nk_rope_qk_write_paged_mrope(const void *q, const void *k, const void *v, int32_t in_dtype,
+                                 void *q_out, const int32_t *q_offsets, const int32_t *kv_lens,
+                                 const int32_t *position_ids, int32_t num_sections,
+                                 const int32_t *section_pairs_host, const float *freqs, int32_t max_pos,
+                                 int32_t rotary_dim, int32_t layout, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_q_heads,
+                                 const nk_paged_kv_t *cache, void *stream) {
   if (num_seqs < 0 || total_tokens < 0 || num_q_heads <= 0 || max_pos <= 0) return NK_ERR_INVALID_ARG;
+  if (num_sections < 0 || num_sections > kMaxMropeSections) return NK_ERR_INVALID_ARG;
+  int32_t mrope_end[kMaxMropeSections] = {};
+  if (num_sections > 0) {
+    if (!section_pairs_host || !position_ids) return NK_ERR_INVALID_ARG;
+    int32_t sum = 0;
+    for (int s = 0; s < num_sections; ++s) {
+      if (section_pairs_host[s] <= 0 || section_pairs_host[s] % 8) return NK_ERR_UNSUPPORTED;
+      sum += section_pairs_host[s];
+      mrope_end[s] = sum;
+    }
+    if (sum != rotary_dim / 2) return NK_ERR_INVALID_ARG;
+  }
   int st = check_cache(cache);
   if (st != NK_OK) return st;
   if (num_q_heads % cache->num_kv_heads) return NK_ERR_INVALID_ARG;
@@ -228,6 +252,8 @@ int nk_rope_qk_write_paged(const void *q, const void *k, const void *v, int32_t 
   a.max_pos = max_pos;
   a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.hq = num_q_heads;
   a.cache = *cache;
+  a.mrope_sections = num_sections;
+  for (int s = 0; s < kMaxMropeSections; ++s) a.mrope_end[s] = mrope_end[s];
   return launch_rope_write(a, (hipStream_t)stream) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
 }
 

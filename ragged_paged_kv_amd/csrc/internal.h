@@ -12,6 +12,8 @@
 
 namespace nk {
 
+constexpr int kMaxMropeSections = 4;
+
 struct RopeArgs {
   const void *q, *k, *v;
   void *q_out;
@@ -20,6 +22,10 @@ struct RopeArgs {
   int32_t rotary_dim, layout, in_dtype, max_pos;
   int32_t num_seqs, total_tokens, hq;
   nk_paged_kv_t cache;
+  // M-RoPE: position_ids is [mrope_sections][total_tokens]; section s holds
+  // rotated pairs [mrope_end[s-1], mrope_end[s]) (0: one position per token)
+  int32_t mrope_sections;
+  int32_t mrope_end[kMaxMropeSections];
 };
 
 struct AttnArgs {

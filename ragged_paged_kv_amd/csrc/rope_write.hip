@@ -308,7 +308,17 @@ __global__ void __launch_bounds__(1024) rope_write_kernel(RopeArgs a, int units_
   if (rotates) {
     // out-of-range positions (a precondition violation) are clamped so that
     // the table read stays inside the table
-    const int pos = min(max(a.position_ids ? a.position_ids[t] : slot, 0), a.max_pos - 1);
+    int p = slot;
+    if (a.mrope_sections > 0) {
+      // the unit's 8 pairs (8j..8j+7) lie in one section (sections are
+      // multiples of 8 pairs); that section's position stream
+      int sec = 0;
+      while (sec + 1 < a.mrope_sections && 8 * j >= a.mrope_end[sec]) ++sec;
+      p = a.position_ids[(size_t)sec * a.total_tokens + t];
+    } else if (a.position_ids) {
+      p = a.position_ids[t];
+    }
+    const int pos = min(max(p, 0), a.max_pos - 1);
     const f32x4_t *cs = (const f32x4_t *)(a.freqs + ((size_t)pos * (R >> 1) + 8 * j) * 2);
     double c[8], sn[8];
 #pragma unroll

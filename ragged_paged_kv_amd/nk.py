@@ -19,7 +19,7 @@ NK_F32, NK_BF16, NK_E4M3 = 0, 1, 2
 NK_ROPE_HALF, NK_ROPE_INTERLEAVED, NK_ROPE_HALF_PROPORTIONAL = 0, 1, 2
 NK_OK, NK_ERR_INVALID_ARG, NK_ERR_UNSUPPORTED, NK_ERR_WORKSPACE, NK_ERR_DEVICE = 0, 1, 2, 3, 4
 
-EXPORTS = ("nk_rope_qk_write_paged", "nk_ragged_paged_attention", "nk_ragged_paged_attention_band",
+EXPORTS = ("nk_rope_qk_write_paged", "nk_rope_qk_write_paged_mrope", "nk_ragged_paged_attention", "nk_ragged_paged_attention_band",
            "nk_ragged_paged_attention_workspace_size", "nk_ragged_paged_attention_split_tokens",
            "nk_attention_lse_merge", "nk_status_string", "nk_version", "nk_profile_enable",
            "nk_profile_reset", "nk_profile_read")
@@ -55,6 +55,9 @@ def lib():
         L.nk_rope_qk_write_paged.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
                                              i32, i32, i32, cache_p, vp]
         L.nk_rope_qk_write_paged.restype = ctypes.c_int
+        L.nk_rope_qk_write_paged_mrope.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
+                                                   i32, i32, i32, cache_p, vp]
+        L.nk_rope_qk_write_paged_mrope.restype = ctypes.c_int
         L.nk_ragged_paged_attention.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, vp, vp, i32,
                                                 i32, i32, i32, i32, i32, vp, sz, vp]
         L.nk_ragged_paged_attention.restype = ctypes.c_int
@@ -164,9 +167,12 @@ class PagedKVCache:
 
 
 def rope_qk_write_paged(q, k, v, q_offsets, kv_lens, freqs, cache, rotary_dim, layout="half",
-                        position_ids=None, q_out=None, stream=None):
+                        position_ids=None, q_out=None, stream=None, mrope_sections=None):
     """Rotate q and k by ``freqs`` [max_pos, R/2, 2] and append k/v to the
-    cache; returns q_out ([T, Hq, D], may be q itself)."""
+    cache; returns q_out ([T, Hq, D], may be q itself).  With
+    ``mrope_sections`` (rotated pairs per section, multiples of 8 summing to
+    R/2), position_ids is [n_sections, T] and each section of pairs rotates
+    by its own positions."""
     T, hq, d = q.shape
     if q_out is None:
         q_out = torch.empty_like(q)
@@ -183,11 +189,22 @@ def rope_qk_write_paged(q, k, v, q_offsets, kv_lens, freqs, cache, rotary_dim, l
     lay = {"half": NK_ROPE_HALF, "interleaved": NK_ROPE_INTERLEAVED,
            "half_proportional": NK_ROPE_HALF_PROPORTIONAL}[layout]
     c = cache.struct()
-    st = lib().nk_rope_qk_write_paged(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(q_out),
-                                      _ptr(q_offsets), _ptr(kv_lens), _ptr(position_ids), _ptr(freqs),
-                                      freqs.shape[0], rotary_dim, lay, kv_lens.shape[0], T, hq,
-                                      ctypes.byref(c), _stream(stream))
-    _check(st, "nk_rope_qk_write_paged")
+    if mrope_sections is None:
+        st = lib().nk_rope_qk_write_paged(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(q_out),
+                                          _ptr(q_offsets), _ptr(kv_lens), _ptr(position_ids), _ptr(freqs),
+                                          freqs.shape[0], rotary_dim, lay, kv_lens.shape[0], T, hq,
+                                          ctypes.byref(c), _stream(stream))
+        _check(st, "nk_rope_qk_write_paged")
+        return q_out
+    if position_ids is None or position_ids.shape != (len(mrope_sections), T):
+        raise ValueError("M-RoPE needs position_ids [n_sections, T]")
+    sec = (ctypes.c_int32 * len(mrope_sections))(*[int(x) for x in mrope_sections])
+    st = lib().nk_rope_qk_write_paged_mrope(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(q_out),
+                                            _ptr(q_offsets), _ptr(kv_lens), _ptr(position_ids),
+                                            len(mrope_sections), ctypes.cast(sec, ctypes.c_void_p), _ptr(freqs),
+                                            freqs.shape[0], rotary_dim, lay, kv_lens.shape[0], T, hq,
+                                            ctypes.byref(c), _stream(stream))
+    _check(st, "nk_rope_qk_write_paged_mrope")
     return q_out
 
 

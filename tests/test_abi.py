@@ -155,3 +155,24 @@ def test_profile_api_without_gpu(L):
     assert L.nk_profile_enable(-1) == nk.NK_ERR_INVALID_ARG
     nk.profile_enable(True, ["attn_decode", "lse_merge"])             # host-side only, no launch
     nk.profile_enable(False)
+
+
+def test_mrope_validation(L):
+    c = _cache()
+
+    def mrope(sections, pos=1, **kw):
+        a = dict(q=1, k=1, v=1, in_dtype=nk.NK_BF16, q_out=1, q_offsets=1, kv_lens=1, freqs=1, max_pos=64,
+                 rotary_dim=128, layout=nk.NK_ROPE_HALF, num_seqs=1, total=4, hq=4)
+        a.update(kw)
+        arr = None if sections is None else (ctypes.c_int32 * max(len(sections), 1))(*sections)
+        return L.nk_rope_qk_write_paged_mrope(a["q"], a["k"], a["v"], a["in_dtype"], a["q_out"], a["q_offsets"],
+                                              a["kv_lens"], pos, 0 if sections is None else len(sections),
+                                              None if arr is None else ctypes.cast(arr, ctypes.c_void_p), a["freqs"],
+                                              a["max_pos"], a["rotary_dim"], a["layout"], a["num_seqs"], a["total"],
+                                              a["hq"], ctypes.byref(c), None)
+    assert mrope([16, 24, 24], total=0) == nk.NK_OK                   # valid, empty batch
+    assert mrope([16, 24, 16], total=0) == nk.NK_ERR_INVALID_ARG      # 56 pairs, not rotary_dim/2 = 64
+    assert mrope([20, 20, 24], total=0) == nk.NK_ERR_UNSUPPORTED      # not multiples of 8 pairs
+    assert mrope([16, 16, 16, 8, 8], total=0) == nk.NK_ERR_INVALID_ARG    # more than 4 sections
+    assert mrope([64], pos=None, total=0) == nk.NK_ERR_INVALID_ARG    # sections need position streams
+    assert mrope(None, total=0) == nk.NK_OK                           # no sections: the plain call
