@@ -51,6 +51,8 @@ DESCR = {
     "mixed_window_bf16": "sliding-window mixed batch, bf16: 4 prefill 1024-4096 + 60 decode 2048-8192, Hq16/Hkv8, D256, window 1024",
     "tiny_prefill_f32": "tiny ragged prefill, fp32: segments 5 and 12, Hq4/Hkv2, D64",
     "prefill_bidir_bf16": "the ragged prefill batch with every row seeing its whole segment (band unbounded on both sides)",
+    "prefill_mrope_bf16": "the ragged prefill batch with M-RoPE: three position streams over 16/24/24 pairs",
+    "prefill_prope_bf16": "the ragged prefill batch with p-RoPE: rotate-half pairs over the head, a quarter rotated",
 }
 # kernels whose launches carry timing events inside the timed region
 DOMINANT = {
@@ -60,6 +62,8 @@ DOMINANT = {
     "mixed_window_bf16": ("attn_prefill", "attn_decode"),
     "tiny_prefill_f32": ("attn_f32",),
     "prefill_bidir_bf16": ("attn_prefill",),
+    "prefill_mrope_bf16": ("rope_write",),
+    "prefill_prope_bf16": ("rope_write",),
 }
 KERNEL_SOURCES = ["attn_decode.hip", "attn_prefill.hip", "rope_write.hip", "lse_merge.hip", "common.h", "internal.h"]
 # the sources a kernel family is built from: a counter summary stays valid
@@ -128,6 +132,8 @@ def prepare(name):
     st.cache = nk.PagedKVCache(kp, vp, t(w.page_table.astype(np.int32)), ks, vs)
     st.q_offsets, st.kv_lens = t(w.q_offsets.astype(np.int32)), t(w.kv_lens.astype(np.int32))
     st.pos = None if w.position_ids is None else t(w.position_ids.astype(np.int32))
+    if w.mrope_sections is not None:
+        st.pos = t(synth.mrope_positions(w))
     st.freqs = t(synth.freqs_table(w))
     st.q_out = torch.empty_like(st.q)
     st.out = torch.empty_like(st.q)
@@ -187,7 +193,7 @@ def measure(st, steps, warmup, flush, split=None):
 
     def step():
         nk.rope_qk_write_paged(st.q, st.k, st.v, st.q_offsets, st.kv_lens, st.freqs, st.cache, w.rotary_dim,
-                               w.rope_layout, position_ids=st.pos, q_out=st.q_out)
+                               w.rope_layout, position_ids=st.pos, q_out=st.q_out, mrope_sections=w.mrope_sections)
         nk.ragged_paged_attention(st.q_out, st.q_offsets, st.kv_lens, st.cache, w.softmax_scale, w.max_q_len,
                                   w.max_kv_len, w.window_left, out=st.out, lse=st.lse, kv_split_tokens=split_req,
                                   workspace=ws, window_right=w.window_right)

@@ -22,9 +22,11 @@ Recipe (per workload, seed = workload number - 1):
 * float8 prior rows: one scale per (token, kv head), float32 absmax / 448, and
   torch's e4m3fn cast of x / scale.
 
-See ``synth.configs`` for the five workloads.
+See ``synth.configs`` for the five workloads and the variants of the
+prefill batch that exercise the band of keys and the RoPE layouts (M-RoPE
+position streams: ``mrope_positions``).
 """
 
 from .configs import (Workload, make, names, new_tokens, freqs_table, custom,  # noqa: F401
-                      prior_rows, build_cache, sentinel_cache)
+                      prior_rows, build_cache, sentinel_cache, mrope_positions)
 from . import work  # noqa: F401

@@ -28,7 +28,7 @@ import torch
 NAMES = ("tiny_prefill_f32", "decode_bf16", "prefill_bf16", "mixed_window_bf16", "decode_fp8")
 # beyond the five: the prefill batch under a band unbounded on both sides
 # (every row sees its whole segment), for the band entry point
-EXTRA = ("prefill_bidir_bf16",)
+EXTRA = ("prefill_bidir_bf16", "prefill_mrope_bf16", "prefill_prope_bf16")
 
 
 def names():
@@ -61,6 +61,7 @@ class Workload:
     token_ids: np.ndarray = field(default=None)  # original token ids
     full_total_q: int = 0       # tokens of the original batch (RNG identity)
     window_right: int = 0       # keys after a row's position it sees: 0 causal, -1 unbounded
+    mrope_sections: tuple = None  # M-RoPE: rotated pairs per section (position streams from mrope_positions)
 
     @property
     def num_seqs(self):
@@ -140,7 +141,12 @@ def make(which):
     """Workload by number (1..5) or name."""
     if which in EXTRA:
         w = replace(make("prefill_bf16"), name=which)
-        w.window_right = -1
+        if which == "prefill_bidir_bf16":
+            w.window_right = -1
+        elif which == "prefill_mrope_bf16":            # three position streams over 16/24/24 pairs
+            w.mrope_sections = (16, 24, 24)
+        else:                                          # p-RoPE, a quarter of the pairs rotated
+            w.rope_layout, w.rotary_dim = "half_proportional", w.head_dim // 4
         return w
     k = NAMES.index(which) + 1 if isinstance(which, str) else int(which)
     seed = k - 1
@@ -238,6 +244,15 @@ def new_tokens(w):
         q, k = _rms_normalize(q), _rms_normalize(k)
     return {"q": _to_storage(q, w.in_dtype), "k": _to_storage(k, w.in_dtype),
             "v": _to_storage(v, w.in_dtype)}
+
+
+def mrope_positions(w):
+    """M-RoPE position streams [3, T] int32 in the manner of vision-language
+    models: temporal = the token's position, then height and width walking
+    a 4-wide grid (all below the token's position + 1, so inside the
+    table)."""
+    p = w.positions.astype(np.int64)
+    return np.stack([p, p // 4, p % 4 + p // 16]).astype(np.int32)
 
 
 def freqs_table(w, max_pos=None):

@@ -77,7 +77,8 @@ def rope_bytes(w):
     if w.cache_dtype == "e4m3":
         b += T * w.num_kv_heads * 2 * 4
     b += T * (w.rotary_dim // 2) * 8                               # table rows
-    b += T * 4 * (2 if w.explicit_positions else 1)                 # page-table entry (+ position id)
+    streams = len(w.mrope_sections) if w.mrope_sections is not None else (1 if w.explicit_positions else 0)
+    b += T * 4 * (1 + streams)                                     # page-table entry + position ids
     return int(b)
 
 
