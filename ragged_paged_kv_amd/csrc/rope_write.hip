@@ -26,6 +26,8 @@
 // whole runs from LDS where a run's 4 slots are all new, single elements
 // where a segment's new slots start or end inside one (append_v_quads).
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -242,8 +244,10 @@ NK_DEVICE void append_v_quads(const RopeArgs &a, int t0, int ntok, int head, uin
   }
 }
 
-// LAYOUT: NK_ROPE_HALF, NK_ROPE_INTERLEAVED or NK_ROPE_HALF_PROPORTIONAL
-template <typename TIn, int CACHE, int LAYOUT>
+// LAYOUT: NK_ROPE_HALF, NK_ROPE_INTERLEAVED or NK_ROPE_HALF_PROPORTIONAL;
+// MROPE: position streams per section of pairs (a separate instantiation,
+// so the one-stream kernel carries none of its lookup)
+template <typename TIn, int CACHE, int LAYOUT, bool MROPE>
 __global__ void __launch_bounds__(1024) rope_write_kernel(RopeArgs a, int units_per_token, int blocks_per_token,
                                                           int v_blocks, int v_group) {
   extern __shared__ __attribute__((aligned(16))) uint8_t v_stage[];
@@ -309,7 +313,7 @@ __global__ void __launch_bounds__(1024) rope_write_kernel(RopeArgs a, int units_
     // out-of-range positions (a precondition violation) are clamped so that
     // the table read stays inside the table
     int p = slot;
-    if (a.mrope_sections > 0) {
+    if (MROPE) {
       // the unit's 8 pairs (8j..8j+7) lie in one section (sections are
       // multiples of 8 pairs); that section's position stream
       int sec = 0;
@@ -397,9 +401,13 @@ hipError_t launch_layout(const RopeArgs &a, hipStream_t stream) {
   if (qk_blocks + v_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const unsigned grid = (unsigned)(qk_blocks + v_blocks);
   const size_t lds = (size_t)(block / 64) * 4 * D * esz;
-  auto k = a.layout == NK_ROPE_INTERLEAVED ? rope_write_kernel<TIn, CACHE, NK_ROPE_INTERLEAVED>
-           : a.layout == NK_ROPE_HALF_PROPORTIONAL ? rope_write_kernel<TIn, CACHE, NK_ROPE_HALF_PROPORTIONAL>
-                                                  : rope_write_kernel<TIn, CACHE, NK_ROPE_HALF>;
+  auto pick = [&](auto mrope) {
+    constexpr bool M = decltype(mrope)::value;
+    return a.layout == NK_ROPE_INTERLEAVED ? rope_write_kernel<TIn, CACHE, NK_ROPE_INTERLEAVED, M>
+           : a.layout == NK_ROPE_HALF_PROPORTIONAL ? rope_write_kernel<TIn, CACHE, NK_ROPE_HALF_PROPORTIONAL, M>
+                                                  : rope_write_kernel<TIn, CACHE, NK_ROPE_HALF, M>;
+  };
+  auto k = a.mrope_sections > 0 ? pick(std::true_type{}) : pick(std::false_type{});
   return launch(k, dim3(grid), dim3(block), lds, stream, a, upt, bpt, (int)v_blocks, v_group);
 }
 
