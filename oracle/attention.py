@@ -16,6 +16,9 @@ Definitions followed:
   replaces 1/sqrt(d), as the aria_kernel ``attention_with_scale`` entry
   allows), the causal mask admits key position <= query position, and the
   softmax subtracts the row maximum before exponentiating.
+* Algenta, "Ten named techniques, one scalar formula each",
+  ``streaming_llm_sink_score``: StreamingLLM keeps the first few ("sink")
+  keys visible besides a sliding window of recent keys.
 * Algenta, "Flash attention's running state ...":
   ``grouped_query_attention_scale(32, 8) = 4`` -- each KV head serves
   Hq / Hkv query heads.
@@ -23,8 +26,11 @@ Definitions followed:
 Readings taken where the pages leave a step open: query head h reads KV head
 floor(h / G) with G = Hq / Hkv; ``window_left`` = keys_before and
 ``window_right`` = keys_after, -1 standing for the pages' None (unbounded),
-window_right 0 (the default) being causal; the log-sum-exp is the natural
-log of sum_j exp(scale * q.k_j); an empty row has lse = -inf.
+window_right 0 (the default) being causal; ``sink_keys`` = n keys from the
+segment's first that every row sees in addition to its band, up to the
+band's right edge (sinks widen the left side only; 0 = none);
+the log-sum-exp is the natural log of sum_j exp(scale * q.k_j); an empty
+row has lse = -inf.
 
 This is the plain definition: full score rows, one max, one exponent, one
 sum, one division -- no tiling, no online softmax, no split.
@@ -44,7 +50,18 @@ def visible_range(row, q_len, kv_len, window_left, window_right=0):
     return lo, hi
 
 
-def attend_rows(q_rows, K, V, row_ids, q_len, kv_len, softmax_scale, window_left, window_right=0):
+def visible_keys(row, q_len, kv_len, window_left, window_right=0, sink_keys=0):
+    """Sorted indices of the keys visible to query row ``row``: its band
+    [lo, hi] and, up to hi, the first ``sink_keys`` keys of the segment."""
+    lo, hi = visible_range(row, q_len, kv_len, window_left, window_right)
+    band = np.arange(lo, hi + 1) if lo <= hi else np.zeros(0, dtype=np.int64)
+    if sink_keys <= 0:
+        return band
+    return np.union1d(np.arange(max(0, min(sink_keys, hi + 1))), band).astype(np.int64)
+
+
+def attend_rows(q_rows, K, V, row_ids, q_len, kv_len, softmax_scale, window_left, window_right=0,
+                sink_keys=0):
     """Attention for selected query rows of one segment and one KV head.
 
     q_rows [n, D] float64, K/V [kv_len, D] float64, row_ids [n] local rows.
@@ -55,20 +72,20 @@ def attend_rows(q_rows, K, V, row_ids, q_len, kv_len, softmax_scale, window_left
     lse = np.full(n, -np.inf)
     scores = softmax_scale * (q_rows @ K.T)     # [n, kv_len]
     for r in range(n):
-        lo, hi = visible_range(int(row_ids[r]), q_len, kv_len, window_left, window_right)
-        if lo > hi:
+        idx = visible_keys(int(row_ids[r]), q_len, kv_len, window_left, window_right, sink_keys)
+        if idx.size == 0:
             continue
-        s = scores[r, lo:hi + 1]
+        s = scores[r, idx]
         m = np.max(s)
         e = np.exp(s - m)
         l = np.sum(e)
-        out[r] = (e @ V[lo:hi + 1]) / l
+        out[r] = (e @ V[idx]) / l
         lse[r] = m + np.log(l)
     return out, lse
 
 
 def ragged_paged_attention(q, q_offsets, kv_lens, cache, page_table, softmax_scale,
-                           window_left=-1, rows=None, window_right=0):
+                           window_left=-1, rows=None, window_right=0, sink_keys=0):
     """Attention of every (or the selected) query row of a ragged batch.
 
     q [T, Hq, D]: float64 values of the stored queries.  ``cache`` is an
@@ -101,13 +118,13 @@ def ragged_paged_attention(q, q_offsets, kv_lens, cache, page_table, softmax_sca
         for h in range(hq):
             g = h // group
             o, l = attend_rows(q[a + local, h, :], K[:, g, :], V[:, g, :], local,
-                               q_len, kv_len, softmax_scale, window_left, window_right)
+                               q_len, kv_len, softmax_scale, window_left, window_right, sink_keys)
             out[a + local, h, :] = o
             lse[a + local, h] = l
     return out, lse
 
 
-def dense_attention(q, k, v, softmax_scale, window_left=-1, window_right=0):
+def dense_attention(q, k, v, softmax_scale, window_left=-1, window_right=0, sink_keys=0):
     """Single-segment attention on contiguous arrays (no pages).
 
     q [n_q, Hq, D], k/v [n_kv, Hkv, D] float64; end-aligned band (causal by
@@ -122,7 +139,7 @@ def dense_attention(q, k, v, softmax_scale, window_left=-1, window_right=0):
     for h in range(hq):
         g = h // group
         o, l = attend_rows(q[:, h, :], k[:, g, :], v[:, g, :], np.arange(n_q),
-                           n_q, n_kv, softmax_scale, window_left, window_right)
+                           n_q, n_kv, softmax_scale, window_left, window_right, sink_keys)
         out[:, h, :] = o
         lse[:, h] = l
     return out, lse

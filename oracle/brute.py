@@ -41,7 +41,8 @@ def attention_row(q, keys, values, scale):
     return out, m + math.log(l)
 
 
-def ragged_attention(q, q_offsets, kv_lens, keys, values, scale, window_left=-1, window_right=0):
+def ragged_attention(q, q_offsets, kv_lens, keys, values, scale, window_left=-1, window_right=0,
+                     sink_keys=0):
     """q: list over tokens of list over heads of vectors; keys/values: list
     over sequences of list over slots of list over kv heads of vectors.
     Returns (out, lse) nested lists [T][Hq][D], [T][Hq]."""
@@ -56,11 +57,12 @@ def ragged_attention(q, q_offsets, kv_lens, keys, values, scale, window_left=-1,
             p = r + kv_len - q_len
             lo = 0 if window_left < 0 else max(0, p - window_left)
             hi = kv_len - 1 if window_right < 0 else min(p + window_right, kv_len - 1)
+            seen = [j for j in range(kv_len) if j <= hi and (j < sink_keys or j >= lo)]
             row_out, row_lse = [], []
             for h in range(hq):
                 g = h // group
-                ks = [keys[s][j][g] for j in range(lo, hi + 1)]
-                vs = [values[s][j][g] for j in range(lo, hi + 1)]
+                ks = [keys[s][j][g] for j in seen]
+                vs = [values[s][j][g] for j in seen]
                 o, l = attention_row(q[a + r][h], ks, vs, scale)
                 row_out.append(o)
                 row_lse.append(l)

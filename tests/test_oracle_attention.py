@@ -188,6 +188,26 @@ def test_p9_matches_torch_sdpa(n_q, n_kv, window, after):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("n_q,n_kv,window,after,sinks", [(6, 30, 4, 0, 3), (1, 40, 9, 0, 4), (9, 9, 1, 2, 2)])
+def test_p9b_sinks_match_torch_sdpa(n_q, n_kv, window, after, sinks):
+    """Sink keys (Algenta streaming_llm_sink_score) as an explicit mask:
+    key j is seen when j <= position + keys_after and (j >= position -
+    keys_before or j < sinks)."""
+    rng = np.random.default_rng(19)
+    hq, hkv, d = 2, 1, 8
+    q = rng.standard_normal((n_q, hq, d)); k = rng.standard_normal((n_kv, hkv, d)); v = rng.standard_normal((n_kv, hkv, d))
+    out, lse = attention.dense_attention(q, k, v, 0.5, window, after, sinks)
+    i = np.arange(n_q)[:, None] + n_kv - n_q
+    j = np.arange(n_kv)[None, :]
+    mask = (j <= i + after) & ((j >= i - window) | (j < sinks))
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(np.repeat(k, hq, axis=1)).permute(1, 0, 2).contiguous()
+    tv = torch.from_numpy(np.repeat(v, hq, axis=1)).permute(1, 0, 2).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.from_numpy(mask), scale=0.5).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-13)
+
+
 def test_p10_window_band(golden):
     g = golden("numkong_band_example.json")
     rng = np.random.default_rng(10)
@@ -256,6 +276,50 @@ def test_p10b_band_after_the_row(golden):
         o1, l1 = attention.dense_attention(q1, k9, v9, 0.5, 4, after)
         np.testing.assert_array_equal(o0, o1)
         np.testing.assert_array_equal(l0, l1)
+
+
+def test_p10c_streaming_sinks(golden):
+    """Algenta streaming_llm_sink_score: 4 sink tokens plus a 20-token
+    window over 100 positions attend positions 0-3 and 80-99 from the last
+    position; here window_left = window - 1 and sink_keys = n_sink.  Also:
+    brute force, sinks 0 = the band, sinks reaching the band = one range."""
+    g = golden("algenta_streaming_sink.json")
+    n = g["seq_len"]
+    idx = attention.visible_keys(0, 1, n, g["window_size"] - 1, 0, g["n_sink_tokens"])   # one row, at position n - 1
+    seen = np.zeros(n); seen[idx] = 1.0
+    assert [seen[p] for p in g["positions"]] == g["scores"]
+    assert list(idx) == list(range(4)) + list(range(80, 100))
+    # the attention over that set is the plain softmax over exactly those keys
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((1, 1, 8)); k = rng.standard_normal((n, 1, 8)); v = rng.standard_normal((n, 1, 8))
+    out, lse = attention.dense_attention(q, k, v, 0.4, g["window_size"] - 1, 0, g["n_sink_tokens"])
+    sc = 0.4 * (k[idx, 0] @ q[0, 0])
+    w = np.exp(sc - sc.max())
+    np.testing.assert_allclose(out[0, 0], (w / w.sum()) @ v[idx, 0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], sc.max() + np.log(w.sum()), rtol=0, atol=1e-14)
+    # brute force on the two-segment example, several bands with sinks
+    gb = golden("numkong_band_example.json")
+    lens, offs = gb["lengths"], gb["offsets"]
+    T = offs[-1]
+    q = rng.standard_normal((T, 2, 8)); k = rng.standard_normal((T, 2, 8)); v = rng.standard_normal((T, 2, 8))
+    cache, pt = _pack_contiguous(k, v, offs, 16)
+    ks = [k[offs[s]:offs[s + 1]].tolist() for s in range(2)]
+    vs = [v[offs[s]:offs[s + 1]].tolist() for s in range(2)]
+    for before, after, sinks in ((2, 0, 2), (1, 1, 3), (0, 0, 1), (3, -1, 2), (-1, 0, 4)):
+        out, lse = attention.ragged_paged_attention(q, offs, lens, cache, pt, 0.3, before, window_right=after,
+                                                    sink_keys=sinks)
+        bo, bl = brute.ragged_attention(q.tolist(), offs, lens, ks, vs, 0.3, before, after, sinks)
+        np.testing.assert_allclose(out, np.array(bo), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, np.array(bl), rtol=0, atol=1e-13)
+    o_b, l_b = attention.ragged_paged_attention(q, offs, lens, cache, pt, 0.3, 2)
+    o_0, l_0 = attention.ragged_paged_attention(q, offs, lens, cache, pt, 0.3, 2, sink_keys=0)
+    np.testing.assert_array_equal(o_b, o_0)
+    # sinks covering every key before any band: the causal rows from key 0
+    # (sinks widen the band's left side only; keys after a row stay hidden)
+    o_c, l_c = attention.ragged_paged_attention(q, offs, lens, cache, pt, 0.3, -1)
+    o_s, l_s = attention.ragged_paged_attention(q, offs, lens, cache, pt, 0.3, 1, sink_keys=max(lens))
+    np.testing.assert_array_equal(o_c, o_s)
+    np.testing.assert_array_equal(l_c, l_s)
 
 
 def test_rows_with_no_key_are_zero():
