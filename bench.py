@@ -196,7 +196,8 @@ def measure(st, steps, warmup, flush, split=None):
                                w.rope_layout, position_ids=st.pos, q_out=st.q_out, mrope_sections=w.mrope_sections)
         nk.ragged_paged_attention(st.q_out, st.q_offsets, st.kv_lens, st.cache, w.softmax_scale, w.max_q_len,
                                   w.max_kv_len, w.window_left, out=st.out, lse=st.lse, kv_split_tokens=split_req,
-                                  workspace=ws, window_right=w.window_right)
+                                  workspace=ws, window_right=w.window_right,
+                                  sink_keys=w.sink_keys)
 
     scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
     sink = torch.empty((), dtype=torch.float32, device="cuda")

@@ -230,13 +230,23 @@ int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_o
  * window_right = 0 is causal (nk_ragged_paged_attention is this call with
  * window_right 0); window_right < -1 returns NK_ERR_INVALID_ARG.  A
  * single-token row sits at its segment's last key, so window_right does not
- * change it.  Every other argument, the workspace and the errors are those
- * of nk_ragged_paged_attention.
+ * change it.
+ *
+ * sink_keys: Algenta "Ten named techniques, one scalar formula each",
+ * streaming_llm_sink_score -- StreamingLLM attention keeps a segment's first
+ * keys visible beside the window.  Here the row also sees keys
+ * 0 .. sink_keys-1 that are not right of hi (they widen the band's left side
+ * only); 0 = none; ignored when window_left = -1 (those keys are already in
+ * the band); negative returns NK_ERR_INVALID_ARG.  Decode rows take the sink
+ * keys as one extra split-KV chunk, which the workspace of every windowed
+ * call reserves (nk_ragged_paged_attention_workspace_size covers it).
+ * Every other argument, the workspace and the errors are those of
+ * nk_ragged_paged_attention.
  */
 int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t *q_offsets,
                                    const int32_t *kv_lens, const nk_paged_kv_t *cache,
                                    float softmax_scale, int32_t window_left, int32_t window_right,
-                                   void *out, float *lse, int32_t num_seqs, int32_t total_q,
+                                   int32_t sink_keys, void *out, float *lse, int32_t num_seqs, int32_t total_q,
                                    int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
                                    int32_t kv_split_tokens, void *workspace,
                                    size_t workspace_bytes, void *stream);

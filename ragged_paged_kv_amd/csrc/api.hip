@@ -60,11 +60,20 @@ int max_chunks(int max_kv_len, int window_left, int split) {
 
 bool uses_split(int q_dtype, int cache_dtype) { return q_dtype == NK_BF16 && cache_dtype != NK_F32; }
 
+// A windowed call may also attend to sink keys left of its band: those take
+// one more split-KV chunk per decode row, which the workspace always reserves
+// for windowed calls (the size query does not see the sink count).
+bool sink_chunk_possible(int max_kv_len, int window_left) {
+  return window_left >= 0 && (long long)max_kv_len > (long long)window_left + 1;
+}
+
 // Workspace: the split-KV partials of decode rows (when a row spans several
 // chunks), then the prefill work list (when any row block may be a prefill
 // one), each 256-byte aligned.
 struct WorkspacePlan {
-  int split = 0, chunks = 1;
+  int split = 0;
+  int band_chunks = 1;      // chunks of a row's band
+  int chunks = 1;           // capacity per row: band chunks + a sink chunk when possible
   size_t part_lse = 0, sched = 0, total = 0;
   bool partials = false, prefill = false;
 };
@@ -74,7 +83,8 @@ WorkspacePlan plan_workspace(int q_dtype, int cache_dtype, int num_seqs, int tot
                              int requested_split) {
   WorkspacePlan w;
   w.split = split_tokens(num_seqs, max_kv_len, hq, hkv, head_dim, window_left, requested_split);
-  w.chunks = max_chunks(max_kv_len, window_left, w.split);
+  w.band_chunks = max_chunks(max_kv_len, window_left, w.split);
+  w.chunks = w.band_chunks + (sink_chunk_possible(max_kv_len, window_left) ? 1 : 0);
   if (!uses_split(q_dtype, cache_dtype)) return w;
   size_t off = 0;
   if (w.chunks > 1) {
@@ -285,20 +295,20 @@ int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_o
                               int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens,
                               void *workspace, size_t workspace_bytes_given, void *stream) {
   return nk_ragged_paged_attention_band(q, q_dtype, q_offsets, kv_lens, cache, softmax_scale, window_left, 0,
-                                        out, lse, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads,
+                                        0, out, lse, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads,
                                         kv_split_tokens, workspace, workspace_bytes_given, stream);
 }
 
 int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t *q_offsets,
                                    const int32_t *kv_lens, const nk_paged_kv_t *cache,
                                    float softmax_scale, int32_t window_left, int32_t window_right,
-                                   void *out, float *lse, int32_t num_seqs, int32_t total_q,
+                                   int32_t sink_keys, void *out, float *lse, int32_t num_seqs, int32_t total_q,
                                    int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
                                    int32_t kv_split_tokens, void *workspace,
                                    size_t workspace_bytes_given, void *stream) {
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0 || num_q_heads <= 0)
     return NK_ERR_INVALID_ARG;
-  if (window_left < -1 || window_right < -1) return NK_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1 || sink_keys < 0) return NK_ERR_INVALID_ARG;
   if (kv_split_tokens < 0 || kv_split_tokens % 32) return NK_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return NK_ERR_INVALID_ARG;
   int st = check_cache(cache);
@@ -316,6 +326,7 @@ int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t
   a.q = q; a.q_dtype = q_dtype; a.q_offsets = q_offsets; a.kv_lens = kv_lens;
   a.cache = *cache; a.softmax_scale = softmax_scale;
   a.window_left = window_left; a.window_right = window_right;
+  a.sink_keys = window_left < 0 ? 0 : sink_keys;     // a full left side already holds them
   a.out = out; a.lse = lse;
   a.num_seqs = num_seqs; a.total_q = total_q; a.max_q_len = max_q_len; a.max_kv_len = max_kv_len;
   a.hq = num_q_heads;
@@ -328,7 +339,8 @@ int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t
                                          cache->head_dim, window_left, kv_split_tokens);
   if (wp.total > 0 && (!workspace || workspace_bytes_given < wp.total)) return NK_ERR_WORKSPACE;
   a.split_tokens = wp.split;
-  a.max_chunks = wp.chunks;
+  // grid and partials stride: the sink chunk only when there are sink keys
+  a.max_chunks = a.sink_keys > 0 ? wp.chunks : wp.band_chunks;
   if (wp.partials) {
     a.part_out = (float *)workspace;
     a.part_lse = (float *)((char *)workspace + wp.part_lse);

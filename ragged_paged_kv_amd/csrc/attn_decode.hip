@@ -3,8 +3,11 @@
 //
 // What it computes: NumKong matrix-kernels page, attention_packed, for a
 // segment with one query row (it sits at position kv_len - 1 and sees every
-// key, or the last window_left + 1 keys); aria_kernel `attention` (single
-// query step against the KV cache, GQA layout).  The keys are cut into
+// key, or the last window_left + 1 keys, plus the first sink_keys keys beside a
+// window: Algenta, "Ten named techniques, one scalar formula each",
+// StreamingLLM sinks); aria_kernel `attention` (single
+// query step against the KV cache, GQA layout).  The sink keys left of the
+// window form one chunk of their own.  The keys are cut into
 // chunks whose states are merged by log-sum-exp as on the Algenta page's
 // flash-attention walkthrough (running max, rescale by exp(old - new)).
 // e4m3 caches: a stored code times its per-(token, head) scale is the value;
@@ -220,15 +223,16 @@ attn_decode_kernel(AttnArgs a) {
   if (a.q_offsets[s + 1] - q0 != 1) return;
   const int L = a.kv_lens[s];
   const int hi = L - 1;
-  const int lo = a.window_left < 0 ? 0 : max(0, hi - a.window_left);
-  const int c0 = (lo / 32) * 32;              // chunks are aligned to 32 keys
-  // (clamped to the grid: a kv_len above max_kv_len violates the
-  // precondition, and its row then covers only the first max_chunks chunks)
-  const int n_chunks = L > 0 ? min((hi + 1 - c0 + a.split_tokens - 1) / a.split_tokens, a.max_chunks) : 1;
+  // band chunks from c0 (32-key aligned), then the chunk of the sink keys
+  // before the band, if any (clamped to the grid: a kv_len above max_kv_len
+  // violates the precondition, and its row covers only max_chunks chunks)
+  const DecodeChunks dc = decode_chunks(L, a.window_left, a.sink_keys, a.split_tokens, a.max_chunks);
+  const int n_chunks = dc.n;
   if (c >= n_chunks) return;
-  const int cs = c0 + c * a.split_tokens;
-  const int ce = min(cs + a.split_tokens, hi + 1);
-  const int vlo = max(cs, lo);                // valid keys [vlo, ce)
+  const bool sink_chunk = c >= dc.n_band;
+  const int cs = sink_chunk ? 0 : dc.c0 + c * a.split_tokens;
+  const int ce = sink_chunk ? dc.sink_end : min(cs + a.split_tokens, hi + 1);
+  const int vlo = sink_chunk ? 0 : max(cs, dc.lo);          // valid keys [vlo, ce)
   const int nsteps = L > 0 ? (ce - cs + 15) / 16 : 0;
   const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
   const LaneOffsets loff = lane_offsets<D, P, FP8>(lane);

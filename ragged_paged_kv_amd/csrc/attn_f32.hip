@@ -2,7 +2,9 @@
 //
 // What it computes: NumKong matrix-kernels page, attention_packed -- query
 // row i of a segment sits at i + kv_len - q_len and sees the causal band
-// (optionally windowed: window_left keys before it); rows with no key give
+// (optionally windowed: window_left keys before it, window_right after it,
+// and beside a window the segment's first sink_keys keys -- Algenta, "Ten
+// named techniques, one scalar formula each", StreamingLLM sinks); rows with no key give
 // zeros; the log-sum-exp is filled alongside.  Scores are
 // softmax_scale * q.k (Algenta "A scalar reference, not a buffer kernel";
 // explicit scale as in aria_kernel `attention_with_scale`).
@@ -46,12 +48,18 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
   const float *vp = (const float *)a.cache.v_pages;
   const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
 
+  // visible keys: the sink keys before the band, then the band; walked as
+  // one list, entry v being key v (v < n_sink) or lo + v - n_sink
+  const int n_sink = max(0, min(a.sink_keys, min(lo, hi + 1)));
+  const int n_keys = n_sink + max(0, hi - lo + 1);
+  auto key_of = [&](int v) { return v < n_sink ? v : lo + v - n_sink; };
   float m = -INFINITY, l = 0.f;
   float o[4] = {0.f, 0.f, 0.f, 0.f};     // dims lane, lane+64, lane+128, lane+192
-  for (int base = lo; base <= hi; base += kWave) {
-    const int key = base + lane;
+  for (int base = 0; base < n_keys; base += kWave) {
+    const bool valid = base + lane < n_keys;
+    const int key = key_of(base + lane);
     float sc = -INFINITY;
-    if (key <= hi) {
+    if (valid) {
       const int page = pt[key / P];
       // K page-head: [dim/32][slot][32]
       const float *kph = kp + ((size_t)page * hkv + g) * P * D + (key % P) * 32;
@@ -62,14 +70,14 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
     const float cm = wave_max(sc);
     const float nm = fmaxf(m, cm);
     const float corr = expf(m - nm);                 // 0 when m = -inf
-    const float pj = key <= hi ? expf(sc - nm) : 0.f;
+    const float pj = valid ? expf(sc - nm) : 0.f;
     l = l * corr + wave_sum(pj);
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] *= corr;
-    const int nk = min(kWave, hi - base + 1);
+    const int nk = min(kWave, n_keys - base);
     for (int i = 0; i < nk; ++i) {
       const float pi = __shfl(pj, i, kWave);
-      const int kk = base + i;
+      const int kk = key_of(base + i);
       const int page = pt[kk / P];
       // V page-head block in MFMA operand order (one 16-dim tile per
       // 16-byte run for float32): element (d, t) at

@@ -6,6 +6,10 @@
 // i + kv_len - q_len and sees the keys of its causal band (the last
 // window_left + 1 of them when a window is set); aria_kernel
 // `attention_causal_with_scale` (explicit scale, optional sliding window).
+// A general band (keys up to window_right past the row) and, beside a
+// window, the segment's first sink_keys keys (Algenta, "Ten named
+// techniques, one scalar formula each", StreamingLLM sinks) widen the set;
+// the sink keys' tiles are visited before the band's.
 // The softmax is accumulated online, tile by tile, as on the Algenta page's
 // flash-attention walkthrough: a running maximum, a running sum and a
 // running output, rescaled by exp(old - new) when the maximum rises.
@@ -138,6 +142,13 @@ NK_DEVICE float dot2_ones(uint32_t pk, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, acc, false);
 }
 
+// Key tiles of the sink keys left of a work item's band: the tiles that hold
+// keys 0 .. sink_keys-1 below the band's first tile tb0 (sink keys in tile
+// tb0 or later are visited with the band).
+NK_DEVICE int sink_tiles(int sink_keys, int tb0, int bn) {
+  return sink_keys > 0 ? min((sink_keys + bn - 1) / bn, tb0) : 0;
+}
+
 // One work item: BM query rows (q-block qb) of segment s for the GW query
 // heads of head block hy (KV head hy / HB).  Every thread of the work-group
 // calls it with the same arguments.
@@ -226,6 +237,14 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const size_t page_bytes = (size_t)hkv * head_bytes;
   const uint8_t *kb = (const uint8_t *)a.cache.k_pages + (size_t)g * head_bytes;
   const uint8_t *vb = (const uint8_t *)a.cache.v_pages + (size_t)g * head_bytes;
+  // tiles are visited in the order t0 .. t1 of a virtual index: first the
+  // ns sink tiles (physical tiles 0 .. ns-1), then the band's tiles, whose
+  // virtual index is their physical one
+  const int tb0 = kmin_wg / BN, t1 = kmax_wg / BN;
+  const int ns = sink_tiles(a.sink_keys, tb0, BN);
+  const int t0 = tb0 - ns;
+  auto phys = [&](int t) { return t < tb0 ? t - t0 : t; };
+
   int pit[PER];                                         // page of the tile (wave-uniform)
   uint32_t kg[PER], vg[PER], kl[PER], vl[PER], vkey[PER];
   constexpr int NV = FP8 ? 4 : 2;                        // 16-dim groups per 16-byte V run
@@ -263,7 +282,8 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   // is the same tile
   size_t pgk[PER];
   // K of `tile` into the given staging registers
-  auto load_k_to = [&](int tile, Raw (&dst)[PER], float &dss) {
+  auto load_k_to = [&](int vtile, Raw (&dst)[PER], float &dss) {
+    const int tile = phys(vtile);
 #pragma unroll
     for (int i = 0; i < PER; ++i) pgk[i] = page_of(tile, pit[i]);
     __builtin_amdgcn_sched_barrier(0);     // all page lookups in flight together
@@ -298,8 +318,8 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   auto store_k = [&](int buf) { store_k_from(buf, kst, kss); };
   // e4m3 V enters LDS as bf16(code * scale); keys >= L become zeros (their
   // slots may hold anything, and 0 * NaN is NaN)
-  auto store_v = [&](int buf, int tile) {
-    const int base = tile * BN;
+  auto store_v = [&](int buf, int vtile) {
+    const int base = phys(vtile) * BN;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       // elements 0..3: dim dim0, tokens vkey..+3; 4..7: dim dim0 + 16
@@ -335,8 +355,10 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
 #pragma unroll
   for (int j = 0; j < 16; ++j) pk[j] = 0u;
 
-  const int t0 = kmin_wg / BN, t1 = kmax_wg / BN;
-  auto active = [&](int t) { return wave_active && t * BN <= wk_hi && t * BN + BN - 1 >= wk_lo; };
+  auto active = [&](int t) {
+    const int b = phys(t) * BN;
+    return wave_active && b <= wk_hi && (b + BN - 1 >= wk_lo || b < a.sink_keys);
+  };
 
   // M(t), t >= t0: S(t+1) = K(t+1) Q^T and O^T += V(t)^T P(t)^T -- MFMA
   // work only, one straight block (past the last tile S reads a stale
@@ -387,7 +409,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
       for (int j = 0; j < 16; ++j) pk[j] = 0u;
       return;
     }
-    const int tile_base = tn * BN;
+    const int tile_base = phys(tn) * BN;
     if constexpr (FP8) {
       const float *ks = (const float *)(lds + C::KS_OFF + (tn & 1) * C::SBUF);
 #pragma unroll
@@ -404,12 +426,13 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     if (mask) {
       const int rel_hi = row_valid ? my_hi - tile_base - 8 * half : -1000000;
       const int rel_lo = my_lo - tile_base - 8 * half;
+      const int rel_sink = a.sink_keys - tile_base - 8 * half;    // keys below it are sinks
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int kv = 32 * st + 16 * (v >> 3) + (v & 7);
-          if (kv > rel_hi || kv < rel_lo) sc[st][v] = -INFINITY;
+          if (kv > rel_hi || (kv < rel_lo && kv >= rel_sink)) sc[st][v] = -INFINITY;
         }
     }
     float tmax = sc[0][0];
@@ -532,7 +555,7 @@ NK_DEVICE int item_tiles(const AttnArgs &a, int BM, int s, int qb) {
   const int r_last = min(r0 + BM, q_len) - 1;
   const int kmax = band_hi(r_last + shift, L, a.window_right);
   const int kmin = a.window_left < 0 ? 0 : max(0, r0 + shift - a.window_left);
-  return (kmax < kmin || L <= 0) ? 0 : kmax / BN - kmin / BN + 1;
+  return (kmax < kmin || L <= 0) ? 0 : kmax / BN - kmin / BN + 1 + sink_tiles(a.sink_keys, kmin / BN, BN);
 }
 
 constexpr int kPlanThreads = 1024;

@@ -79,6 +79,25 @@ NK_DEVICE int band_hi(int p, int L, int window_right) {
   return (window_right < 0 || window_right >= L) ? L - 1 : min(p + window_right, L - 1);
 }
 
+// Split-KV chunks of a single-token row with L keys (its position L - 1):
+// the band [lo, L-1] cut into chunks of `split` keys from c0 (lo rounded
+// down to 32), then, when sink keys lie before lo, one chunk of the keys
+// [0, sink_end).  At most max_chunks chunks (a key count above the batch's
+// bound violates the precondition and loses the rest).
+struct DecodeChunks {
+  int lo, c0, n_band, n, sink_end;
+};
+NK_DEVICE DecodeChunks decode_chunks(int L, int window_left, int sink_keys, int split, int max_chunks) {
+  DecodeChunks d;
+  const int hi = L - 1;
+  d.lo = window_left < 0 ? 0 : max(0, hi - window_left);
+  d.c0 = (d.lo / 32) * 32;
+  d.sink_end = min(sink_keys, d.lo);
+  d.n_band = L > 0 ? min((hi + 1 - d.c0 + split - 1) / split, max_chunks) : 1;
+  d.n = min(d.n_band + (L > 0 && d.sink_end > 0 ? 1 : 0), max_chunks);
+  return d;
+}
+
 // Index of the first segment s with q_offsets[s+1] > t (binary search).
 NK_DEVICE int find_segment(const int32_t *__restrict__ q_offsets, int num_seqs, int t) {
   int lo = 0, hi = num_seqs - 1;

@@ -36,6 +36,7 @@ struct AttnArgs {
   float softmax_scale;
   int32_t window_left;      // keys before a row's position it sees (-1: all)
   int32_t window_right;     // keys after it (0: causal; -1: all)
+  int32_t sink_keys;        // first keys of a segment every row also sees, up to its band's right edge
   void *out;
   float *lse;
   int32_t num_seqs, total_q, max_q_len, max_kv_len, hq;

@@ -154,10 +154,7 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(AttnArgs a) {
     const int L = a.kv_lens[s];
     RowTarget<TOut> t{-1, nullptr, nullptr};
     if (q1 - q0 != 1 || L <= 0) return t;
-    const int hi = L - 1;
-    const int lo = a.window_left < 0 ? 0 : max(0, hi - a.window_left);
-    const int c0 = (lo / 32) * 32;            // the decode kernel's chunk origin
-    const int n = min((hi + 1 - c0 + a.split_tokens - 1) / a.split_tokens, a.max_chunks);
+    const int n = decode_chunks(L, a.window_left, a.sink_keys, a.split_tokens, a.max_chunks).n;   // the decode kernel's
     if (n <= 1) return t;
     t.n = n;
     t.out_row = (TOut *)a.out + ((size_t)q0 * a.hq + h) * a.cache.head_dim;

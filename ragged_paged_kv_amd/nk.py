@@ -61,7 +61,7 @@ def lib():
         L.nk_ragged_paged_attention.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, vp, vp, i32,
                                                 i32, i32, i32, i32, i32, vp, sz, vp]
         L.nk_ragged_paged_attention.restype = ctypes.c_int
-        L.nk_ragged_paged_attention_band.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, i32, vp, vp, i32,
+        L.nk_ragged_paged_attention_band.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, i32, i32, vp, vp, i32,
                                                      i32, i32, i32, i32, i32, vp, sz, vp]
         L.nk_ragged_paged_attention_band.restype = ctypes.c_int
         L.nk_ragged_paged_attention_workspace_size.argtypes = [i32] * 11
@@ -223,10 +223,11 @@ def split_tokens(cache, num_seqs, max_kv_len, num_q_heads, window_left=-1, kv_sp
 
 def ragged_paged_attention(q, q_offsets, kv_lens, cache, softmax_scale, max_q_len, max_kv_len,
                            window_left=-1, out=None, lse=None, kv_split_tokens=0, workspace=None,
-                           stream=None, window_right=0):
+                           stream=None, window_right=0, sink_keys=0):
     """GQA attention of q [T, Hq, D] over the cache under the band
     [position - window_left, position + window_right] (-1 = unbounded side;
-    window_right 0, the default, is causal); returns (out, lse).  ``lse`` is
+    window_right 0, the default, is causal), plus the segment's first
+    ``sink_keys`` keys up to the band's right edge; returns (out, lse).  ``lse`` is
     filled when given (float32 [T, Hq]); ``workspace`` is allocated here when
     not given."""
     T, hq, d = q.shape
@@ -246,7 +247,7 @@ def ragged_paged_attention(q, q_offsets, kv_lens, cache, softmax_scale, max_q_le
     c = cache.struct()
     st = lib().nk_ragged_paged_attention_band(_ptr(q), _dtype_code(q.dtype), _ptr(q_offsets), _ptr(kv_lens),
                                               ctypes.byref(c), float(softmax_scale), int(window_left),
-                                              int(window_right), _ptr(out), _ptr(lse), B, T, int(max_q_len),
+                                              int(window_right), int(sink_keys), _ptr(out), _ptr(lse), B, T, int(max_q_len),
                                               int(max_kv_len), hq, int(kv_split_tokens), _ptr(workspace),
                                               ws_bytes, _stream(stream))
     _check(st, "nk_ragged_paged_attention_band")

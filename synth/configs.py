@@ -61,6 +61,7 @@ class Workload:
     token_ids: np.ndarray = field(default=None)  # original token ids
     full_total_q: int = 0       # tokens of the original batch (RNG identity)
     window_right: int = 0       # keys after a row's position it sees: 0 causal, -1 unbounded
+    sink_keys: int = 0          # beside a window: the segment's first keys every row also sees
     mrope_sections: tuple = None  # M-RoPE: rotated pairs per section (position streams from mrope_positions)
 
     @property
@@ -358,7 +359,8 @@ def build_cache(w, threads=8):
 def custom(q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, *, rotary_dim=None,
            rope_layout="half", rope_theta=1e4, page_size=16, in_dtype="bf16", cache_dtype="bf16",
            softmax_scale=None, window_left=-1, qk_norm=False, explicit_positions=True,
-           page_order="permuted", seed=1000, split_tokens=0, name="custom", window_right=0):
+           page_order="permuted", seed=1000, split_tokens=0, name="custom", window_right=0,
+           sink_keys=0):
     """A workload of given shapes (for tests); pages drawn from
     ``default_rng(seed)``, values from the same per-token/per-sequence streams
     as the named workloads."""
@@ -374,4 +376,5 @@ def custom(q_lens, kv_lens, num_q_heads, num_kv_heads, head_dim, *, rotary_dim=N
     w.token_ids = np.arange(w.total_q)
     w.full_total_q = w.total_q
     w.window_right = window_right
+    w.sink_keys = sink_keys
     return w

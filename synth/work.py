@@ -27,7 +27,8 @@ def visible_keys(w):
         p = np.arange(ql) + L - ql
         hi = np.full_like(p, L - 1) if w.window_right < 0 else np.minimum(p + w.window_right, L - 1)
         lo = np.zeros_like(p) if w.window_left < 0 else np.maximum(0, p - w.window_left)
-        out[offs[s]:offs[s] + ql] = np.maximum(hi - lo + 1, 0)
+        sinks = np.maximum(0, np.minimum(np.minimum(lo, hi + 1), w.sink_keys if w.window_left >= 0 else 0))
+        out[offs[s]:offs[s] + ql] = np.maximum(hi - lo + 1, 0) + sinks
     return out
 
 

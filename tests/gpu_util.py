@@ -71,7 +71,7 @@ def run_hip(w, d, split=None, out_lse=True):
     lse = torch.empty(w.total_q, w.num_q_heads, dtype=torch.float32, device=q_out.device) if out_lse else None
     out, lse = nk.ragged_paged_attention(q_out, d["q_offsets"], d["kv_lens"], d["cache"], w.softmax_scale,
                                          w.max_q_len, w.max_kv_len, w.window_left, lse=lse,
-                                         window_right=w.window_right,
+                                         window_right=w.window_right, sink_keys=w.sink_keys,
                                          kv_split_tokens=w.split_tokens if split is None else split)
     return q_out, out, lse
 
@@ -97,7 +97,8 @@ def oracle_run(w, raw_cache=None):
                                                synth.freqs_table(w), w.rotary_dim, w.rope_layout, cache,
                                                w.page_table)
     out, lse = o_attn.ragged_paged_attention(q_out, w.q_offsets, w.kv_lens, cache2, w.page_table,
-                                             w.softmax_scale, w.window_left, window_right=w.window_right)
+                                             w.softmax_scale, w.window_left, window_right=w.window_right,
+                                             sink_keys=w.sink_keys)
     return q_out, cache2, out, lse
 
 

@@ -104,11 +104,11 @@ def test_attention_validation(L):
 
 def attn_band(L, cache, window_right, **kw):
     a = dict(q=1, q_dtype=nk.NK_BF16, q_offsets=1, kv_lens=1, scale=0.1, window=-1, out=1, lse=None, num_seqs=1,
-             total=4, max_q=4, max_kv=64, hq=4, split=0, ws=None, ws_bytes=0)
+             total=4, max_q=4, max_kv=64, hq=4, split=0, ws=None, ws_bytes=0, sinks=0)
     a.update(kw)
     return L.nk_ragged_paged_attention_band(a["q"], a["q_dtype"], a["q_offsets"], a["kv_lens"],
                                             None if cache is None else ctypes.byref(cache), a["scale"], a["window"],
-                                            window_right, a["out"], a["lse"], a["num_seqs"], a["total"], a["max_q"],
+                                            window_right, a["sinks"], a["out"], a["lse"], a["num_seqs"], a["total"], a["max_q"],
                                             a["max_kv"], a["hq"], a["split"], a["ws"], a["ws_bytes"], None)
 
 
@@ -119,6 +119,8 @@ def test_band_validation(L):
     assert attn_band(L, None, 0) == nk.NK_ERR_INVALID_ARG
     assert attn_band(L, c, 5, q_dtype=nk.NK_F32) == nk.NK_ERR_UNSUPPORTED
     assert attn_band(L, c, -1, total=0) == nk.NK_OK                   # empty batch: nothing launched
+    assert attn_band(L, c, 0, window=8, sinks=-1) == nk.NK_ERR_INVALID_ARG
+    assert attn_band(L, c, 0, window=8, sinks=4, total=0) == nk.NK_OK
 
 
 def test_workspace_and_split_queries(L):
@@ -136,6 +138,10 @@ def test_workspace_and_split_queries(L):
     ws_full = L.nk_ragged_paged_attention_workspace_size(nk.NK_BF16, nk.NK_BF16, 8, 8, 1, 100000, 4, 2, 128, -1, 512)
     ws_win = L.nk_ragged_paged_attention_workspace_size(nk.NK_BF16, nk.NK_BF16, 8, 8, 1, 100000, 4, 2, 128, 1023, 512)
     assert 0 < ws_win < ws_full
+    # a window whose band fits one chunk still reserves a second chunk per
+    # decode row: the sink keys left of the window (none without a window)
+    assert L.nk_ragged_paged_attention_workspace_size(nk.NK_BF16, nk.NK_BF16, 8, 8, 1, 100000, 4, 2, 128, 100, 512) > 0
+    assert L.nk_ragged_paged_attention_workspace_size(nk.NK_BF16, nk.NK_BF16, 8, 8, 1, 100, 4, 2, 128, 99, 512) == 0
 
 
 def test_merge_validation(L):
