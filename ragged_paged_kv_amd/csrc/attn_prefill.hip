@@ -152,7 +152,7 @@ NK_DEVICE int sink_tiles(int sink_keys, int tb0, int bn) {
 // One work item: BM query rows (q-block qb) of segment s for the GW query
 // heads of head block hy (KV head hy / HB).  Every thread of the work-group
 // calls it with the same arguments.
-template <int D, int P, bool FP8, int NW>
+template <int D, int P, bool FP8, int NW, bool SINKS>
 NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, int q_len, int L, int hy,
                             uint8_t *lds) {
   using C = Cfg<D, P, FP8, NW>;
@@ -239,11 +239,12 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const uint8_t *vb = (const uint8_t *)a.cache.v_pages + (size_t)g * head_bytes;
   // tiles are visited in the order t0 .. t1 of a virtual index: first the
   // ns sink tiles (physical tiles 0 .. ns-1), then the band's tiles, whose
-  // virtual index is their physical one
+  // virtual index is their physical one (calls without sink keys run an
+  // instantiation where the index is the physical one throughout)
   const int tb0 = kmin_wg / BN, t1 = kmax_wg / BN;
-  const int ns = sink_tiles(a.sink_keys, tb0, BN);
+  const int ns = SINKS ? sink_tiles(a.sink_keys, tb0, BN) : 0;
   const int t0 = tb0 - ns;
-  auto phys = [&](int t) { return t < tb0 ? t - t0 : t; };
+  auto phys = [&](int t) { return SINKS && t < tb0 ? t - t0 : t; };
 
   int pit[PER];                                         // page of the tile (wave-uniform)
   uint32_t kg[PER], vg[PER], kl[PER], vl[PER], vkey[PER];
@@ -357,7 +358,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
 
   auto active = [&](int t) {
     const int b = phys(t) * BN;
-    return wave_active && b <= wk_hi && (b + BN - 1 >= wk_lo || b < a.sink_keys);
+    return wave_active && b <= wk_hi && (b + BN - 1 >= wk_lo || (SINKS && b < a.sink_keys));
   };
 
   // M(t), t >= t0: S(t+1) = K(t+1) Q^T and O^T += V(t)^T P(t)^T -- MFMA
@@ -432,7 +433,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int kv = 32 * st + 16 * (v >> 3) + (v & 7);
-          if (kv > rel_hi || (kv < rel_lo && kv >= rel_sink)) sc[st][v] = -INFINITY;
+          if (kv > rel_hi || (kv < rel_lo && (!SINKS || kv >= rel_sink))) sc[st][v] = -INFINITY;
         }
     }
     float tmax = sc[0][0];
@@ -666,7 +667,7 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
 // one queue share that XCD's L2); a unit is (item, head block).  An item
 // record carries its segment's row offset, row count and key count, so a
 // unit starts after one read.
-template <int D, int P, bool FP8, int NW>
+template <int D, int P, bool FP8, int NW, bool SINKS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 1 : 2)))
 attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -687,7 +688,7 @@ attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
     if (threadIdx.x == 0) next = atomicAdd(ctr, 1);   // in flight while the item runs
     const int4 rec = items[2 * (u / NHq)];      // {segment, q-block, q0, q_len}
     const int kv = items[2 * (u / NHq) + 1].x;
-    prefill_item<D, P, FP8, NW>(a, GW, rec.x, rec.y, rec.z, rec.w, kv, q + NQ * (u % NHq), lds);
+    prefill_item<D, P, FP8, NW, SINKS>(a, GW, rec.x, rec.y, rec.z, rec.w, kv, q + NQ * (u % NHq), lds);
     if (threadIdx.x == 0) unit_slot = next;
     __syncthreads();
     u = unit_slot;
@@ -700,7 +701,7 @@ DeviceShape &device_shape(int dev) {
   return shapes[dev & 63];
 }
 
-template <int D, int P, bool FP8>
+template <int D, int P, bool FP8, bool SINKS>
 hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
   constexpr int DH = D == 256 ? NK_PREFILL_D256_SPLIT : 1;
   constexpr int NW = D == 256 ? 4 * DH : NK_PREFILL_NW;
@@ -713,7 +714,7 @@ hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
   const int NH = hkv * (G / GW);
   const int NQ = NH % kSchedQueues == 0 ? kSchedQueues : 1;
   if (!a.sched) return hipErrorInvalidValue;
-  auto kern = attn_prefill_kernel<D, P, FP8, NW>;
+  auto kern = attn_prefill_kernel<D, P, FP8, NW, SINKS>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -747,8 +748,10 @@ hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
 
 template <int D, int P>
 hipError_t launch_dp(const AttnArgs &a, hipStream_t stream) {
-  if (a.cache.dtype == NK_E4M3) return launch_cfg<D, P, true>(a, stream);
-  return launch_cfg<D, P, false>(a, stream);
+  const bool sinks = a.sink_keys > 0;
+  if (a.cache.dtype == NK_E4M3)
+    return sinks ? launch_cfg<D, P, true, true>(a, stream) : launch_cfg<D, P, true, false>(a, stream);
+  return sinks ? launch_cfg<D, P, false, true>(a, stream) : launch_cfg<D, P, false, false>(a, stream);
 }
 
 }  // namespace
