@@ -53,6 +53,7 @@ DESCR = {
     "prefill_bidir_bf16": "the ragged prefill batch with every row seeing its whole segment (band unbounded on both sides)",
     "prefill_mrope_bf16": "the ragged prefill batch with M-RoPE: three position streams over 16/24/24 pairs",
     "prefill_prope_bf16": "the ragged prefill batch with p-RoPE: rotate-half pairs over the head, a quarter rotated",
+    "mixed_sinks_bf16": "the sliding-window mixed batch with 4 sink keys beside the window (StreamingLLM)",
 }
 # kernels whose launches carry timing events inside the timed region
 DOMINANT = {
@@ -64,6 +65,7 @@ DOMINANT = {
     "prefill_bidir_bf16": ("attn_prefill",),
     "prefill_mrope_bf16": ("rope_write",),
     "prefill_prope_bf16": ("rope_write",),
+    "mixed_sinks_bf16": ("attn_prefill", "attn_decode"),
 }
 KERNEL_SOURCES = ["attn_decode.hip", "attn_prefill.hip", "rope_write.hip", "lse_merge.hip", "common.h", "internal.h"]
 # the sources a kernel family is built from: a counter summary stays valid

@@ -294,6 +294,46 @@ int nk_attention_lse_merge(const float *partial_out, const float *partial_lse,
 /* Static description of a status code. */
 const char *nk_status_string(int status);
 
+/*
+ * nk_attention_pack -- pack ragged K/V token matrices into the paged cache.
+ *
+ * NumKong matrix-kernels page, "Attention with a Pre-Packed KV-Cache" and
+ * attention_pack: the keys and values of all segments are packed once and
+ * scored against many queries; segments of different lengths share the
+ * pack, addressed by cumulative key_offsets, and segment s keeps
+ * key_lengths[s] keys (by default its whole slot) from row key_offsets[s].
+ * The pack is this library's paged cache: attention over it is
+ * nk_ragged_paged_attention (or _band) with kv_lens = kv_lens_out, the
+ * queries aligned to the end of each segment's kept keys.
+ *
+ *   k, v         device, in_dtype [rows][num_kv_heads][head_dim] row-major
+ *                (rows >= key_offsets[num_seqs]); in_dtype NK_F32 for an
+ *                NK_F32 cache, NK_BF16 for NK_BF16 and NK_E4M3 caches.
+ *   key_offsets  device int32 [num_seqs + 1], non-decreasing: segment s's
+ *                slot is rows key_offsets[s] .. key_offsets[s+1]-1.
+ *   key_lengths  device int32 [num_seqs] or NULL (whole slots): kept keys,
+ *                clamped to [0, slot size] and to max_key_len.
+ *   cache        written: segment s takes the next ceil(kept/page_size)
+ *                pages after those of segments 0..s-1 (pages 0, 1, ... in
+ *                order), its page_table row lists them (entries past that
+ *                count are left alone), and the kept tokens' K, V (and e4m3
+ *                scales, absmax/448 per token and head, as the append
+ *                step) are stored unrotated, rounded once to the cache type.
+ *                Slots past a segment's last kept key are not written.
+ *   kv_lens_out  device int32 [num_seqs]: the kept lengths.
+ *   max_key_len  an upper bound of the kept lengths; the page table's
+ *                stride must hold ceil(max_key_len / page_size) entries.
+ * Precondition: num_pages >= sum over s of ceil(kept_s / page_size); with a
+ * smaller cache, page ids are clamped to num_pages - 1 (no access out of
+ * bounds, the contents unspecified).  Two kernels on `stream`, no
+ * allocation, no synchronisation.  Errors: NK_ERR_INVALID_ARG (negative
+ * sizes, null pointers, a table stride too small), NK_ERR_UNSUPPORTED
+ * (dtype pair, head_dim, page_size), NK_ERR_DEVICE (launch failure).
+ */
+int nk_attention_pack(const void *k, const void *v, int32_t in_dtype, const int32_t *key_offsets,
+                      const int32_t *key_lengths, const nk_paged_kv_t *cache, int32_t *kv_lens_out,
+                      int32_t num_seqs, int32_t max_key_len, void *stream);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int nk_version(void);
 
@@ -302,7 +342,8 @@ int nk_version(void);
  * families: NK_PROF_ROPE_WRITE ("rope_write"), NK_PROF_ATTN_DECODE
  * ("attn_decode"), NK_PROF_ATTN_PREFILL ("attn_prefill", which includes its
  * scheduling kernel), NK_PROF_ATTN_F32 ("attn_f32"), NK_PROF_LSE_MERGE
- * ("lse_merge"); NK_PROF_ALL selects every family and 0 turns timing off.
+ * ("lse_merge"), NK_PROF_ATTENTION_PACK ("attention_pack", with its page
+ * assignment kernel); NK_PROF_ALL selects every family and 0 turns timing off.
  * The kernels of a selected family are launched with a pair of HIP events
  * (hipExtLaunchKernel) that take the first kernel's dispatch start time and
  * the last one's end time on the call's stream; no marker packets are added
@@ -318,7 +359,8 @@ int nk_version(void);
 #define NK_PROF_ATTN_PREFILL 4
 #define NK_PROF_ATTN_F32 8
 #define NK_PROF_LSE_MERGE 16
-#define NK_PROF_ALL 31
+#define NK_PROF_ATTENTION_PACK 32
+#define NK_PROF_ALL 63
 int nk_profile_enable(int family_mask);
 int nk_profile_reset(void);
 int nk_profile_read(const char *kernel, double *total_ms_host, int64_t *launches_host);

@@ -20,6 +20,8 @@ definitions state:
                    ``generic_fused_qk_rope_bshd_paged_ragged_kernel_api``;
                    NumKong matrix-kernels page, ``attention_rope``; aria_kernel
                    crate, ``rope`` / ``rope_half`` / ``rope_half_partial``).
+* ``pack``      -- ragged K/V token rows packed into the paged cache (NumKong
+                   matrix-kernels page, ``attention_pack``).
 * ``attention`` -- ragged scaled-dot-product attention under a key band
                    (NumKong matrix-kernels page, "Attention with a Pre-Packed
                    KV-Cache" and ``attention_packed``; Algenta "Attention
@@ -34,4 +36,4 @@ Every function is pinned by tests in ``tests/test_oracle_*.py`` against values
 the pages print, closed forms, invariants, library routines or brute force.
 """
 
-from . import formats, paged, rope, attention, merge, brute  # noqa: F401
+from . import formats, paged, pack, rope, attention, merge, brute  # noqa: F401

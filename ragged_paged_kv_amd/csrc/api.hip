@@ -140,8 +140,9 @@ void flush_pending(ProfileState &p) {
 namespace nk {
 
 static int family_bit(const char *family) {
-  static const char *const names[] = {"rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge"};
-  for (int i = 0; i < 5; ++i)
+  static const char *const names[] = {"rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge",
+                                      "attention_pack"};
+  for (int i = 0; i < 6; ++i)
     if (std::strcmp(family, names[i]) == 0) return 1 << i;
   return 0;
 }
@@ -355,6 +356,27 @@ int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t
   if (launch_attn_decode(a, s) != hipSuccess) return NK_ERR_DEVICE;
   if (wp.partials && launch_decode_merge(a, s) != hipSuccess) return NK_ERR_DEVICE;
   return NK_OK;
+}
+
+int nk_attention_pack(const void *k, const void *v, int32_t in_dtype, const int32_t *key_offsets,
+                      const int32_t *key_lengths, const nk_paged_kv_t *cache, int32_t *kv_lens_out,
+                      int32_t num_seqs, int32_t max_key_len, void *stream) {
+  if (num_seqs < 0 || max_key_len < 0) return NK_ERR_INVALID_ARG;
+  int st = check_cache(cache);
+  if (st != NK_OK) return st;
+  const bool ok_types = (in_dtype == NK_F32 && cache->dtype == NK_F32) ||
+                        (in_dtype == NK_BF16 && (cache->dtype == NK_BF16 || cache->dtype == NK_E4M3));
+  if (!ok_types) return NK_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return NK_OK;
+  if (!key_offsets || !kv_lens_out) return NK_ERR_INVALID_ARG;
+  if (max_key_len > 0 && (!k || !v || cache->num_pages <= 0)) return NK_ERR_INVALID_ARG;
+  if ((long long)cache->page_table_stride * cache->page_size < (long long)max_key_len) return NK_ERR_INVALID_ARG;
+  PackArgs a{};
+  a.k = k; a.v = v; a.in_dtype = in_dtype;
+  a.key_offsets = key_offsets; a.key_lengths = key_lengths;
+  a.cache = *cache; a.kv_lens_out = kv_lens_out;
+  a.num_seqs = num_seqs; a.max_key_len = max_key_len;
+  return launch_attention_pack(a, (hipStream_t)stream) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
 }
 
 int nk_attention_lse_merge(const float *partial_out, const float *partial_lse,

@@ -69,7 +69,19 @@ __host__ __device__ inline size_t sched_bytes(int num_seqs, int total_q) {
 
 // Each launcher enqueues its kernel(s) on `stream` and returns a
 // hipError_t (hipSuccess when the launch was accepted).
+// Packing ragged K/V token rows into cache pages (no rotation): segment s
+// keeps its first kept-length rows from row key_offsets[s]
+struct PackArgs {
+  const void *k, *v;
+  int32_t in_dtype;
+  const int32_t *key_offsets, *key_lengths;   // [num_seqs + 1], [num_seqs] or null
+  nk_paged_kv_t cache;                         // pages, scales and page table written
+  int32_t *kv_lens_out;                        // [num_seqs]
+  int32_t num_seqs, max_key_len;
+};
+
 hipError_t launch_rope_write(const RopeArgs &a, hipStream_t stream);
+hipError_t launch_attention_pack(const PackArgs &a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream);

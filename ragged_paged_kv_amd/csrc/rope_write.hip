@@ -423,4 +423,143 @@ hipError_t launch_rope_write(const RopeArgs &a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------------------ packing
+// NumKong matrix-kernels page, "Attention with a Pre-Packed KV-Cache" and
+// attention_pack: ragged K/V token matrices are packed once into a cache that
+// attention then reads many times; segment s keeps key_lengths[s] keys (by
+// default its whole slot key_offsets[s] .. key_offsets[s+1]-1) from row
+// key_offsets[s].  The pack here is this library's paged cache: segment s
+// takes the next ceil(kept/P) pages after those of segments 0..s-1, its
+// table row lists them, and kv_lens_out[s] = kept.  The keys are stored as
+// they come (no rotation), rounded once to the cache type; e4m3 rows take
+// one scale per (token, kv head), absmax / 448, as the append step does.
+namespace {
+
+// kept keys of segment s: key_lengths[s] clamped to [0, slot] and to the
+// stated maximum (a larger value violates the precondition; clamping keeps
+// every access inside the table row and the grid)
+NK_DEVICE int pack_len(const PackArgs &a, int s) {
+  const int slot = a.key_offsets[s + 1] - a.key_offsets[s];
+  const int n = a.key_lengths ? a.key_lengths[s] : slot;
+  return max(0, min(min(n, slot), a.max_key_len));
+}
+
+constexpr int kPackPlanThreads = 1024;
+
+// One work-group: kept lengths, then an exclusive scan of the page counts in
+// blocks of kPackPlanThreads segments, then the table rows.  Page ids are
+// clamped to the cache (a cache smaller than the pack violates the
+// precondition; nothing is then read or written out of bounds).
+__global__ void __launch_bounds__(kPackPlanThreads) pack_plan_kernel(PackArgs a) {
+  __shared__ int part[kPackPlanThreads / 64];
+  __shared__ int first[kPackPlanThreads], count[kPackPlanThreads];
+  __shared__ int carry;
+  const int P = a.cache.page_size;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int s0 = 0; s0 < a.num_seqs; s0 += kPackPlanThreads) {
+    const int s = s0 + tid;
+    const int len = s < a.num_seqs ? pack_len(a, s) : 0;
+    const int np = (len + P - 1) / P;
+    int x = np;                                   // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, kWave);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) part[w] = x;
+    __syncthreads();
+    int before = carry;
+    for (int i = 0; i < w; ++i) before += part[i];
+    first[tid] = before + x - np;
+    count[tid] = np;
+    if (s < a.num_seqs) a.kv_lens_out[s] = len;
+    __syncthreads();                              // every read of carry and part is done
+    if (tid == kPackPlanThreads - 1) carry = first[tid] + np;
+    const int nseg = min(kPackPlanThreads, a.num_seqs - s0);
+    for (int k = 0; k < nseg; ++k) {
+      int32_t *row = const_cast<int32_t *>(a.cache.page_table) + (size_t)(s0 + k) * a.cache.page_table_stride;
+      for (int i = tid; i < count[k]; i += kPackPlanThreads) row[i] = min(first[k] + i, a.cache.num_pages - 1);
+    }
+    __syncthreads();
+  }
+}
+
+template <int CACHE> NK_DEVICE void store_v1(uint8_t *p, double x);
+template <> NK_DEVICE void store_v1<kCacheF32>(uint8_t *p, double x) { *(float *)p = (float)x; }
+template <> NK_DEVICE void store_v1<kCacheBF16>(uint8_t *p, double x) { *(bf16_t *)p = (bf16_t)round_odd_f32(x); }
+template <> NK_DEVICE void store_v1<kCacheE4M3>(uint8_t *p, double x) { *p = (uint8_t)(fp8x2(x, 0.0) & 0xffu); }
+
+// One work-group per (segment, page of its pack, kv head): every 8-dim unit
+// of the page's kept tokens, K and V.  A token's D/8 units are consecutive
+// lanes (D/8 divides 64), so the e4m3 absmax is a lane-group reduction.
+template <typename TIn, int CACHE>
+__global__ void __launch_bounds__(256) pack_kernel(PackArgs a, int pages_per_seq) {
+  constexpr int esz = CACHE == kCacheF32 ? 4 : (CACHE == kCacheBF16 ? 2 : 1);
+  const int s = blockIdx.x / pages_per_seq, i = blockIdx.x % pages_per_seq, g = blockIdx.y;
+  const int P = a.cache.page_size, D = a.cache.head_dim, hkv = a.cache.num_kv_heads;
+  const int len = pack_len(a, s);
+  if (i * P >= len) return;
+  const int page = a.cache.page_table[(size_t)s * a.cache.page_table_stride + i];
+  const size_t ph = (size_t)page * hkv + g;
+  uint8_t *kph = (uint8_t *)a.cache.k_pages + ph * P * (size_t)D * esz;
+  uint8_t *vph = (uint8_t *)a.cache.v_pages + ph * P * (size_t)D * esz;
+  const int upt = D / 8;
+  const int row0 = a.key_offsets[s] + i * P;
+  for (int u0 = 0; u0 < P * upt; u0 += 256) {          // uniform trip count: shuffles see every lane
+    const int u = u0 + (int)threadIdx.x;
+    const int t = u / upt, c = u % upt;
+    const bool valid = u < P * upt && i * P + t < len;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      double x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (valid) {
+        const TIn *src = (const TIn *)(kv == 0 ? a.k : a.v) + ((size_t)(row0 + t) * hkv + g) * D + 8 * c;
+        InTraits<TIn>::load8(src, x);
+      }
+      if (CACHE == kCacheE4M3) {
+        double m = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmax(m, fabs(x[e]));
+        for (int mask = 1; mask < upt; mask <<= 1) m = fmax(m, __shfl_xor(m, mask, kWave));
+        const float scale = (float)(m / 448.0);          // float32 nearest to absmax / 448
+        const double sd = scale;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = scale > 0.f ? x[e] / sd : 0.0;
+        if (valid && c == 0) (kv == 0 ? a.cache.k_scales : a.cache.v_scales)[ph * P + t] = scale;
+      }
+      if (!valid) continue;
+      if (kv == 0) {
+        store_k8<CACHE>(kph + k_index<CACHE>(8 * c, t, P) * esz, 0, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store_v1<CACHE>(vph + v_index<CACHE>(8 * c + e, t, D) * esz, x[e]);
+      }
+    }
+  }
+}
+
+template <typename TIn, int CACHE>
+hipError_t launch_pack(const PackArgs &a, hipStream_t stream) {
+  hipError_t e = launch(pack_plan_kernel, dim3(1), dim3(kPackPlanThreads), 0, stream, a);
+  if (e != hipSuccess || a.max_key_len == 0) return e;
+  const int pages_per_seq = (a.max_key_len + a.cache.page_size - 1) / a.cache.page_size;
+  const long long blocks = (long long)a.num_seqs * pages_per_seq;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  return launch(pack_kernel<TIn, CACHE>, dim3((unsigned)blocks, (unsigned)a.cache.num_kv_heads), dim3(256), 0,
+                stream, a, pages_per_seq);
+}
+
+}  // namespace
+
+hipError_t launch_attention_pack(const PackArgs &a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  ProfileScope prof("attention_pack", stream);
+  if (a.in_dtype == NK_F32 && a.cache.dtype == NK_F32) return launch_pack<float, kCacheF32>(a, stream);
+  if (a.in_dtype == NK_BF16 && a.cache.dtype == NK_BF16) return launch_pack<bf16_t, kCacheBF16>(a, stream);
+  if (a.in_dtype == NK_BF16 && a.cache.dtype == NK_E4M3) return launch_pack<bf16_t, kCacheE4M3>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace nk

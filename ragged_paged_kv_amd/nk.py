@@ -22,7 +22,7 @@ NK_OK, NK_ERR_INVALID_ARG, NK_ERR_UNSUPPORTED, NK_ERR_WORKSPACE, NK_ERR_DEVICE =
 EXPORTS = ("nk_rope_qk_write_paged", "nk_rope_qk_write_paged_mrope", "nk_ragged_paged_attention", "nk_ragged_paged_attention_band",
            "nk_ragged_paged_attention_workspace_size", "nk_ragged_paged_attention_split_tokens",
            "nk_attention_lse_merge", "nk_status_string", "nk_version", "nk_profile_enable",
-           "nk_profile_reset", "nk_profile_read")
+           "nk_profile_reset", "nk_profile_read", "nk_attention_pack")
 
 
 class NKError(RuntimeError):
@@ -73,6 +73,8 @@ def lib():
         L.nk_status_string.argtypes = [ctypes.c_int]
         L.nk_status_string.restype = ctypes.c_char_p
         L.nk_version.restype = ctypes.c_int
+        L.nk_attention_pack.argtypes = [vp, vp, i32, vp, vp, cache_p, vp, i32, i32, vp]
+        L.nk_attention_pack.restype = ctypes.c_int
         L.nk_profile_enable.argtypes = [ctypes.c_int]
         L.nk_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
@@ -269,7 +271,55 @@ def attention_lse_merge(partial_out, partial_lse, merge_offsets, out, lse_out=No
     return out, lse_out
 
 
-PROFILE_FAMILIES = ("rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge")
+def attention_pack(k, v, key_offsets, key_lengths=None, page_size=16, cache_dtype=None, max_key_len=None,
+                   num_pages=None, stream=None):
+    """Pack ragged K/V rows [rows, Hkv, D] into a new paged cache: segment s
+    keeps ``key_lengths[s]`` keys (default: its whole slot) from row
+    ``key_offsets[s]``.  Returns (cache, kv_lens, max_key_len); attention
+    over it is ``ragged_paged_attention(q, q_offsets, kv_lens, cache, ...)``.
+    ``cache_dtype`` is "f32", "bf16" or "e4m3" (default: the input's type).
+    When ``max_key_len`` or ``num_pages`` is not given it is read from the
+    lengths (a device-to-host copy)."""
+    rows, hkv, d = k.shape
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must share shape and dtype")
+    _i32(key_offsets, "key_offsets")
+    if key_lengths is not None:
+        _i32(key_lengths, "key_lengths")
+    _dev(k, v, key_offsets, key_lengths)
+    B = key_offsets.shape[0] - 1
+    cdt = cache_dtype or ("f32" if k.dtype == torch.float32 else "bf16")
+    if max_key_len is None or num_pages is None:
+        slots = (key_offsets[1:] - key_offsets[:-1]).cpu()
+        kept = slots if key_lengths is None else torch.minimum(torch.clamp(key_lengths.cpu(), min=0), slots)
+        if max_key_len is None:
+            max_key_len = int(kept.max()) if B > 0 else 0
+        kept = torch.clamp(kept, max=max_key_len)
+        if num_pages is None:
+            num_pages = int(((kept + page_size - 1) // page_size).sum())
+    num_pages = max(int(num_pages), 1)
+    stride = max(1, -(-int(max_key_len) // page_size))
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[cdt]
+    nk_ = 2 if cdt == "e4m3" else 1
+    nv = {"f32": 1, "bf16": 2, "e4m3": 4}[cdt]
+    dev = k.device
+    kp = torch.empty(num_pages, hkv, d // (32 * nk_), page_size, 32 * nk_, dtype=tdt, device=dev)
+    vp = torch.empty(num_pages, hkv, page_size // 16, d // (16 * nv), 64, 4 * nv, dtype=tdt, device=dev)
+    ks = vs = None
+    if cdt == "e4m3":
+        ks = torch.empty(num_pages, hkv, page_size, dtype=torch.float32, device=dev)
+        vs = torch.empty_like(ks)
+    table = torch.zeros(max(B, 1), stride, dtype=torch.int32, device=dev)
+    cache = PagedKVCache(kp, vp, table, ks, vs)
+    kv_lens = torch.empty(max(B, 0), dtype=torch.int32, device=dev)
+    c = cache.struct()
+    st = lib().nk_attention_pack(_ptr(k), _ptr(v), _dtype_code(k.dtype), _ptr(key_offsets), _ptr(key_lengths),
+                                 ctypes.byref(c), _ptr(kv_lens), B, int(max_key_len), _stream(stream))
+    _check(st, "nk_attention_pack")
+    return cache, kv_lens, int(max_key_len)
+
+
+PROFILE_FAMILIES = ("rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge", "attention_pack")
 
 
 def profile_enable(on=True, families=None):

@@ -27,8 +27,9 @@ import torch
 
 NAMES = ("tiny_prefill_f32", "decode_bf16", "prefill_bf16", "mixed_window_bf16", "decode_fp8")
 # beyond the five: the prefill batch under a band unbounded on both sides
-# (every row sees its whole segment), for the band entry point
-EXTRA = ("prefill_bidir_bf16", "prefill_mrope_bf16", "prefill_prope_bf16")
+# (every row sees its whole segment), with M-RoPE and with p-RoPE; the mixed
+# batch with 4 sink keys beside its window
+EXTRA = ("prefill_bidir_bf16", "prefill_mrope_bf16", "prefill_prope_bf16", "mixed_sinks_bf16")
 
 
 def names():
@@ -140,6 +141,8 @@ def _pages(rng, kv_lens, page_size, order):
 
 def make(which):
     """Workload by number (1..5) or name."""
+    if which == "mixed_sinks_bf16":                    # StreamingLLM: 4 sink keys beside the window
+        return replace(make("mixed_window_bf16"), name=which, sink_keys=4)
     if which in EXTRA:
         w = replace(make("prefill_bf16"), name=which)
         if which == "prefill_bidir_bf16":

@@ -157,7 +157,7 @@ def test_profile_api_without_gpu(L):
     assert L.nk_profile_enable(0) == 0
     ms, n = nk.profile_read("attn_decode")
     assert n == 0 and ms == 0.0
-    assert L.nk_profile_enable(1 << 5) == nk.NK_ERR_INVALID_ARG       # no such family
+    assert L.nk_profile_enable(1 << 6) == nk.NK_ERR_INVALID_ARG       # no such family
     assert L.nk_profile_enable(-1) == nk.NK_ERR_INVALID_ARG
     nk.profile_enable(True, ["attn_decode", "lse_merge"])             # host-side only, no launch
     nk.profile_enable(False)
@@ -182,3 +182,26 @@ def test_mrope_validation(L):
     assert mrope([16, 16, 16, 8, 8], total=0) == nk.NK_ERR_INVALID_ARG    # more than 4 sections
     assert mrope([64], pos=None, total=0) == nk.NK_ERR_INVALID_ARG    # sections need position streams
     assert mrope(None, total=0) == nk.NK_OK                           # no sections: the plain call
+
+
+def pack(L, cache, **kw):
+    a = dict(k=1, v=1, in_dtype=nk.NK_BF16, offs=1, lens=None, out=1, num_seqs=2, max_len=64)
+    a.update(kw)
+    return L.nk_attention_pack(a["k"], a["v"], a["in_dtype"], a["offs"], a["lens"],
+                               None if cache is None else ctypes.byref(cache), a["out"], a["num_seqs"],
+                               a["max_len"], None)
+
+
+def test_pack_validation(L):
+    c = _cache()                                                      # 4 pages of 16, table stride 4
+    assert pack(L, c, num_seqs=-1) == nk.NK_ERR_INVALID_ARG
+    assert pack(L, c, max_len=-1) == nk.NK_ERR_INVALID_ARG
+    assert pack(L, None) == nk.NK_ERR_INVALID_ARG
+    assert pack(L, c, max_len=65) == nk.NK_ERR_INVALID_ARG            # the table row holds 4 pages of 16
+    assert pack(L, c, offs=None) == nk.NK_ERR_INVALID_ARG
+    assert pack(L, c, out=None) == nk.NK_ERR_INVALID_ARG
+    assert pack(L, c, k=None) == nk.NK_ERR_INVALID_ARG
+    assert pack(L, c, in_dtype=nk.NK_F32) == nk.NK_ERR_UNSUPPORTED    # float32 rows into a bf16 cache
+    assert pack(L, _cache(dtype=nk.NK_E4M3), in_dtype=nk.NK_F32) == nk.NK_ERR_UNSUPPORTED
+    assert pack(L, _cache(head_dim=96)) == nk.NK_ERR_UNSUPPORTED
+    assert pack(L, c, num_seqs=0) == nk.NK_OK                         # nothing to pack: no launch
