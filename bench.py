@@ -54,6 +54,7 @@ DESCR = {
     "prefill_mrope_bf16": "the ragged prefill batch with M-RoPE: three position streams over 16/24/24 pairs",
     "prefill_prope_bf16": "the ragged prefill batch with p-RoPE: rotate-half pairs over the head, a quarter rotated",
     "mixed_sinks_bf16": "the sliding-window mixed batch with 4 sink keys beside the window (StreamingLLM)",
+    "pack_bf16": "attention_pack of the decode batch's keys (32 slots with 64 spare rows each), Hkv8, D128, page16",
 }
 # kernels whose launches carry timing events inside the timed region
 DOMINANT = {
@@ -268,8 +269,73 @@ def measure(st, steps, warmup, flush, split=None):
     return res
 
 
+def measure_pack(steps, warmup, flush):
+    """nk_attention_pack of the decode batch's keys: 32 slots of kv_len + 64
+    rows each (spare room, left out through key_lengths), Hkv 8, D 128,
+    bf16 rows into 16-token pages.  Algorithmic bytes: the kept K and V rows
+    read once and written once, plus the offsets, lengths and table."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    from ragged_paged_kv_amd import nk
+
+    w = synth.make("decode_bf16")
+    kept = w.kv_lens.astype(np.int64)
+    slots = kept + 64
+    offs = np.concatenate([[0], np.cumsum(slots)]).astype(np.int32)
+    rows, hkv, d, P = int(offs[-1]), w.num_kv_heads, w.head_dim, 16
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    k = torch.randn(rows, hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(rows, hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    d_offs = torch.from_numpy(offs).cuda()
+    d_lens = torch.from_numpy(kept.astype(np.int32)).cuda()
+    cache, kv_lens, max_len = nk.attention_pack(k, v, d_offs, d_lens, page_size=P, max_key_len=int(kept.max()))
+    c = cache.struct()
+    B = len(kept)
+
+    def step():
+        st = nk.lib().nk_attention_pack(k.data_ptr(), v.data_ptr(), nk.NK_BF16, d_offs.data_ptr(),
+                                        d_lens.data_ptr(), ctypes.byref(c), kv_lens.data_ptr(), B, max_len,
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == nk.NK_OK
+
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    nk.profile_reset()
+    nk.profile_enable(True, ["attention_pack"])
+    evs = [(StepEvent(), StepEvent()) for _ in range(steps)]
+    for i in range(steps):
+        if scratch is not None:
+            torch.sum(scratch, dim=0, out=sink)
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    nk.profile_enable(False)
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    tot, n = nk.profile_read("attention_pack")
+    kb = int(kept.sum()) * hkv * d * 2 * 2
+    nbytes = 2 * kb + (B + 1) * 4 + B * 4 + int(((kept + P - 1) // P).sum()) * 4 + B * 4
+    ms = times[len(times) // 2]
+    res = {"workload": "pack_bf16", "descr": DESCR["pack_bf16"], "ms_per_step": ms, "ms_min": times[0],
+           "ms_max": times[-1], "kernels": {"attention_pack": {"avg_ms": tot / n, "launches": n}},
+           "kernels_timed_in_region": ["attention_pack"], "pack_bytes": nbytes,
+           "pack_GBps_kernel": nbytes / (tot / n) / 1e6}
+    del scratch
+    return res
+
+
 def run_workload(name, steps, warmup, flush):
     import torch
+    if name == "pack_bf16":
+        res = measure_pack(steps, warmup, flush)
+        torch.cuda.empty_cache()
+        return res
     st = prepare(name)
     res = measure(st, steps, warmup, flush)
     del st
@@ -555,7 +621,10 @@ def main():
     }
     extra = {}
     for n, r in results.items():
-        e = {"ms_per_step": r["ms_per_step"], "kernels": r["kernels"], "split_tokens": r["split_tokens"]}
+        e = {"ms_per_step": r["ms_per_step"], "kernels": r["kernels"], "split_tokens": r.get("split_tokens")}
+        if r.get("pack_GBps_kernel"):
+            e["pack_GBps_kernel"] = r["pack_GBps_kernel"]
+            e["pack_hbm_frac"] = r["pack_GBps_kernel"] / HBM_PEAK_GBS
         if r.get("decode_GBps_kernel"):
             e["decode_GBps_kernel"] = r["decode_GBps_kernel"]
             e["decode_hbm_frac"] = r["decode_GBps_kernel"] / HBM_PEAK_GBS
