@@ -334,6 +334,42 @@ int nk_attention_pack(const void *k, const void *v, int32_t in_dtype, const int3
                       const int32_t *key_lengths, const nk_paged_kv_t *cache, int32_t *kv_lens_out,
                       int32_t num_seqs, int32_t max_key_len, void *stream);
 
+/*
+ * nk_ragged_paged_attention_backward -- query, key and value gradients.
+ *
+ * NumKong matrix-kernels page, attention_packed_gradients: from the
+ * forward's output, its gradient and its (tokens, heads) log-sum-exp, the
+ * gradients of q, k and v under the same band.  With s_ij = scale * q_i.k_j
+ * over the keys row i sees (window_left, window_right, sink_keys exactly as
+ * nk_ragged_paged_attention_band) and P_ij = exp(s_ij - lse_i):
+ *   dv_j = sum_i P_ij dout_i,  ds_ij = P_ij (dout_i.v_j - dout_i.out_i),
+ *   dq_i = scale * sum_j ds_ij k_j,  dk_j = scale * sum_i ds_ij q_i,
+ * each KV head's dk, dv summed over its query heads.
+ *
+ *   q, out, dout q_dtype [total_q][num_q_heads][head_dim]: the (rotated)
+ *                queries the forward used, its output, the output gradient.
+ *   lse          float32 [total_q][num_q_heads], the forward's.
+ *   cache, q_offsets, kv_lens: as the forward (keys read from the pages).
+ *   key_offsets  int32 [num_seqs + 1]: segment s's key j has its dk, dv at
+ *                row key_offsets[s] + j (e.g. the offsets nk_attention_pack
+ *                read the keys from); rows past kv_lens[s] are not written.
+ *   dq           float32 [total_q][num_q_heads][head_dim].
+ *   dk, dv       float32 [rows][num_kv_heads][head_dim]; every key of every
+ *                segment is written (zeros when no row sees it).
+ * The pages call these bf16 gradients yet take a float32 query-gradient
+ * buffer; all three are float32 here (a bf16 copy is one rounding away).
+ * Types: q_dtype NK_F32 with an NK_F32 cache, NK_BF16 with NK_BF16;
+ * e4m3 caches return NK_ERR_UNSUPPORTED.  Two kernels on `stream`, no
+ * workspace, no allocation.  Errors as nk_ragged_paged_attention_band.
+ */
+int nk_ragged_paged_attention_backward(const void *q, int32_t q_dtype, const int32_t *q_offsets,
+                                       const int32_t *kv_lens, const nk_paged_kv_t *cache, float softmax_scale,
+                                       int32_t window_left, int32_t window_right, int32_t sink_keys,
+                                       const void *out, const void *dout, const float *lse,
+                                       const int32_t *key_offsets, float *dq, float *dk, float *dv,
+                                       int32_t num_seqs, int32_t total_q, int32_t max_kv_len,
+                                       int32_t num_q_heads, void *stream);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int nk_version(void);
 
@@ -343,7 +379,8 @@ int nk_version(void);
  * ("attn_decode"), NK_PROF_ATTN_PREFILL ("attn_prefill", which includes its
  * scheduling kernel), NK_PROF_ATTN_F32 ("attn_f32"), NK_PROF_LSE_MERGE
  * ("lse_merge"), NK_PROF_ATTENTION_PACK ("attention_pack", with its page
- * assignment kernel); NK_PROF_ALL selects every family and 0 turns timing off.
+ * assignment kernel), NK_PROF_ATTN_BACKWARD ("attn_backward", both of its
+ * kernels); NK_PROF_ALL selects every family and 0 turns timing off.
  * The kernels of a selected family are launched with a pair of HIP events
  * (hipExtLaunchKernel) that take the first kernel's dispatch start time and
  * the last one's end time on the call's stream; no marker packets are added
@@ -360,7 +397,8 @@ int nk_version(void);
 #define NK_PROF_ATTN_F32 8
 #define NK_PROF_LSE_MERGE 16
 #define NK_PROF_ATTENTION_PACK 32
-#define NK_PROF_ALL 63
+#define NK_PROF_ATTN_BACKWARD 64
+#define NK_PROF_ALL 127
 int nk_profile_enable(int family_mask);
 int nk_profile_reset(void);
 int nk_profile_read(const char *kernel, double *total_ms_host, int64_t *launches_host);

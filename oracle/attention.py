@@ -143,3 +143,49 @@ def dense_attention(q, k, v, softmax_scale, window_left=-1, window_right=0, sink
         out[:, h, :] = o
         lse[:, h] = l
     return out, lse
+
+
+def ragged_paged_attention_backward(q, q_offsets, kv_lens, cache, page_table, softmax_scale, dout,
+                                    window_left=-1, window_right=0, sink_keys=0):
+    """Gradients of ``ragged_paged_attention`` (NumKong matrix-kernels page,
+    ``attention_packed_gradients``: query, key and value gradients under the
+    same band), from the plain definition: per row, P = softmax of the
+    visible scores, out = P V; for the output gradient dO the softmax
+    Jacobian gives dS_j = P_j (dO.v_j - dO.out), and
+    dq = scale sum_j dS_j k_j, dk_j += scale dS_j q, dv_j += P_j dO,
+    summed over the query heads sharing a KV head.
+
+    q, dout [T, Hq, D] float64.  Returns dq [T, Hq, D] and lists dk, dv of
+    per-segment [kv_len, Hkv, D] arrays.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    T, hq, d = q.shape
+    hkv = cache.num_kv_heads
+    group = hq // hkv
+    dq = np.zeros_like(q)
+    dk, dv = [], []
+    for s in range(len(kv_lens)):
+        a, b = int(q_offsets[s]), int(q_offsets[s + 1])
+        q_len, kv_len = b - a, int(kv_lens[s])
+        K, V = cache.gather(page_table, s, kv_len)
+        dK = np.zeros((kv_len, hkv, d))
+        dV = np.zeros((kv_len, hkv, d))
+        for r in range(q_len):
+            idx = visible_keys(r, q_len, kv_len, window_left, window_right, sink_keys)
+            if idx.size == 0:
+                continue
+            for h in range(hq):
+                g = h // group
+                qi, doi = q[a + r, h], dout[a + r, h]
+                sc = softmax_scale * (K[idx, g] @ qi)
+                e = np.exp(sc - np.max(sc))
+                p = e / np.sum(e)
+                o = p @ V[idx, g]
+                ds = p * (V[idx, g] @ doi - doi @ o)
+                dq[a + r, h] = softmax_scale * (ds @ K[idx, g])
+                dK[idx, g] += softmax_scale * ds[:, None] * qi[None, :]
+                dV[idx, g] += p[:, None] * doi[None, :]
+        dk.append(dK)
+        dv.append(dV)
+    return dq, dk, dv

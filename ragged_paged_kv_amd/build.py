@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnk.so")
-SOURCES = ["api.hip", "rope_write.hip", "attn_decode.hip", "attn_prefill.hip", "attn_f32.hip",
+SOURCES = ["api.hip", "rope_write.hip", "attn_decode.hip", "attn_prefill.hip", "attn_f32.hip", "attn_backward.hip",
            "lse_merge.hip"]
 ARCH = "gfx950"
 # per-file extra flags: the decode kernel keeps its MFMA accumulators in

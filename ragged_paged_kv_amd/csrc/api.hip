@@ -141,8 +141,8 @@ namespace nk {
 
 static int family_bit(const char *family) {
   static const char *const names[] = {"rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge",
-                                      "attention_pack"};
-  for (int i = 0; i < 6; ++i)
+                                      "attention_pack", "attn_backward"};
+  for (int i = 0; i < 7; ++i)
     if (std::strcmp(family, names[i]) == 0) return 1 << i;
   return 0;
 }
@@ -377,6 +377,36 @@ int nk_attention_pack(const void *k, const void *v, int32_t in_dtype, const int3
   a.cache = *cache; a.kv_lens_out = kv_lens_out;
   a.num_seqs = num_seqs; a.max_key_len = max_key_len;
   return launch_attention_pack(a, (hipStream_t)stream) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
+}
+
+int nk_ragged_paged_attention_backward(const void *q, int32_t q_dtype, const int32_t *q_offsets,
+                                       const int32_t *kv_lens, const nk_paged_kv_t *cache, float softmax_scale,
+                                       int32_t window_left, int32_t window_right, int32_t sink_keys,
+                                       const void *out, const void *dout, const float *lse,
+                                       const int32_t *key_offsets, float *dq, float *dk, float *dv,
+                                       int32_t num_seqs, int32_t total_q, int32_t max_kv_len,
+                                       int32_t num_q_heads, void *stream) {
+  if (num_seqs < 0 || total_q < 0 || max_kv_len < 0 || num_q_heads <= 0) return NK_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1 || sink_keys < 0) return NK_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return NK_ERR_INVALID_ARG;
+  int st = check_cache(cache);
+  if (st != NK_OK) return st;
+  if (num_q_heads % cache->num_kv_heads) return NK_ERR_INVALID_ARG;
+  const bool ok_types = (q_dtype == NK_F32 && cache->dtype == NK_F32) ||
+                        (q_dtype == NK_BF16 && cache->dtype == NK_BF16);
+  if (!ok_types) return NK_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return total_q == 0 ? NK_OK : NK_ERR_INVALID_ARG;
+  if (!q_offsets || !kv_lens || !key_offsets) return NK_ERR_INVALID_ARG;
+  if (total_q > 0 && (!q || !out || !dout || !lse || !dq)) return NK_ERR_INVALID_ARG;
+  if (max_kv_len > 0 && (!dk || !dv)) return NK_ERR_INVALID_ARG;
+  BackwardArgs a{};
+  a.q = q; a.out = out; a.dout = dout; a.q_dtype = q_dtype; a.lse = lse;
+  a.q_offsets = q_offsets; a.kv_lens = kv_lens; a.key_offsets = key_offsets;
+  a.cache = *cache; a.softmax_scale = softmax_scale;
+  a.window_left = window_left; a.window_right = window_right; a.sink_keys = sink_keys;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.num_seqs = num_seqs; a.total_q = total_q; a.max_kv_len = max_kv_len; a.hq = num_q_heads;
+  return launch_attn_backward(a, (hipStream_t)stream) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
 }
 
 int nk_attention_lse_merge(const float *partial_out, const float *partial_lse,

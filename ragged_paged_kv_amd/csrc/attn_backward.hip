@@ -1,0 +1,215 @@
+// Gradients of ragged paged attention with respect to Q, K and V.
+//
+// What it computes: NumKong matrix-kernels page, attention_packed_gradients
+// -- from the forward's output O, its gradient dO and its log-sum-exp, the
+// query, key and value gradients under the same band (and sink keys) as the
+// forward.  With scores s_ij = scale * q_i.k_j over the keys row i sees and
+// P_ij = exp(s_ij - lse_i):
+//   dV_j  = sum_i P_ij dO_i
+//   dS_ij = P_ij (dO_i.v_j - dO_i.O_i)
+//   dQ_i  = scale * sum_j dS_ij k_j
+//   dK_j  = scale * sum_i dS_ij q_i
+// summed over the query heads that share a KV head (GQA).  This is the
+// softmax's Jacobian applied row by row (the running-state identities of the
+// Algenta page's flash-attention walkthrough give the same P from lse).
+//
+// Design (float32 VALU, correctness first): two kernels.
+//   * dQ: one wave per (query row, query head); lanes take 64 visible keys at
+//     a time, each lane computing its key's two dot products (q.k, dO.v), then
+//     lanes over head dimensions accumulate dS_j k_j;
+//   * dK/dV: one wave per (segment key, KV head); lanes take 64 (row, head)
+//     pairs of the rows that see the key, each computing q.k, dO.v and dO.O,
+//     then lanes over dimensions accumulate P dO and dS q.
+// Every key of a segment gets its rows written (zeros when no row sees it).
+// Scores are recomputed from the cache, as the forward computes them.
+
+#include "common.h"
+#include "internal.h"
+
+namespace nk {
+namespace {
+
+template <typename T> NK_DEVICE float ld(const T *p) { return (float)*p; }
+
+// Element (dim d, key t of its page) of a K or V page-head block (include/nk.h
+// layouts; NV = 4 / element bytes for V's 16-byte runs).
+template <typename T> NK_DEVICE size_t k_elem(int d, int t, int P) {
+  return ((size_t)(d >> 5) * P + t) * 32 + (d & 31);
+}
+template <typename T> NK_DEVICE size_t v_elem(int d, int t, int D) {
+  constexpr int NV = 4 / (int)sizeof(T);
+  return ((size_t)(t >> 4) * (D / (16 * NV)) + ((d >> 4) / NV)) * (64 * 4 * NV) +
+         (size_t)(16 * ((t & 15) >> 2) + (d & 15)) * (4 * NV) + ((d >> 4) % NV) * 4 + (t & 3);
+}
+
+// Keys a row at position p sees: [lo, hi] plus the sink keys 0..n_sink-1
+// left of lo, walked as one list (entry v: key v if v < n_sink, else
+// lo + v - n_sink).
+struct RowKeys {
+  int lo, hi, n_sink, n;
+  NK_DEVICE int key(int v) const { return v < n_sink ? v : lo + v - n_sink; }
+};
+NK_DEVICE RowKeys row_keys(const BackwardArgs &a, int p, int L) {
+  RowKeys r;
+  r.hi = band_hi(p, L, a.window_right);
+  r.lo = a.window_left < 0 ? 0 : max(0, p - a.window_left);
+  const int sinks = a.window_left < 0 ? 0 : a.sink_keys;
+  r.n_sink = max(0, min(sinks, min(r.lo, r.hi + 1)));
+  r.n = r.n_sink + max(0, r.hi - r.lo + 1);
+  return r;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(64) attn_dq_kernel(BackwardArgs a) {
+  const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int D = a.cache.head_dim, P = a.cache.page_size, hkv = a.cache.num_kv_heads;
+  const int g = h / (a.hq / hkv);
+  __shared__ float qs[256], dos[256];
+  const int s = find_segment(a.q_offsets, a.num_seqs, t);
+  const int q0 = a.q_offsets[s];
+  const int q_len = a.q_offsets[s + 1] - q0;
+  const int L = a.kv_lens[s];
+  const RowKeys rk = row_keys(a, (t - q0) + L - q_len, L);
+  const size_t row = (size_t)t * a.hq + h;
+  float di = 0.f;                                   // dO.O of the row
+  for (int d = lane; d < D; d += kWave) {
+    qs[d] = ld((const T *)a.q + row * D + d);
+    dos[d] = ld((const T *)a.dout + row * D + d);
+    di += dos[d] * ld((const T *)a.out + row * D + d);
+  }
+  di = wave_sum(di);
+  __syncthreads();
+  const float lse = a.lse[row];
+  const T *kp = (const T *)a.cache.k_pages;
+  const T *vp = (const T *)a.cache.v_pages;
+  const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
+  float dq[4] = {0.f, 0.f, 0.f, 0.f};                // dims lane, lane+64, ...
+  for (int base = 0; base < rk.n; base += kWave) {
+    const bool valid = base + lane < rk.n;
+    float ds = 0.f;
+    if (valid) {
+      const int key = rk.key(base + lane);
+      const size_t blk = ((size_t)pt[key / P] * hkv + g) * P * D;
+      float qk = 0.f, dv = 0.f;
+      for (int d = 0; d < D; ++d) {
+        qk = fmaf(qs[d], ld(kp + blk + k_elem<T>(d, key % P, P)), qk);
+        dv = fmaf(dos[d], ld(vp + blk + v_elem<T>(d, key % P, D)), dv);
+      }
+      const float p = expf(a.softmax_scale * qk - lse);
+      ds = p * (dv - di);
+    }
+    const int nk = min(kWave, rk.n - base);
+    for (int i = 0; i < nk; ++i) {
+      const float dsi = __shfl(ds, i, kWave);
+      const int key = rk.key(base + i);
+      const size_t blk = ((size_t)pt[key / P] * hkv + g) * P * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = lane + r * kWave;
+        if (d < D) dq[r] = fmaf(dsi, ld(kp + blk + k_elem<T>(d, key % P, P)), dq[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int d = lane + r * kWave;
+    if (d < D) a.dq[row * D + d] = a.softmax_scale * dq[r];
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(64) attn_dkv_kernel(BackwardArgs a) {
+  const int s = blockIdx.x / a.max_kv_len, j = blockIdx.x % a.max_kv_len, g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int D = a.cache.head_dim, P = a.cache.page_size, hkv = a.cache.num_kv_heads;
+  const int G = a.hq / hkv;
+  const int L = a.kv_lens[s];
+  if (j >= L) return;
+  __shared__ float ks[256], vs[256];
+  const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
+  const size_t blk = ((size_t)pt[j / P] * hkv + g) * P * D;
+  for (int d = lane; d < D; d += kWave) {
+    ks[d] = ld((const T *)a.cache.k_pages + blk + k_elem<T>(d, j % P, P));
+    vs[d] = ld((const T *)a.cache.v_pages + blk + v_elem<T>(d, j % P, D));
+  }
+  __syncthreads();
+  const int q0 = a.q_offsets[s];
+  const int q_len = a.q_offsets[s + 1] - q0;
+  const int shift = L - q_len;
+  // rows that may see key j: hi >= j from i_min on, lo <= j up to i_max
+  // (no upper limit for a sink key); each pair is checked exactly below
+  const int i_min = a.window_right < 0 ? 0 : max(0, j - a.window_right - shift);
+  const bool sink = a.window_left >= 0 && j < a.sink_keys;
+  const int i_max = (a.window_left < 0 || sink) ? q_len - 1 : min(q_len - 1, j + a.window_left - shift);
+  const int n_pairs = max(0, i_max - i_min + 1) * G;
+  float dk[4] = {0.f, 0.f, 0.f, 0.f}, dv[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < n_pairs; base += kWave) {
+    const int e = base + lane;
+    float p = 0.f, ds = 0.f;
+    if (e < n_pairs) {
+      const int i = i_min + e / G, h = g * G + e % G;
+      const RowKeys rk = row_keys(a, i + shift, L);
+      const bool sees = j <= rk.hi && (j >= rk.lo || j < rk.n_sink);
+      if (sees) {
+        const size_t row = (size_t)(q0 + i) * a.hq + h;
+        const T *q = (const T *)a.q + row * D, *dout = (const T *)a.dout + row * D, *o = (const T *)a.out + row * D;
+        float qk = 0.f, dov = 0.f, doo = 0.f;
+        for (int d = 0; d < D; ++d) {
+          const float dd = ld(dout + d);
+          qk = fmaf(ld(q + d), ks[d], qk);
+          dov = fmaf(dd, vs[d], dov);
+          doo = fmaf(dd, ld(o + d), doo);
+        }
+        p = expf(a.softmax_scale * qk - a.lse[row]);
+        ds = p * (dov - doo);
+      }
+    }
+    const int np = min(kWave, n_pairs - base);
+    for (int u = 0; u < np; ++u) {
+      const float pu = __shfl(p, u, kWave), dsu = __shfl(ds, u, kWave);
+      if (pu == 0.f && dsu == 0.f) continue;          // wave-uniform (shuffled values)
+      const int i = i_min + (base + u) / G, h = g * G + (base + u) % G;
+      const size_t row = (size_t)(q0 + i) * a.hq + h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = lane + r * kWave;
+        if (d < D) {
+          dv[r] = fmaf(pu, ld((const T *)a.dout + row * D + d), dv[r]);
+          dk[r] = fmaf(dsu, ld((const T *)a.q + row * D + d), dk[r]);
+        }
+      }
+    }
+  }
+  const size_t orow = ((size_t)a.key_offsets[s] + j) * hkv + g;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int d = lane + r * kWave;
+    if (d < D) {
+      a.dk[orow * D + d] = a.softmax_scale * dk[r];
+      a.dv[orow * D + d] = dv[r];
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const BackwardArgs &a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (a.total_q > 0)
+    e = launch(attn_dq_kernel<T>, dim3((unsigned)a.total_q, (unsigned)a.hq), dim3(kWave), 0, stream, a);
+  if (e != hipSuccess || a.max_kv_len == 0) return e;
+  const long long blocks = (long long)a.num_seqs * a.max_kv_len;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  return launch(attn_dkv_kernel<T>, dim3((unsigned)blocks, (unsigned)a.cache.num_kv_heads), dim3(kWave), 0,
+                stream, a);
+}
+
+}  // namespace
+
+hipError_t launch_attn_backward(const BackwardArgs &a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  ProfileScope prof("attn_backward", stream);
+  if (a.q_dtype == NK_F32) return launch_t<float>(a, stream);
+  return launch_t<bf16_t>(a, stream);
+}
+
+}  // namespace nk

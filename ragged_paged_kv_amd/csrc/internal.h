@@ -80,7 +80,22 @@ struct PackArgs {
   int32_t num_seqs, max_key_len;
 };
 
+// Gradients of the attention: dq [total_q][hq][D], dk/dv [rows][Hkv][D]
+// (segment s's key j at row key_offsets[s] + j), all float32
+struct BackwardArgs {
+  const void *q, *out, *dout;          // q_dtype [total_q][hq][D]
+  int32_t q_dtype;
+  const float *lse;                    // [total_q][hq]
+  const int32_t *q_offsets, *kv_lens, *key_offsets;
+  nk_paged_kv_t cache;
+  float softmax_scale;
+  int32_t window_left, window_right, sink_keys;
+  float *dq, *dk, *dv;
+  int32_t num_seqs, total_q, max_kv_len, hq;
+};
+
 hipError_t launch_rope_write(const RopeArgs &a, hipStream_t stream);
+hipError_t launch_attn_backward(const BackwardArgs &a, hipStream_t stream);
 hipError_t launch_attention_pack(const PackArgs &a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);

@@ -22,7 +22,7 @@ NK_OK, NK_ERR_INVALID_ARG, NK_ERR_UNSUPPORTED, NK_ERR_WORKSPACE, NK_ERR_DEVICE =
 EXPORTS = ("nk_rope_qk_write_paged", "nk_rope_qk_write_paged_mrope", "nk_ragged_paged_attention", "nk_ragged_paged_attention_band",
            "nk_ragged_paged_attention_workspace_size", "nk_ragged_paged_attention_split_tokens",
            "nk_attention_lse_merge", "nk_status_string", "nk_version", "nk_profile_enable",
-           "nk_profile_reset", "nk_profile_read", "nk_attention_pack")
+           "nk_profile_reset", "nk_profile_read", "nk_attention_pack", "nk_ragged_paged_attention_backward")
 
 
 class NKError(RuntimeError):
@@ -75,6 +75,9 @@ def lib():
         L.nk_version.restype = ctypes.c_int
         L.nk_attention_pack.argtypes = [vp, vp, i32, vp, vp, cache_p, vp, i32, i32, vp]
         L.nk_attention_pack.restype = ctypes.c_int
+        L.nk_ragged_paged_attention_backward.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, i32, i32, vp, vp, vp,
+                                                         vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        L.nk_ragged_paged_attention_backward.restype = ctypes.c_int
         L.nk_profile_enable.argtypes = [ctypes.c_int]
         L.nk_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
@@ -319,7 +322,35 @@ def attention_pack(k, v, key_offsets, key_lengths=None, page_size=16, cache_dtyp
     return cache, kv_lens, int(max_key_len)
 
 
-PROFILE_FAMILIES = ("rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge", "attention_pack")
+def ragged_paged_attention_backward(q, q_offsets, kv_lens, cache, softmax_scale, max_kv_len, out, dout, lse,
+                                    key_offsets, num_key_rows, window_left=-1, window_right=0, sink_keys=0,
+                                    dq=None, dk=None, dv=None, stream=None):
+    """Gradients (dq [T, Hq, D], dk, dv [num_key_rows, Hkv, D], float32) of
+    ragged_paged_attention from its out, lse and the output gradient dout;
+    segment s's key j has its dk, dv at row key_offsets[s] + j."""
+    T, hq, d = q.shape
+    B = kv_lens.shape[0]
+    _i32(q_offsets, "q_offsets"), _i32(kv_lens, "kv_lens"), _i32(key_offsets, "key_offsets")
+    _dev(q, q_offsets, kv_lens, out, dout, lse, key_offsets, cache.k_pages, dq, dk, dv)
+    if out.shape != q.shape or dout.shape != q.shape or out.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("out and dout must match q")
+    if lse.shape != (T, hq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [T, Hq]")
+    f = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(T, hq, d, **f) if dq is None else dq
+    dk = torch.empty(num_key_rows, cache.num_kv_heads, d, **f) if dk is None else dk
+    dv = torch.empty(num_key_rows, cache.num_kv_heads, d, **f) if dv is None else dv
+    c = cache.struct()
+    st = lib().nk_ragged_paged_attention_backward(
+        _ptr(q), _dtype_code(q.dtype), _ptr(q_offsets), _ptr(kv_lens), ctypes.byref(c), float(softmax_scale),
+        int(window_left), int(window_right), int(sink_keys), _ptr(out), _ptr(dout), _ptr(lse), _ptr(key_offsets),
+        _ptr(dq), _ptr(dk), _ptr(dv), B, T, int(max_kv_len), hq, _stream(stream))
+    _check(st, "nk_ragged_paged_attention_backward")
+    return dq, dk, dv
+
+
+PROFILE_FAMILIES = ("rope_write", "attn_decode", "attn_prefill", "attn_f32", "lse_merge", "attention_pack",
+                    "attn_backward")
 
 
 def profile_enable(on=True, families=None):

@@ -157,7 +157,7 @@ def test_profile_api_without_gpu(L):
     assert L.nk_profile_enable(0) == 0
     ms, n = nk.profile_read("attn_decode")
     assert n == 0 and ms == 0.0
-    assert L.nk_profile_enable(1 << 6) == nk.NK_ERR_INVALID_ARG       # no such family
+    assert L.nk_profile_enable(1 << 7) == nk.NK_ERR_INVALID_ARG       # no such family
     assert L.nk_profile_enable(-1) == nk.NK_ERR_INVALID_ARG
     nk.profile_enable(True, ["attn_decode", "lse_merge"])             # host-side only, no launch
     nk.profile_enable(False)
@@ -205,3 +205,29 @@ def test_pack_validation(L):
     assert pack(L, _cache(dtype=nk.NK_E4M3), in_dtype=nk.NK_F32) == nk.NK_ERR_UNSUPPORTED
     assert pack(L, _cache(head_dim=96)) == nk.NK_ERR_UNSUPPORTED
     assert pack(L, c, num_seqs=0) == nk.NK_OK                         # nothing to pack: no launch
+
+
+def backward(L, cache, **kw):
+    a = dict(q=1, q_dtype=nk.NK_BF16, q_offsets=1, kv_lens=1, scale=0.1, wl=-1, wr=0, sinks=0, out=1, dout=1,
+             lse=1, key_offsets=1, dq=1, dk=1, dv=1, num_seqs=1, total=4, max_kv=64, hq=4)
+    a.update(kw)
+    return L.nk_ragged_paged_attention_backward(
+        a["q"], a["q_dtype"], a["q_offsets"], a["kv_lens"], None if cache is None else ctypes.byref(cache),
+        a["scale"], a["wl"], a["wr"], a["sinks"], a["out"], a["dout"], a["lse"], a["key_offsets"], a["dq"],
+        a["dk"], a["dv"], a["num_seqs"], a["total"], a["max_kv"], a["hq"], None)
+
+
+def test_backward_validation(L):
+    c = _cache()
+    assert backward(L, c, total=-1) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, c, wr=-2) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, c, sinks=-1) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, c, scale=float("nan")) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, None) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, c, hq=5) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, _cache(dtype=nk.NK_E4M3)) == nk.NK_ERR_UNSUPPORTED
+    assert backward(L, c, q_dtype=nk.NK_F32) == nk.NK_ERR_UNSUPPORTED
+    assert backward(L, c, lse=None) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, c, key_offsets=None) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, c, dk=None) == nk.NK_ERR_INVALID_ARG
+    assert backward(L, c, num_seqs=0, total=0) == nk.NK_OK
