@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s
 FLUSH_BYTES = 1 << 30
 HIP_EVENT_NO_SYSTEM_FENCE = 0x20000000     # hipEventDisableSystemFence
 
@@ -54,6 +55,7 @@ DESCR = {
     "prefill_mrope_bf16": "the ragged prefill batch with M-RoPE: three position streams over 16/24/24 pairs",
     "prefill_prope_bf16": "the ragged prefill batch with p-RoPE: rotate-half pairs over the head, a quarter rotated",
     "mixed_sinks_bf16": "the sliding-window mixed batch with 4 sink keys beside the window (StreamingLLM)",
+    "prefill_backward_bf16": "gradients (dq, dk, dv) of the ragged causal prefill batch from its forward's out and lse",
     "pack_bf16": "attention_pack of the decode batch's keys (32 slots with 64 spare rows each), Hkv8, D128, page16",
 }
 # kernels whose launches carry timing events inside the timed region
@@ -330,8 +332,72 @@ def measure_pack(steps, warmup, flush):
     return res
 
 
+def measure_backward(steps, warmup, flush):
+    """nk_ragged_paged_attention_backward on the ragged prefill batch: its
+    forward (RoPE + append + attention) once, a seeded output gradient, then
+    the timed gradient calls.  Algorithmic flops: 10 D per (row, head, visible
+    key) -- the score recomputation, dO V^T, dV, dQ and dK products."""
+    import numpy as np
+    import torch
+
+    from ragged_paged_kv_amd import nk
+    from synth import work
+
+    st = prepare("prefill_bf16")
+    w = st.w
+    nk.rope_qk_write_paged(st.q, st.k, st.v, st.q_offsets, st.kv_lens, st.freqs, st.cache, w.rotary_dim,
+                           w.rope_layout, position_ids=st.pos, q_out=st.q_out)
+    nk.ragged_paged_attention(st.q_out, st.q_offsets, st.kv_lens, st.cache, w.softmax_scale, w.max_q_len,
+                              w.max_kv_len, w.window_left, out=st.out, lse=st.lse)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dout = torch.randn(st.q.shape, generator=gen, device="cuda").to(torch.bfloat16)
+    key_offsets = np.concatenate([[0], np.cumsum(w.kv_lens)]).astype(np.int32)
+    d_koffs = torch.from_numpy(key_offsets).cuda()
+    rows = int(key_offsets[-1])
+    dq = torch.empty(w.total_q, w.num_q_heads, w.head_dim, dtype=torch.float32, device="cuda")
+    dk = torch.empty(rows, w.num_kv_heads, w.head_dim, dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+
+    def step():
+        nk.ragged_paged_attention_backward(st.q_out, st.q_offsets, st.kv_lens, st.cache, w.softmax_scale,
+                                           w.max_kv_len, st.out, dout, st.lse, d_koffs, rows, w.window_left,
+                                           dq=dq, dk=dk, dv=dv)
+
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    nk.profile_reset()
+    nk.profile_enable(True, ["attn_backward"])
+    evs = [(StepEvent(), StepEvent()) for _ in range(steps)]
+    for i in range(steps):
+        if scratch is not None:
+            torch.sum(scratch, dim=0, out=sink)
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    nk.profile_enable(False)
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    tot, n = nk.profile_read("attn_backward")
+    flops = 10 * w.head_dim * w.num_q_heads * work.prefill_pairs(w)
+    ms = times[len(times) // 2]
+    res = {"workload": "prefill_backward_bf16", "descr": DESCR["prefill_backward_bf16"], "ms_per_step": ms,
+           "ms_min": times[0], "ms_max": times[-1],
+           "kernels": {"attn_backward": {"avg_ms": tot / n, "launches": n}},
+           "kernels_timed_in_region": ["attn_backward"], "backward_flops": flops,
+           "backward_TFLOPs_kernel": flops / (tot / n) / 1e9}
+    del scratch, st
+    return res
+
+
 def run_workload(name, steps, warmup, flush):
     import torch
+    if name == "prefill_backward_bf16":
+        res = measure_backward(steps, warmup, flush)
+        torch.cuda.empty_cache()
+        return res
     if name == "pack_bf16":
         res = measure_pack(steps, warmup, flush)
         torch.cuda.empty_cache()
@@ -622,6 +688,9 @@ def main():
     extra = {}
     for n, r in results.items():
         e = {"ms_per_step": r["ms_per_step"], "kernels": r["kernels"], "split_tokens": r.get("split_tokens")}
+        if r.get("backward_TFLOPs_kernel"):
+            e["backward_TFLOPs_kernel"] = r["backward_TFLOPs_kernel"]
+            e["backward_fp32_valu_frac"] = r["backward_TFLOPs_kernel"] / FP32_VALU_PEAK_TFLOPS
         if r.get("pack_GBps_kernel"):
             e["pack_GBps_kernel"] = r["pack_GBps_kernel"]
             e["pack_hbm_frac"] = r["pack_GBps_kernel"] / HBM_PEAK_GBS

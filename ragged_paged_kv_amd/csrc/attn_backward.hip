@@ -31,6 +31,19 @@ namespace {
 
 template <typename T> NK_DEVICE float ld(const T *p) { return (float)*p; }
 
+// 8 consecutive elements (16-byte aligned) as float32: one 16-byte load for
+// bf16, two for float32
+NK_DEVICE void ld8(const bf16_t *p, float *x) {
+  const bf16x8_t v = *(const bf16x8_t *)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+NK_DEVICE void ld8(const float *p, float *x) {
+  const f32x4_t a = *(const f32x4_t *)p, b = *(const f32x4_t *)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+
 // Element (dim d, key t of its page) of a K or V page-head block (include/nk.h
 // layouts; NV = 4 / element bytes for V's 16-byte runs).
 template <typename T> NK_DEVICE size_t k_elem(int d, int t, int P) {
@@ -91,10 +104,13 @@ __global__ void __launch_bounds__(64) attn_dq_kernel(BackwardArgs a) {
       const int key = rk.key(base + lane);
       const size_t blk = ((size_t)pt[key / P] * hkv + g) * P * D;
       float qk = 0.f, dv = 0.f;
-      for (int d = 0; d < D; ++d) {
-        qk = fmaf(qs[d], ld(kp + blk + k_elem<T>(d, key % P, P)), qk);
-        dv = fmaf(dos[d], ld(vp + blk + v_elem<T>(d, key % P, D)), dv);
+      for (int d0 = 0; d0 < D; d0 += 8) {                // a key's 8 dims of one block are contiguous
+        float kx[8];
+        ld8(kp + blk + k_elem<T>(d0, key % P, P), kx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qk = fmaf(qs[d0 + e], kx[e], qk);
       }
+      for (int d = 0; d < D; ++d) dv = fmaf(dos[d], ld(vp + blk + v_elem<T>(d, key % P, D)), dv);
       const float p = expf(a.softmax_scale * qk - lse);
       ds = p * (dv - di);
     }
@@ -154,11 +170,17 @@ __global__ void __launch_bounds__(64) attn_dkv_kernel(BackwardArgs a) {
         const size_t row = (size_t)(q0 + i) * a.hq + h;
         const T *q = (const T *)a.q + row * D, *dout = (const T *)a.dout + row * D, *o = (const T *)a.out + row * D;
         float qk = 0.f, dov = 0.f, doo = 0.f;
-        for (int d = 0; d < D; ++d) {
-          const float dd = ld(dout + d);
-          qk = fmaf(ld(q + d), ks[d], qk);
-          dov = fmaf(dd, vs[d], dov);
-          doo = fmaf(dd, ld(o + d), doo);
+        for (int d0 = 0; d0 < D; d0 += 8) {
+          float qx[8], dx[8], ox[8];
+          ld8(q + d0, qx);
+          ld8(dout + d0, dx);
+          ld8(o + d0, ox);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            qk = fmaf(qx[e], ks[d0 + e], qk);
+            dov = fmaf(dx[e], vs[d0 + e], dov);
+            doo = fmaf(dx[e], ox[e], doo);
+          }
         }
         p = expf(a.softmax_scale * qk - a.lse[row]);
         ds = p * (dov - doo);
