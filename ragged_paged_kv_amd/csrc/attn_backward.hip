@@ -18,7 +18,7 @@
 //     take 64 visible keys at a time, each lane loading its key's K and V once
 //     and computing q.k and dO.v for every head, then lanes over head
 //     dimensions accumulate dS_j k_j;
-//   * dK/dV: one wave per (4 consecutive keys of a segment, KV head); lanes
+//   * dK/dV: one wave per (8 consecutive keys of a segment, KV head); lanes
 //     take 64 (row, head) pairs of the rows that see one of the keys, each
 //     loading the pair's rows once and computing dO.O and, per key, q.k and
 //     dO.v, then lanes over dimensions accumulate P dO and dS q per key.
@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(64) attn_dq_kernel(BackwardArgs a) {
 
 // dK/dV of KB consecutive keys of one segment and KV head per wave: each
 // (row, head) pair's q, dO and O rows are loaded once for all KB keys.
-constexpr int kDkvKeys = 4;
+constexpr int kDkvKeys = 8;
 
 template <typename T>
 __global__ void __launch_bounds__(64) attn_dkv_kernel(BackwardArgs a, int blocks_per_seq) {
