@@ -107,3 +107,48 @@ def test_pack_parity(name):
     og = out.cpu().numpy().astype(np.float64) if cdt == "f32" else gu.host_values(out, "bf16")
     gu.check_close(og, out_o, tol, "out")
     gu.check_close(lse.cpu().numpy(), lse_o, tol, "lse")
+
+
+def test_pack_attention_backward_rows():
+    """Pack with spare room, attention under a window with sink keys, then
+    the gradients with dk/dv at the pack's input rows: rows of kept keys
+    match the oracle; the spare rows past each kept length are untouched."""
+    slots, kept_in, q_lens, hq, hkv, d, P = [70, 203, 1, 300], [65, 200, 1, 250], [65, 37, 1, 1], 8, 2, 128, 16
+    wl, sinks = 40, 4
+    gu.say("pack + attention + backward rows")
+    rng = np.random.default_rng(2024)
+    offs, k, v, dk_in, dv_in = _inputs("bwd", slots, kept_in, hkv, d, "bf16", rng)
+    d_offs = torch.from_numpy(offs).cuda()
+    cache, kv_lens, max_len = nk.attention_pack(dk_in, dv_in, d_offs, torch.tensor(kept_in, dtype=torch.int32).cuda(),
+                                                page_size=P)
+    q_offsets = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    T = int(q_offsets[-1])
+    qb = formats.bf16_bits(formats.bf16_round(rng.standard_normal((T, hq, d))))
+    gb = formats.bf16_bits(formats.bf16_round(rng.standard_normal((T, hq, d))))
+    dq_t = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16)
+    dout = torch.from_numpy(gb.view(np.int16)).cuda().view(torch.bfloat16)
+    scale = 1.0 / np.sqrt(d)
+    d_qoffs = torch.from_numpy(q_offsets).cuda()
+    lse = torch.empty(T, hq, dtype=torch.float32, device="cuda")
+    out, lse = nk.ragged_paged_attention(dq_t, d_qoffs, kv_lens, cache, scale, max(q_lens), max_len, wl, lse=lse,
+                                         sink_keys=sinks)
+    rows = int(offs[-1])
+    dk = torch.full((rows, hkv, d), 7.0, dtype=torch.float32, device="cuda")
+    dv = torch.full((rows, hkv, d), 7.0, dtype=torch.float32, device="cuda")
+    dq, dk, dv = nk.ragged_paged_attention_backward(dq_t, d_qoffs, kv_lens, cache, scale, max_len, out, dout, lse,
+                                                    d_offs, rows, wl, 0, sinks, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+
+    o_cache, o_table, kept = o_pack.attention_pack(k, v, offs, kept_in, "bf16", P)
+    dq_o, dk_o, dv_o = o_attn.ragged_paged_attention_backward(formats.bf16_value(qb), q_offsets, kept, o_cache,
+                                                              o_table, scale, formats.bf16_value(gb), wl, 0, sinks)
+    dqg, dkg, dvg = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    sc = max(1.0, float(np.max(np.abs(dq_o))))
+    gu.check_close(dqg / sc, dq_o / sc, 2e-2, "dq")
+    for s in range(len(slots)):
+        a, n = int(offs[s]), int(kept[s])
+        sk = max(1.0, float(np.max(np.abs(dk_o[s])))) if n else 1.0
+        sv = max(1.0, float(np.max(np.abs(dv_o[s])))) if n else 1.0
+        gu.check_close(dkg[a:a + n] / sk, dk_o[s] / sk, 2e-2, f"dk segment {s}")
+        gu.check_close(dvg[a:a + n] / sv, dv_o[s] / sv, 2e-2, f"dv segment {s}")
+        assert np.all(dkg[a + n:int(offs[s + 1])] == 7.0) and np.all(dvg[a + n:int(offs[s + 1])] == 7.0)
