@@ -2,7 +2,7 @@
  * nk.h -- ragged paged attention with fused RoPE + KV append, for AMD
  * Instinct MI355X (gfx950).  C ABI of libnk.so.
  *
- * Three operations:
+ * Three operations on the forward path:
  *
  *   nk_rope_qk_write_paged     rotate Q and K with a (cos, sin) table, write
  *                              the rotated Q out and append rotated K and
@@ -19,6 +19,13 @@
  *                              log-sum-exp (Algenta "Attention variant kernels",
  *                              "Flash attention's running state reproduces the
  *                              same softmax").
+ *
+ * Beside them: nk_ragged_paged_attention_band (any band of keys before and
+ * after a row, plus attention-sink keys), nk_attention_pack (ragged K/V
+ * token rows packed into the paged cache, NumKong attention_pack),
+ * nk_ragged_paged_attention_backward (query, key and value gradients,
+ * NumKong attention_packed_gradients) and nk_rope_qk_write_paged_mrope
+ * (multimodal RoPE sections).
  *
  * Conventions for every call (after the NumKong python page, "GPU Tensors
  * through DLPack": no verb allocates, each GPU call queues its launches on
