@@ -492,7 +492,7 @@ template <> NK_DEVICE void store_v1<kCacheBF16>(uint8_t *p, double x) { *(bf16_t
 template <> NK_DEVICE void store_v1<kCacheE4M3>(uint8_t *p, double x) { *p = (uint8_t)(fp8x2(x, 0.0) & 0xffu); }
 
 // One work-group per (segment, page of its pack, kv head): every 8-dim unit
-// of the page's kept tokens, K and V.  A token's D/8 units are consecutive
+// of the page's kept tokens, K and V (V through LDS, stored as whole runs).  A token's D/8 units are consecutive
 // lanes (D/8 divides 64), so the e4m3 absmax is a lane-group reduction.
 template <typename TIn, int CACHE>
 __global__ void __launch_bounds__(256) pack_kernel(PackArgs a, int pages_per_seq) {
@@ -505,6 +505,8 @@ __global__ void __launch_bounds__(256) pack_kernel(PackArgs a, int pages_per_seq
   const size_t ph = (size_t)page * hkv + g;
   uint8_t *kph = (uint8_t *)a.cache.k_pages + ph * P * (size_t)D * esz;
   uint8_t *vph = (uint8_t *)a.cache.v_pages + ph * P * (size_t)D * esz;
+  // V is assembled in LDS in its page-block order, then leaves as 16-byte runs
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[32 * 256 * esz];
   const int upt = D / 8;
   const int row0 = a.key_offsets[s] + i * P;
   for (int u0 = 0; u0 < P * upt; u0 += 256) {          // uniform trip count: shuffles see every lane
@@ -534,8 +536,26 @@ __global__ void __launch_bounds__(256) pack_kernel(PackArgs a, int pages_per_seq
         store_k8<CACHE>(kph + k_index<CACHE>(8 * c, t, P) * esz, 0, x);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) store_v1<CACHE>(vph + v_index<CACHE>(8 * c + e, t, D) * esz, x[e]);
+        for (int e = 0; e < 8; ++e) store_v1<CACHE>(vtile + v_index<CACHE>(8 * c + e, t, D) * esz, x[e]);
       }
+    }
+  }
+  __syncthreads();
+  // a run holds 4 consecutive slots (t0 .. t0+3) of 4*NV elements: whole
+  // runs of kept slots leave as one store; a run cut by the segment's last
+  // kept key (the last page only) is written element by element
+  constexpr int NV = v_nv<CACHE>();
+  const int kept = min(P, len - i * P);
+  const int runs = P * D / (4 * NV);
+  for (int r = (int)threadIdx.x; r < runs; r += 256) {
+    const int t0 = 16 * ((r / 64) / (D / (16 * NV))) + 4 * ((r % 64) / 16);
+    if (t0 >= kept) continue;
+    if (t0 + 3 < kept) {
+      *(u32x4_t *)(vph + (size_t)r * 16) = *(const u32x4_t *)(vtile + r * 16);
+    } else {
+      for (int k = 0; k < 4 * NV; ++k)
+        if (t0 + (k & 3) < kept)
+          for (int b = 0; b < esz; ++b) vph[(size_t)r * 16 + k * esz + b] = vtile[r * 16 + k * esz + b];
     }
   }
 }
