@@ -133,9 +133,9 @@ typedef struct nk_paged_kv {
  * nk_rope_qk_write_paged -- fused RoPE on Q and K plus append of K/V.
  *
  * Defined by the Mojo docs page generic_fused_qk_rope_bshd_paged_ragged_
- * kernel_api ("Applies fused rotary position embedding to Q and K, updating
- * keys in the paged KV cache"; Args input_row_offsets, freqs_cis,
- * position_ids, output; parameter `interleaved`), extended to append V.
+ * kernel_api (one fused pass rotates Q and K and writes the rotated keys into
+ * the paged cache; Args input_row_offsets, freqs_cis, position_ids, output;
+ * parameter `interleaved`), extended to append V.
  *
  * For token t = q_offsets[s] + i (i < q_len(s) = q_offsets[s+1]-q_offsets[s]):
  *   slot  j   = kv_lens[s] - q_len(s) + i      (kv_lens counts keys AFTER
@@ -305,10 +305,10 @@ const char *nk_status_string(int status);
  * nk_attention_pack -- pack ragged K/V token matrices into the paged cache.
  *
  * NumKong matrix-kernels page, "Attention with a Pre-Packed KV-Cache" and
- * attention_pack: the keys and values of all segments are packed once and
- * scored against many queries; segments of different lengths share the
- * pack, addressed by cumulative key_offsets, and segment s keeps
- * key_lengths[s] keys (by default its whole slot) from row key_offsets[s].
+ * attention_pack (a pack built once, then read by many attention calls).
+ * Input rows key_offsets[s] .. key_offsets[s+1]-1 form segment s's slot;
+ * the first kept_s rows of the slot enter the pack, kept_s being
+ * key_lengths[s] or, when key_lengths is NULL, the slot's size.
  * The pack is this library's paged cache: attention over it is
  * nk_ragged_paged_attention (or _band) with kv_lens = kv_lens_out, the
  * queries aligned to the end of each segment's kept keys.

@@ -8,9 +8,9 @@ Definitions followed:
   align to the end of their segment's keys, so row r of q query rows over k
   keys sits at position r + k - q and sees keys from that position minus
   ``keys_before`` through that position plus ``keys_after``; ``keys_after=0``
-  is causal; ``keys_before = w - 1`` is a window of w keys; rows that see no
-  key come back as zeros; the forward also fills a (tokens, heads)
-  log-sum-exp.
+  is causal; ``keys_before = w - 1`` is a window of w keys; a row without a
+  visible key has an all-zero output; the forward also returns a
+  log-sum-exp per (token, head).
 * Algenta "Attention variant kernels", "A scalar reference, not a buffer
   kernel": the score is q.k / sqrt(d) (here an explicit ``softmax_scale``
   replaces 1/sqrt(d), as the aria_kernel ``attention_with_scale`` entry

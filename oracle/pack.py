@@ -2,11 +2,10 @@
 INFRASTRUCTURE).
 
 NumKong matrix-kernels page, "Attention with a Pre-Packed KV-Cache" and
-``attention_pack``: the K/V tokens of all segments are packed once and then
-scored against many queries; segments of different lengths share the pack,
-addressed by cumulative ``key_offsets`` (segment s's slot is rows
-key_offsets[s] .. key_offsets[s+1]-1), and segment s keeps
-``key_lengths[s]`` keys from row key_offsets[s] (by default the whole slot).
+``attention_pack``: one pack, built once, serves many attention calls.
+Segment s's input slot is rows key_offsets[s] .. key_offsets[s+1]-1; the
+first kept_s rows of it enter the pack, kept_s being ``key_lengths[s]``, or
+the slot's size when no lengths are given.
 
 The pack's layout is opaque on the page; here it is the library's paged
 cache (``paged``).  Readings taken where the page leaves a step open:

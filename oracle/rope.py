@@ -151,12 +151,3 @@ def rope_qk_write_paged(q, k, v, in_dtype, q_offsets, kv_lens, position_ids,
                           formats.storage_round(k_rot[t, h], cache.dtype),
                           formats.storage_round(v[t, h], cache.dtype))
     return q_out, out
-
-
-def rope_rotated_unrounded(x, positions, freqs, rotary_dim, layout):
-    """Rotated rows before any store rounding (float64), x [T, H, D]."""
-    freqs = np.asarray(freqs, dtype=np.float64)
-    positions = np.asarray(positions, dtype=np.int64)
-    cos = freqs[positions, :, 0][:, None, :]
-    sin = freqs[positions, :, 1][:, None, :]
-    return rotate(x, cos, sin, rotary_dim, layout)

@@ -67,7 +67,7 @@ struct RowKeys {
 NK_DEVICE RowKeys row_keys(const BackwardArgs &a, int p, int L) {
   RowKeys r;
   r.hi = band_hi(p, L, a.window_right);
-  r.lo = a.window_left < 0 ? 0 : max(0, p - a.window_left);
+  r.lo = band_lo(p, a.window_left);
   const int sinks = a.window_left < 0 ? 0 : a.sink_keys;
   r.n_sink = max(0, min(sinks, min(r.lo, r.hi + 1)));
   r.n = r.n_sink + max(0, r.hi - r.lo + 1);
@@ -200,9 +200,10 @@ __global__ void __launch_bounds__(64) attn_dkv_kernel(BackwardArgs a, int blocks
   // rows that may see a key of the block: hi >= j0 from i_min on, lo <= jl
   // up to i_max (no upper limit when a key of the block is a sink key); each
   // (pair, key) is checked exactly below
-  const int i_min = a.window_right < 0 ? 0 : max(0, j0 - a.window_right - shift);
+  const int i_min = a.window_right < 0 ? 0 : (int)max(0LL, (long long)j0 - a.window_right - shift);
   const bool sink = a.window_left >= 0 && j0 < a.sink_keys;
-  const int i_max = (a.window_left < 0 || sink) ? q_len - 1 : min(q_len - 1, jl + a.window_left - shift);
+  const int i_max = (a.window_left < 0 || sink) ? q_len - 1
+                                                 : (int)min((long long)q_len - 1, (long long)jl + a.window_left - shift);
   const int n_pairs = max(0, i_max - i_min + 1) * G;
   float dk[KB][4], dv[KB][4];
 #pragma unroll

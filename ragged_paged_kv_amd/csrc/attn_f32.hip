@@ -38,7 +38,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
   const int L = a.kv_lens[s];
   const int p = (t - q0) + L - q_len;
   const int hi = band_hi(p, L, a.window_right);
-  const int lo = a.window_left < 0 ? 0 : max(0, p - a.window_left);
+  const int lo = band_lo(p, a.window_left);
 
   const float *q = (const float *)a.q + ((size_t)t * a.hq + h) * D;
   for (int d = lane; d < D; d += kWave) qs[d] = q[d];

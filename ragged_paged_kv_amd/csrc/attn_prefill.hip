@@ -176,7 +176,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const int shift = L - q_len;                // row r sits at position r + shift
   const int r_last = min(r0 + BM, q_len) - 1;
   const int kmax_wg = band_hi(r_last + shift, L, a.window_right);
-  const int kmin_wg = a.window_left < 0 ? 0 : max(0, r0 + shift - a.window_left);
+  const int kmin_wg = band_lo(r0 + shift, a.window_left);
   if (kmax_wg < kmin_wg || L <= 0) {
     // no row of the group sees a key (q_len > kv_len): zeros, -inf
     for (int e = threadIdx.x; e < (r_last - r0 + 1) * GW * D; e += NT) {
@@ -201,13 +201,13 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const int my_row = rw + qcol;
   const bool row_valid = my_row < q_len;
   const int my_pos = my_row + shift;
-  const int my_lo = a.window_left < 0 ? 0 : max(0, my_pos - a.window_left);
+  const int my_lo = band_lo(my_pos, a.window_left);
   const int my_hi = band_hi(my_pos, L, a.window_right);
   // the wave's key range (over its valid rows)
   const bool wave_active = rw < q_len;
   const int w_rows_last = min(rw + 31, q_len - 1);
   const int wk_hi = band_hi(w_rows_last + shift, L, a.window_right);
-  const int wk_lo = a.window_left < 0 ? 0 : max(0, rw + shift - a.window_left);
+  const int wk_lo = band_lo(rw + shift, a.window_left);
 
   // ---- Q operand (B of the score product): lane holds Q[row][16kk + 8*half .. +8].
   // A negative scale is folded into Q's sign (exact), a zero scale into a
@@ -423,7 +423,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
         }
     }
     const bool mask = tile_base + BN - 1 > band_hi(rw + shift, L, a.window_right) ||
-                      (a.window_left >= 0 && tile_base < w_rows_last + shift - a.window_left);
+                      (a.window_left >= 0 && tile_base < band_lo(w_rows_last + shift, a.window_left));
     if (mask) {
       const int rel_hi = row_valid ? my_hi - tile_base - 8 * half : -1000000;
       const int rel_lo = my_lo - tile_base - 8 * half;
@@ -555,7 +555,7 @@ NK_DEVICE int item_tiles(const AttnArgs &a, int BM, int s, int qb) {
   const int r0 = qb * BM;
   const int r_last = min(r0 + BM, q_len) - 1;
   const int kmax = band_hi(r_last + shift, L, a.window_right);
-  const int kmin = a.window_left < 0 ? 0 : max(0, r0 + shift - a.window_left);
+  const int kmin = band_lo(r0 + shift, a.window_left);
   return (kmax < kmin || L <= 0) ? 0 : kmax / BN - kmin / BN + 1 + sink_tiles(a.sink_keys, kmin / BN, BN);
 }
 

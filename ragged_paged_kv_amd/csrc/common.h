@@ -72,11 +72,20 @@ NK_DEVICE float wave_sum(float v) {
 NK_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 NK_DEVICE float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Last key visible to a query at position p of a segment with L keys: p plus
-// the keys after it, or the segment's last key when those are unbounded
-// (-1) or reach past it.
+// Last key visible to a query at position p of a segment with L keys:
+// min(p + window_right, L - 1), or L - 1 when the right side is unbounded
+// (-1).  p may be negative (a row placed before the segment's first key);
+// the comparison is made without forming p + window_right, which could
+// overflow.
 NK_DEVICE int band_hi(int p, int L, int window_right) {
-  return (window_right < 0 || window_right >= L) ? L - 1 : min(p + window_right, L - 1);
+  if (window_right < 0 || p >= L - 1 - window_right) return L - 1;
+  return p + window_right;
+}
+
+// First key visible at position p: max(0, p - window_left), or 0 when the
+// left side is unbounded (-1); p - window_left is formed only when positive.
+NK_DEVICE int band_lo(int p, int window_left) {
+  return (window_left < 0 || p <= window_left) ? 0 : p - window_left;
 }
 
 // Split-KV chunks of a single-token row with L keys (its position L - 1):
@@ -90,7 +99,7 @@ struct DecodeChunks {
 NK_DEVICE DecodeChunks decode_chunks(int L, int window_left, int sink_keys, int split, int max_chunks) {
   DecodeChunks d;
   const int hi = L - 1;
-  d.lo = window_left < 0 ? 0 : max(0, hi - window_left);
+  d.lo = band_lo(hi, window_left);
   d.c0 = (d.lo / 32) * 32;
   d.sink_end = min(sink_keys, d.lo);
   d.n_band = L > 0 ? min((hi + 1 - d.c0 + split - 1) / split, max_chunks) : 1;

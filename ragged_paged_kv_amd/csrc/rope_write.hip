@@ -425,10 +425,10 @@ hipError_t launch_rope_write(const RopeArgs &a, hipStream_t stream) {
 
 // ------------------------------------------------------------------ packing
 // NumKong matrix-kernels page, "Attention with a Pre-Packed KV-Cache" and
-// attention_pack: ragged K/V token matrices are packed once into a cache that
-// attention then reads many times; segment s keeps key_lengths[s] keys (by
-// default its whole slot key_offsets[s] .. key_offsets[s+1]-1) from row
-// key_offsets[s].  The pack here is this library's paged cache: segment s
+// attention_pack.  Segment s's input slot is rows key_offsets[s] ..
+// key_offsets[s+1]-1, of which the first kept_s enter the pack (kept_s =
+// key_lengths[s], or the slot's size without lengths).  The pack here is
+// this library's paged cache: segment s
 // takes the next ceil(kept/P) pages after those of segments 0..s-1, its
 // table row lists them, and kv_lens_out[s] = kept.  The keys are stored as
 // they come (no rotation), rounded once to the cache type; e4m3 rows take

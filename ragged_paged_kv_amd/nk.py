@@ -276,9 +276,9 @@ def attention_lse_merge(partial_out, partial_lse, merge_offsets, out, lse_out=No
 
 def attention_pack(k, v, key_offsets, key_lengths=None, page_size=16, cache_dtype=None, max_key_len=None,
                    num_pages=None, stream=None):
-    """Pack ragged K/V rows [rows, Hkv, D] into a new paged cache: segment s
-    keeps ``key_lengths[s]`` keys (default: its whole slot) from row
-    ``key_offsets[s]``.  Returns (cache, kv_lens, max_key_len); attention
+    """Pack ragged K/V rows [rows, Hkv, D] into a new paged cache: the first
+    ``key_lengths[s]`` rows (all of them without lengths) of segment s's
+    rows ``key_offsets[s]`` .. ``key_offsets[s+1]`` - 1 enter the pack.  Returns (cache, kv_lens, max_key_len); attention
     over it is ``ragged_paged_attention(q, q_offsets, kv_lens, cache, ...)``.
     ``cache_dtype`` is "f32", "bf16" or "e4m3" (default: the input's type).
     When ``max_key_len`` or ``num_pages`` is not given it is read from the
@@ -327,7 +327,11 @@ def ragged_paged_attention_backward(q, q_offsets, kv_lens, cache, softmax_scale,
                                     dq=None, dk=None, dv=None, stream=None):
     """Gradients (dq [T, Hq, D], dk, dv [num_key_rows, Hkv, D], float32) of
     ragged_paged_attention from its out, lse and the output gradient dout;
-    segment s's key j has its dk, dv at row key_offsets[s] + j."""
+    segment s's key j has its dk, dv at row key_offsets[s] + j.  The library
+    writes only the rows of kept keys (key_offsets[s] .. + kv_lens[s] - 1);
+    when dk/dv are not given they are allocated zero-filled, so rows of keys
+    left out of the pack (a key nobody reads has zero gradient) come back as
+    zeros; caller-given dk/dv keep their contents in those rows."""
     T, hq, d = q.shape
     B = kv_lens.shape[0]
     _i32(q_offsets, "q_offsets"), _i32(kv_lens, "kv_lens"), _i32(key_offsets, "key_offsets")
@@ -338,8 +342,8 @@ def ragged_paged_attention_backward(q, q_offsets, kv_lens, cache, softmax_scale,
         raise ValueError("lse must be float32 [T, Hq]")
     f = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty(T, hq, d, **f) if dq is None else dq
-    dk = torch.empty(num_key_rows, cache.num_kv_heads, d, **f) if dk is None else dk
-    dv = torch.empty(num_key_rows, cache.num_kv_heads, d, **f) if dv is None else dv
+    dk = torch.zeros(num_key_rows, cache.num_kv_heads, d, **f) if dk is None else dk
+    dv = torch.zeros(num_key_rows, cache.num_kv_heads, d, **f) if dv is None else dv
     c = cache.struct()
     st = lib().nk_ragged_paged_attention_backward(
         _ptr(q), _dtype_code(q.dtype), _ptr(q_offsets), _ptr(kv_lens), ctypes.byref(c), float(softmax_scale),

@@ -32,3 +32,17 @@ def golden():
         with open(os.path.join(ROOT, "tests", "golden", name)) as f:
             return json.load(f)
     return load
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Max errors of the GPU parity runs against their tolerances, so that a
+    quiet (-q) run still shows each workload's margin."""
+    gu = sys.modules.get("tests.gpu_util")
+    rows = getattr(gu, "MARGINS", None) if gu else None
+    if not rows:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "parity margins (max abs error vs the oracle)")
+    for case, eo, el, tol in rows:
+        tr.write_line(f"{case:<58s} out {eo:.3e}  lse {el:.3e}  tol {tol:.0e}  "
+                      f"margin {tol / max(eo, el, 1e-30):.1f}x")

@@ -23,6 +23,15 @@ from ragged_paged_kv_amd import nk
 TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 6e-2}
 
 
+# (case, max |out error|, max |lse error|, tolerance) of the compared runs,
+# printed in the test run's terminal summary
+MARGINS = []
+
+
+def record_margin(case, err_out, err_lse, tol):
+    MARGINS.append((case, float(err_out), float(err_lse), float(tol)))
+
+
 def say(*a):
     print("[gpu]", *a, flush=True)
     sys.stdout.flush()

@@ -73,3 +73,44 @@ def test_backward_parity(name):
     e2 = _scaled_check(dkg, dk_ref, tol, "dk")
     e3 = _scaled_check(dvg, dv_ref, tol, "dv")
     gu.say(f"backward {name}: scaled errors dq {e1:.3g} dk {e2:.3g} dv {e3:.3g}")
+
+
+@pytest.mark.parametrize("after", [3, 10])
+def test_backward_rows_before_keys(after):
+    """Gradients with rows placed before the segment's first key (20 rows
+    over 8 keys): a row reaches keys only through its band's right side,
+    which starts at its own position also when it is as long as the segment
+    or longer (10 after: rows 2..11 see a prefix of the keys, rows 0, 1 none
+    and have zero dq)."""
+    w = synth.custom(q_lens=[20, 3], kv_lens=[8, 40], num_q_heads=4, num_kv_heads=2, head_dim=64,
+                     window_right=after, name="backward_rows_before_keys")
+    gu.say(f"backward rows before keys, after={after}")
+    d = gu.to_device(w)
+    rng = np.random.default_rng(8)
+    kp, vp = d["cache"].k_pages, d["cache"].v_pages
+    kp.copy_(torch.from_numpy(rng.standard_normal(tuple(kp.shape), dtype=np.float32)).to(kp))
+    vp.copy_(torch.from_numpy(rng.standard_normal(tuple(vp.shape), dtype=np.float32)).to(vp))
+    lse = torch.empty(w.total_q, w.num_q_heads, dtype=torch.float32, device="cuda")
+    out, lse = nk.ragged_paged_attention(d["q"], d["q_offsets"], d["kv_lens"], d["cache"], w.softmax_scale,
+                                         w.max_q_len, w.max_kv_len, w.window_left, lse=lse, window_right=after)
+    gb = formats.bf16_bits(formats.bf16_round(rng.standard_normal((w.total_q, w.num_q_heads, w.head_dim))))
+    dout = torch.from_numpy(gb.view(np.int16)).cuda().view(torch.bfloat16)
+    key_offsets = np.concatenate([[0], np.cumsum(w.kv_lens)]).astype(np.int32)
+    rows = int(key_offsets[-1])
+    dq, dk, dv = nk.ragged_paged_attention_backward(
+        d["q"], d["q_offsets"], d["kv_lens"], d["cache"], w.softmax_scale, w.max_kv_len, out, dout, lse,
+        torch.from_numpy(key_offsets).cuda(), rows, w.window_left, after, 0)
+    torch.cuda.synchronize()
+    from oracle.paged import PagedCache
+    cache_o = PagedCache.from_storage("bf16", kp.cpu().view(torch.int16).numpy().view(np.uint16),
+                                      vp.cpu().view(torch.int16).numpy().view(np.uint16))
+    q = formats.bf16_value(d["tokens"]["q"])
+    dq_o, dk_o, dv_o = o_attn.ragged_paged_attention_backward(q, w.q_offsets, w.kv_lens, cache_o, w.page_table,
+                                                              w.softmax_scale, formats.bf16_value(gb),
+                                                              w.window_left, after, 0)
+    dqg = dq.cpu().numpy()
+    _scaled_check(dqg, dq_o, 2e-2, "dq")
+    _scaled_check(dk.cpu().numpy(), np.concatenate(dk_o, axis=0), 2e-2, "dk")
+    _scaled_check(dv.cpu().numpy(), np.concatenate(dv_o, axis=0), 2e-2, "dv")
+    first_seen = max(0, 12 - after)
+    assert np.all(dqg[:first_seen] == 0.0)

@@ -52,6 +52,7 @@ def test_band_parity(name):
     e1 = gu.check_close(gu.host_values(out, w.in_dtype), out_o, tol, "out")
     e2 = gu.check_close(lse.cpu().numpy(), lse_o, tol, "lse")
     gu.say(f"band {name}: out err {e1:.3g} lse err {e2:.3g}")
+    gu.record_margin(f"band {name}", e1, e2, gu.tol_for(w))
 
 
 def test_band_zero_is_causal_bit_for_bit():
@@ -82,12 +83,14 @@ def test_band_zero_is_causal_bit_for_bit():
     assert np.array_equal(lse_b.cpu().numpy(), lse_c.cpu().numpy())
 
 
-@pytest.mark.parametrize("after", [5, -1])
+@pytest.mark.parametrize("after", [5, 8, 10, -1])
 def test_band_rows_before_keys(after):
     """20 new rows over 8 keys: rows 0..11 sit before the first key (outside
     the append's precondition, so attention alone on a generated cache).
     With keys after their position they reach the first keys (rows 7..11 with
-    5 after); with an unbounded right side every row sees all 8."""
+    5 after, 4..11 with 8 and 2..11 with 10: a right side as long as the
+    segment or longer still starts at the row's own position); with an
+    unbounded right side every row sees all 8."""
     w = synth.custom(q_lens=[20, 3], kv_lens=[8, 40], num_q_heads=2, num_kv_heads=1, head_dim=64,
                      window_right=after, name="band_rows_before_keys")
     gu.say(f"band rows before keys, after={after}")
@@ -109,6 +112,6 @@ def test_band_rows_before_keys(after):
     gu.check_close(og, out_o, 2e-2, "out")
     gu.check_close(lse.cpu().numpy(), lse_o, 2e-2, "lse")
     lg = lse.cpu().numpy()
-    first_seen = 0 if after < 0 else 12 - after          # first row whose band reaches key 0
+    first_seen = 0 if after < 0 else max(0, 12 - after)  # first row whose band reaches key 0
     assert np.all(np.isneginf(lg[:first_seen])) and np.all(og[:first_seen] == 0)
     assert np.all(np.isfinite(lg[first_seen:20]))

@@ -152,3 +152,42 @@ def test_pack_attention_backward_rows():
         gu.check_close(dkg[a:a + n] / sk, dk_o[s] / sk, 2e-2, f"dk segment {s}")
         gu.check_close(dvg[a:a + n] / sv, dv_o[s] / sv, 2e-2, f"dv segment {s}")
         assert np.all(dkg[a + n:int(offs[s + 1])] == 7.0) and np.all(dvg[a + n:int(offs[s + 1])] == 7.0)
+
+
+def test_pack_backward_default_gradient_buffers():
+    """Gradients into the binding's own dk/dv buffers, over a pack with spare
+    room: rows of kept keys match the oracle, rows past each kept length (keys
+    no row reads) are zeros."""
+    slots, kept_in, q_lens, hq, hkv, d, P = [40, 90, 17], [33, 90, 5], [33, 20, 1], 4, 2, 64, 16
+    gu.say("pack + backward into default buffers")
+    rng = np.random.default_rng(2025)
+    offs, k, v, dk_in, dv_in = _inputs("bwd_default", slots, kept_in, hkv, d, "bf16", rng)
+    d_offs = torch.from_numpy(offs).cuda()
+    cache, kv_lens, max_len = nk.attention_pack(dk_in, dv_in, d_offs, torch.tensor(kept_in, dtype=torch.int32).cuda(),
+                                                page_size=P)
+    q_offsets = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    T = int(q_offsets[-1])
+    qb = formats.bf16_bits(formats.bf16_round(rng.standard_normal((T, hq, d))))
+    gb = formats.bf16_bits(formats.bf16_round(rng.standard_normal((T, hq, d))))
+    q_t = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16)
+    dout = torch.from_numpy(gb.view(np.int16)).cuda().view(torch.bfloat16)
+    scale = 1.0 / np.sqrt(d)
+    d_qoffs = torch.from_numpy(q_offsets).cuda()
+    lse = torch.empty(T, hq, dtype=torch.float32, device="cuda")
+    out, lse = nk.ragged_paged_attention(q_t, d_qoffs, kv_lens, cache, scale, max(q_lens), max_len, lse=lse)
+    rows = int(offs[-1])
+    dq, dk, dv = nk.ragged_paged_attention_backward(q_t, d_qoffs, kv_lens, cache, scale, max_len, out, dout, lse,
+                                                    d_offs, rows)
+    torch.cuda.synchronize()
+    o_cache, o_table, kept = o_pack.attention_pack(k, v, offs, kept_in, "bf16", P)
+    _, dk_o, dv_o = o_attn.ragged_paged_attention_backward(formats.bf16_value(qb), q_offsets, kept, o_cache,
+                                                           o_table, scale, formats.bf16_value(gb), -1, 0, 0)
+    dkg, dvg = dk.cpu().numpy(), dv.cpu().numpy()
+    assert np.all(np.isfinite(dkg)) and np.all(np.isfinite(dvg))
+    for s in range(len(slots)):
+        a, n = int(offs[s]), int(kept[s])
+        sk = max(1.0, float(np.max(np.abs(dk_o[s])))) if n else 1.0
+        sv = max(1.0, float(np.max(np.abs(dv_o[s])))) if n else 1.0
+        gu.check_close(dkg[a:a + n] / sk, dk_o[s] / sk, 2e-2, f"dk segment {s}")
+        gu.check_close(dvg[a:a + n] / sv, dv_o[s] / sv, 2e-2, f"dv segment {s}")
+        assert np.all(dkg[a + n:int(offs[s + 1])] == 0.0) and np.all(dvg[a + n:int(offs[s + 1])] == 0.0)

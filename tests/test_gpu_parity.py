@@ -77,6 +77,7 @@ def test_parity_case(name):
            f"G={w.num_q_heads // w.num_kv_heads} cache={w.cache_dtype}")
     e1, e2, _, _ = _run_and_compare(w)
     gu.say(f"case {name}: out err {e1:.3g} lse err {e2:.3g}")
+    gu.record_margin(f"parity {name}", e1, e2, gu.tol_for(w))
 
 
 @pytest.mark.parametrize("split", [32, 96, 512, 0])

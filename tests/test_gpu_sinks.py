@@ -54,6 +54,7 @@ def test_sink_parity(name):
     e1 = gu.check_close(gu.host_values(out, w.in_dtype), out_o, tol, "out")
     e2 = gu.check_close(lse.cpu().numpy(), lse_o, tol, "lse")
     gu.say(f"sinks {name}: out err {e1:.3g} lse err {e2:.3g}")
+    gu.record_margin(f"sinks {name}", e1, e2, gu.tol_for(w))
 
 
 @pytest.mark.parametrize("split", [128, 256])
