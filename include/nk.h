@@ -258,6 +258,33 @@ int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t
                                    int32_t kv_split_tokens, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/*
+ * nk_ragged_paged_attention_noalloc -- nk_ragged_paged_attention_band without
+ * a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The split-KV partials and the prefill work list live in a
+ * static device array of NK_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * device, held from the first call on that device until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); on its first call on a device it looks the array's address up
+ * and clears it with a fill kernel on `stream`.
+ *
+ * Every argument, result and error is that of nk_ragged_paged_attention_band;
+ * a call whose nk_ragged_paged_attention_workspace_size exceeds
+ * NK_NOALLOC_SCRATCH_BYTES returns NK_ERR_WORKSPACE before launching
+ * anything.  All calls on one device share its array and it keeps the last
+ * call's contents: calls that may overlap on one device (several streams or
+ * host threads without ordering between them) race and must be serialised
+ * by the caller.
+ */
+#define NK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int nk_ragged_paged_attention_noalloc(const void *q, int32_t q_dtype, const int32_t *q_offsets,
+                                      const int32_t *kv_lens, const nk_paged_kv_t *cache,
+                                      float softmax_scale, int32_t window_left, int32_t window_right,
+                                      int32_t sink_keys, void *out, float *lse, int32_t num_seqs,
+                                      int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                                      int32_t num_q_heads, int32_t kv_split_tokens, void *stream);
+
 /* Bytes of workspace nk_ragged_paged_attention needs for these scalars
  * (0 if none).  Pure host computation. */
 size_t nk_ragged_paged_attention_workspace_size(int32_t q_dtype, int32_t cache_dtype,

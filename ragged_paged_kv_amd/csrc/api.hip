@@ -198,6 +198,126 @@ ProfileScope::~ProfileScope() {
 
 }  // namespace nk
 
+// ------------------------------------------------------------------ static scratch
+// The allocation-free attention entry point keeps its split-KV partials and
+// prefill work list in this file-scope device array instead of a caller
+// workspace: every device the library runs on holds one copy, at its own
+// address, until the process ends.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, taken once per
+// device (with that device current) and kept per device below; kernels are
+// handed that address, never the symbol itself.
+static __device__ __align__(256) uint8_t scratch[NK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = NK_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+__global__ void __launch_bounds__(256) zero_scratch_kernel(uint4 *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+struct StaticScratch {
+  std::mutex mu;
+  void *ptr[kMaxDevices] = {};
+};
+StaticScratch &static_scratch_state() {
+  static StaticScratch st;
+  return st;
+}
+
+// This device's scratch address; on the first call for a device it is looked
+// up and the array cleared on `stream` (a fill kernel, so that the clearing
+// may also be captured into a graph).
+hipError_t static_scratch(hipStream_t stream, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  StaticScratch &st = static_scratch_state();
+  std::lock_guard<std::mutex> lock(st.mu);
+  if (!st.ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    hipLaunchKernelGGL(zero_scratch_kernel, dim3(1024), dim3(256), 0, stream, (uint4 *)ptr,
+                       kStaticScratchBytes / sizeof(uint4));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    st.ptr[dev] = ptr;
+  }
+  *out = st.ptr[dev];
+  return hipSuccess;
+}
+
+// The attention call behind both entry points: the caller's workspace, or
+// (use_static) this device's static scratch buffer.
+int attention_call(const void *q, int32_t q_dtype, const int32_t *q_offsets, const int32_t *kv_lens,
+                   const nk_paged_kv_t *cache, float softmax_scale, int32_t window_left, int32_t window_right,
+                   int32_t sink_keys, void *out, float *lse, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                   int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens, void *workspace,
+                   size_t workspace_bytes_given, bool use_static, void *stream) {
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0 || num_q_heads <= 0)
+    return NK_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1 || sink_keys < 0) return NK_ERR_INVALID_ARG;
+  if (kv_split_tokens < 0 || kv_split_tokens % 32) return NK_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return NK_ERR_INVALID_ARG;
+  int st = check_cache(cache);
+  if (st != NK_OK) return st;
+  if (num_q_heads % cache->num_kv_heads) return NK_ERR_INVALID_ARG;
+  const bool ok_types = (q_dtype == NK_F32 && cache->dtype == NK_F32) ||
+                        (q_dtype == NK_BF16 && (cache->dtype == NK_BF16 || cache->dtype == NK_E4M3));
+  if (!ok_types) return NK_ERR_UNSUPPORTED;
+  if (q_dtype == NK_BF16 && num_q_heads / cache->num_kv_heads > 64) return NK_ERR_UNSUPPORTED;
+  if (total_q == 0) return NK_OK;
+  if (num_seqs == 0) return NK_ERR_INVALID_ARG;
+  if (!q || !q_offsets || !kv_lens || !out) return NK_ERR_INVALID_ARG;
+
+  AttnArgs a{};
+  a.q = q; a.q_dtype = q_dtype; a.q_offsets = q_offsets; a.kv_lens = kv_lens;
+  a.cache = *cache; a.softmax_scale = softmax_scale;
+  a.window_left = window_left; a.window_right = window_right;
+  a.sink_keys = window_left < 0 ? 0 : sink_keys;     // a full left side already holds them
+  a.out = out; a.lse = lse;
+  a.num_seqs = num_seqs; a.total_q = total_q; a.max_q_len = max_q_len; a.max_kv_len = max_kv_len;
+  a.hq = num_q_heads;
+
+  if (q_dtype == NK_F32) return launch_attn_f32(a, (hipStream_t)stream) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
+
+  const WorkspacePlan wp = plan_workspace(q_dtype, cache->dtype, num_seqs, total_q, max_q_len,
+                                         max_kv_len, num_q_heads, cache->num_kv_heads,
+                                         cache->head_dim, window_left, kv_split_tokens);
+  hipStream_t s = (hipStream_t)stream;
+  if (use_static) {
+    if (wp.total > kStaticScratchBytes) return NK_ERR_WORKSPACE;
+    if (wp.total > 0) {
+      if (static_scratch(s, &workspace) != hipSuccess) return NK_ERR_DEVICE;
+      workspace_bytes_given = kStaticScratchBytes;
+    }
+  }
+  if (wp.total > 0 && (!workspace || workspace_bytes_given < wp.total)) return NK_ERR_WORKSPACE;
+  a.split_tokens = wp.split;
+  // grid and partials stride: the sink chunk only when there are sink keys
+  a.max_chunks = a.sink_keys > 0 ? wp.chunks : wp.band_chunks;
+  if (wp.partials) {
+    a.part_out = (float *)workspace;
+    a.part_lse = (float *)((char *)workspace + wp.part_lse);
+  }
+  if (wp.prefill) {
+    a.sched = (int32_t *)((char *)workspace + wp.sched);
+    a.sched_items_max = sched_items_max(num_seqs, total_q);
+  }
+  // prefill rows (q_len > 1) and decode rows (q_len == 1) run as separate
+  // launches on the same stream; each kernel skips the rows of the other kind
+  if (wp.prefill && launch_attn_prefill(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  if (launch_attn_decode(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  if (wp.partials && launch_decode_merge(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  return NK_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *nk_status_string(int status) {
@@ -307,55 +427,20 @@ int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t
                                    int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
                                    int32_t kv_split_tokens, void *workspace,
                                    size_t workspace_bytes_given, void *stream) {
-  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0 || num_q_heads <= 0)
-    return NK_ERR_INVALID_ARG;
-  if (window_left < -1 || window_right < -1 || sink_keys < 0) return NK_ERR_INVALID_ARG;
-  if (kv_split_tokens < 0 || kv_split_tokens % 32) return NK_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return NK_ERR_INVALID_ARG;
-  int st = check_cache(cache);
-  if (st != NK_OK) return st;
-  if (num_q_heads % cache->num_kv_heads) return NK_ERR_INVALID_ARG;
-  const bool ok_types = (q_dtype == NK_F32 && cache->dtype == NK_F32) ||
-                        (q_dtype == NK_BF16 && (cache->dtype == NK_BF16 || cache->dtype == NK_E4M3));
-  if (!ok_types) return NK_ERR_UNSUPPORTED;
-  if (q_dtype == NK_BF16 && num_q_heads / cache->num_kv_heads > 64) return NK_ERR_UNSUPPORTED;
-  if (total_q == 0) return NK_OK;
-  if (num_seqs == 0) return NK_ERR_INVALID_ARG;
-  if (!q || !q_offsets || !kv_lens || !out) return NK_ERR_INVALID_ARG;
+  return attention_call(q, q_dtype, q_offsets, kv_lens, cache, softmax_scale, window_left, window_right, sink_keys,
+                        out, lse, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads, kv_split_tokens,
+                        workspace, workspace_bytes_given, false, stream);
+}
 
-  AttnArgs a{};
-  a.q = q; a.q_dtype = q_dtype; a.q_offsets = q_offsets; a.kv_lens = kv_lens;
-  a.cache = *cache; a.softmax_scale = softmax_scale;
-  a.window_left = window_left; a.window_right = window_right;
-  a.sink_keys = window_left < 0 ? 0 : sink_keys;     // a full left side already holds them
-  a.out = out; a.lse = lse;
-  a.num_seqs = num_seqs; a.total_q = total_q; a.max_q_len = max_q_len; a.max_kv_len = max_kv_len;
-  a.hq = num_q_heads;
-
-  hipStream_t s = (hipStream_t)stream;
-  if (q_dtype == NK_F32) return launch_attn_f32(a, s) == hipSuccess ? NK_OK : NK_ERR_DEVICE;
-
-  const WorkspacePlan wp = plan_workspace(q_dtype, cache->dtype, num_seqs, total_q, max_q_len,
-                                         max_kv_len, num_q_heads, cache->num_kv_heads,
-                                         cache->head_dim, window_left, kv_split_tokens);
-  if (wp.total > 0 && (!workspace || workspace_bytes_given < wp.total)) return NK_ERR_WORKSPACE;
-  a.split_tokens = wp.split;
-  // grid and partials stride: the sink chunk only when there are sink keys
-  a.max_chunks = a.sink_keys > 0 ? wp.chunks : wp.band_chunks;
-  if (wp.partials) {
-    a.part_out = (float *)workspace;
-    a.part_lse = (float *)((char *)workspace + wp.part_lse);
-  }
-  if (wp.prefill) {
-    a.sched = (int32_t *)((char *)workspace + wp.sched);
-    a.sched_items_max = sched_items_max(num_seqs, total_q);
-  }
-  // prefill rows (q_len > 1) and decode rows (q_len == 1) run as separate
-  // launches on the same stream; each kernel skips the rows of the other kind
-  if (wp.prefill && launch_attn_prefill(a, s) != hipSuccess) return NK_ERR_DEVICE;
-  if (launch_attn_decode(a, s) != hipSuccess) return NK_ERR_DEVICE;
-  if (wp.partials && launch_decode_merge(a, s) != hipSuccess) return NK_ERR_DEVICE;
-  return NK_OK;
+int nk_ragged_paged_attention_noalloc(const void *q, int32_t q_dtype, const int32_t *q_offsets,
+                                      const int32_t *kv_lens, const nk_paged_kv_t *cache,
+                                      float softmax_scale, int32_t window_left, int32_t window_right,
+                                      int32_t sink_keys, void *out, float *lse, int32_t num_seqs,
+                                      int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                                      int32_t num_q_heads, int32_t kv_split_tokens, void *stream) {
+  return attention_call(q, q_dtype, q_offsets, kv_lens, cache, softmax_scale, window_left, window_right, sink_keys,
+                        out, lse, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads, kv_split_tokens,
+                        nullptr, 0, true, stream);
 }
 
 int nk_attention_pack(const void *k, const void *v, int32_t in_dtype, const int32_t *key_offsets,

@@ -22,7 +22,9 @@ NK_OK, NK_ERR_INVALID_ARG, NK_ERR_UNSUPPORTED, NK_ERR_WORKSPACE, NK_ERR_DEVICE =
 EXPORTS = ("nk_rope_qk_write_paged", "nk_rope_qk_write_paged_mrope", "nk_ragged_paged_attention", "nk_ragged_paged_attention_band",
            "nk_ragged_paged_attention_workspace_size", "nk_ragged_paged_attention_split_tokens",
            "nk_attention_lse_merge", "nk_status_string", "nk_version", "nk_profile_enable",
-           "nk_profile_reset", "nk_profile_read", "nk_attention_pack", "nk_ragged_paged_attention_backward")
+           "nk_profile_reset", "nk_profile_read", "nk_attention_pack", "nk_ragged_paged_attention_backward",
+           "nk_ragged_paged_attention_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20       # NK_NOALLOC_SCRATCH_BYTES
 
 
 class NKError(RuntimeError):
@@ -64,6 +66,9 @@ def lib():
         L.nk_ragged_paged_attention_band.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, i32, i32, vp, vp, i32,
                                                      i32, i32, i32, i32, i32, vp, sz, vp]
         L.nk_ragged_paged_attention_band.restype = ctypes.c_int
+        L.nk_ragged_paged_attention_noalloc.argtypes = [vp, i32, vp, vp, cache_p, f32, i32, i32, i32, vp, vp, i32,
+                                                        i32, i32, i32, i32, i32, vp]
+        L.nk_ragged_paged_attention_noalloc.restype = ctypes.c_int
         L.nk_ragged_paged_attention_workspace_size.argtypes = [i32] * 11
         L.nk_ragged_paged_attention_workspace_size.restype = sz
         L.nk_ragged_paged_attention_split_tokens.argtypes = [i32] * 7
@@ -256,6 +261,32 @@ def ragged_paged_attention(q, q_offsets, kv_lens, cache, softmax_scale, max_q_le
                                               int(max_kv_len), hq, int(kv_split_tokens), _ptr(workspace),
                                               ws_bytes, _stream(stream))
     _check(st, "nk_ragged_paged_attention_band")
+    return out, lse
+
+
+def ragged_paged_attention_noalloc(q, q_offsets, kv_lens, cache, softmax_scale, max_q_len, max_kv_len,
+                                   window_left=-1, out=None, lse=None, kv_split_tokens=0, stream=None,
+                                   window_right=0, sink_keys=0):
+    """ragged_paged_attention through the entry point that takes no
+    workspace (the library's static per-device scratch); ``out`` is allocated
+    here when not given (the C call itself allocates nothing)."""
+    T, hq, d = q.shape
+    B = kv_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    _i32(q_offsets, "q_offsets"), _i32(kv_lens, "kv_lens")
+    _dev(q, q_offsets, kv_lens, out, lse, cache.k_pages)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is not None and (lse.shape != (T, hq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [T, Hq]")
+    c = cache.struct()
+    st = lib().nk_ragged_paged_attention_noalloc(_ptr(q), _dtype_code(q.dtype), _ptr(q_offsets), _ptr(kv_lens),
+                                                 ctypes.byref(c), float(softmax_scale), int(window_left),
+                                                 int(window_right), int(sink_keys), _ptr(out), _ptr(lse), B, T,
+                                                 int(max_q_len), int(max_kv_len), hq, int(kv_split_tokens),
+                                                 _stream(stream))
+    _check(st, "nk_ragged_paged_attention_noalloc")
     return out, lse
 
 

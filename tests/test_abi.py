@@ -231,3 +231,30 @@ def test_backward_validation(L):
     assert backward(L, c, key_offsets=None) == nk.NK_ERR_INVALID_ARG
     assert backward(L, c, dk=None) == nk.NK_ERR_INVALID_ARG
     assert backward(L, c, num_seqs=0, total=0) == nk.NK_OK
+
+
+def attn_noalloc(L, cache, **kw):
+    a = dict(q=1, q_dtype=nk.NK_BF16, q_offsets=1, kv_lens=1, scale=0.1, window=-1, right=0, sinks=0, out=1,
+             lse=None, num_seqs=1, total=4, max_q=4, max_kv=64, hq=16, split=0)
+    a.update(kw)
+    return L.nk_ragged_paged_attention_noalloc(a["q"], a["q_dtype"], a["q_offsets"], a["kv_lens"],
+                                               None if cache is None else ctypes.byref(cache), a["scale"],
+                                               a["window"], a["right"], a["sinks"], a["out"], a["lse"],
+                                               a["num_seqs"], a["total"], a["max_q"], a["max_kv"], a["hq"],
+                                               a["split"], None)
+
+
+def test_noalloc_validation(L):
+    """The allocation-free entry point checks its arguments like the band
+    call and rejects, before launching anything, a call whose workspace
+    would exceed the static scratch (the long-context decode batch's
+    partials: 128 rows x 64 chunks x 64 heads x 128 dims of float32)."""
+    c = _cache(heads=8)
+    assert attn_noalloc(L, None) == nk.NK_ERR_INVALID_ARG
+    assert attn_noalloc(L, c, right=-2) == nk.NK_ERR_INVALID_ARG
+    assert attn_noalloc(L, c, q_dtype=nk.NK_F32) == nk.NK_ERR_UNSUPPORTED
+    assert attn_noalloc(L, c, total=0) == nk.NK_OK
+    big = L.nk_ragged_paged_attention_workspace_size(nk.NK_BF16, nk.NK_BF16, 128, 128, 1, 32768, 64, 8, 128, -1, 512)
+    assert big > nk.NOALLOC_SCRATCH_BYTES
+    assert attn_noalloc(L, c, num_seqs=128, total=128, max_q=1, max_kv=32768, hq=64,
+                        split=512) == nk.NK_ERR_WORKSPACE
