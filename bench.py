@@ -195,6 +195,7 @@ def measure(st, steps, warmup, flush, split=None):
                                  w.num_q_heads, w.window_left, split_req)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     split_used = nk.split_tokens(st.cache, w.num_seqs, w.max_kv_len, w.num_q_heads, w.window_left, split_req)
+    min_q = int(w.q_lens.min())               # host bound: no decode launch for a prefill-only batch
 
     def step():
         nk.rope_qk_write_paged(st.q, st.k, st.v, st.q_offsets, st.kv_lens, st.freqs, st.cache, w.rotary_dim,
@@ -202,7 +203,7 @@ def measure(st, steps, warmup, flush, split=None):
         nk.ragged_paged_attention(st.q_out, st.q_offsets, st.kv_lens, st.cache, w.softmax_scale, w.max_q_len,
                                   w.max_kv_len, w.window_left, out=st.out, lse=st.lse, kv_split_tokens=split_req,
                                   workspace=ws, window_right=w.window_right,
-                                  sink_keys=w.sink_keys)
+                                  sink_keys=w.sink_keys, min_q_len=min_q)
 
     scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
     sink = torch.empty((), dtype=torch.float32, device="cuda")

@@ -247,14 +247,21 @@ int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_o
  * the band); negative returns NK_ERR_INVALID_ARG.  Decode rows take the sink
  * keys as one extra split-KV chunk, which the workspace of every windowed
  * call reserves (nk_ragged_paged_attention_workspace_size covers it).
+ * min_q_len: a host lower bound of q_len(s) over the batch's segments (0 when
+ * unknown; must not exceed max_q_len, else NK_ERR_INVALID_ARG).  Single-token
+ * (decode) rows and longer (prefill) rows run as separate launches; with
+ * min_q_len >= 2 the batch holds no decode row and the call launches no
+ * decode or merge kernel, as with max_q_len <= 1 it launches no prefill
+ * kernel.  A segment shorter than min_q_len violates the precondition (its
+ * rows may be left unwritten).
  * Every other argument, the workspace and the errors are those of
- * nk_ragged_paged_attention.
+ * nk_ragged_paged_attention (which is this call with min_q_len 0).
  */
 int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t *q_offsets,
                                    const int32_t *kv_lens, const nk_paged_kv_t *cache,
                                    float softmax_scale, int32_t window_left, int32_t window_right,
                                    int32_t sink_keys, void *out, float *lse, int32_t num_seqs, int32_t total_q,
-                                   int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
+                                   int32_t min_q_len, int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
                                    int32_t kv_split_tokens, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
@@ -282,7 +289,7 @@ int nk_ragged_paged_attention_noalloc(const void *q, int32_t q_dtype, const int3
                                       const int32_t *kv_lens, const nk_paged_kv_t *cache,
                                       float softmax_scale, int32_t window_left, int32_t window_right,
                                       int32_t sink_keys, void *out, float *lse, int32_t num_seqs,
-                                      int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                                      int32_t total_q, int32_t min_q_len, int32_t max_q_len, int32_t max_kv_len,
                                       int32_t num_q_heads, int32_t kv_split_tokens, void *stream);
 
 /* Bytes of workspace nk_ragged_paged_attention needs for these scalars

@@ -255,11 +255,12 @@ hipError_t static_scratch(hipStream_t stream, void **out) {
 // (use_static) this device's static scratch buffer.
 int attention_call(const void *q, int32_t q_dtype, const int32_t *q_offsets, const int32_t *kv_lens,
                    const nk_paged_kv_t *cache, float softmax_scale, int32_t window_left, int32_t window_right,
-                   int32_t sink_keys, void *out, float *lse, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                   int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens, void *workspace,
-                   size_t workspace_bytes_given, bool use_static, void *stream) {
-  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0 || num_q_heads <= 0)
+                   int32_t sink_keys, void *out, float *lse, int32_t num_seqs, int32_t total_q, int32_t min_q_len,
+                   int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens,
+                   void *workspace, size_t workspace_bytes_given, bool use_static, void *stream) {
+  if (num_seqs < 0 || total_q < 0 || min_q_len < 0 || max_q_len < 0 || max_kv_len < 0 || num_q_heads <= 0)
     return NK_ERR_INVALID_ARG;
+  if (min_q_len > max_q_len) return NK_ERR_INVALID_ARG;
   if (window_left < -1 || window_right < -1 || sink_keys < 0) return NK_ERR_INVALID_ARG;
   if (kv_split_tokens < 0 || kv_split_tokens % 32) return NK_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return NK_ERR_INVALID_ARG;
@@ -309,10 +310,14 @@ int attention_call(const void *q, int32_t q_dtype, const int32_t *q_offsets, con
     a.sched_items_max = sched_items_max(num_seqs, total_q);
   }
   // prefill rows (q_len > 1) and decode rows (q_len == 1) run as separate
-  // launches on the same stream; each kernel skips the rows of the other kind
+  // launches on the same stream; each kernel skips the rows of the other
+  // kind.  The host bounds say which kinds a batch can hold: no prefill
+  // launch when max_q_len <= 1, no decode launch (nor merge) when
+  // min_q_len >= 2.
+  const bool decode_rows = min_q_len <= 1;
   if (wp.prefill && launch_attn_prefill(a, s) != hipSuccess) return NK_ERR_DEVICE;
-  if (launch_attn_decode(a, s) != hipSuccess) return NK_ERR_DEVICE;
-  if (wp.partials && launch_decode_merge(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  if (decode_rows && launch_attn_decode(a, s) != hipSuccess) return NK_ERR_DEVICE;
+  if (decode_rows && wp.partials && launch_decode_merge(a, s) != hipSuccess) return NK_ERR_DEVICE;
   return NK_OK;
 }
 
@@ -416,7 +421,7 @@ int nk_ragged_paged_attention(const void *q, int32_t q_dtype, const int32_t *q_o
                               int32_t max_kv_len, int32_t num_q_heads, int32_t kv_split_tokens,
                               void *workspace, size_t workspace_bytes_given, void *stream) {
   return nk_ragged_paged_attention_band(q, q_dtype, q_offsets, kv_lens, cache, softmax_scale, window_left, 0,
-                                        0, out, lse, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads,
+                                        0, out, lse, num_seqs, total_q, 0, max_q_len, max_kv_len, num_q_heads,
                                         kv_split_tokens, workspace, workspace_bytes_given, stream);
 }
 
@@ -424,11 +429,11 @@ int nk_ragged_paged_attention_band(const void *q, int32_t q_dtype, const int32_t
                                    const int32_t *kv_lens, const nk_paged_kv_t *cache,
                                    float softmax_scale, int32_t window_left, int32_t window_right,
                                    int32_t sink_keys, void *out, float *lse, int32_t num_seqs, int32_t total_q,
-                                   int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
+                                   int32_t min_q_len, int32_t max_q_len, int32_t max_kv_len, int32_t num_q_heads,
                                    int32_t kv_split_tokens, void *workspace,
                                    size_t workspace_bytes_given, void *stream) {
   return attention_call(q, q_dtype, q_offsets, kv_lens, cache, softmax_scale, window_left, window_right, sink_keys,
-                        out, lse, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads, kv_split_tokens,
+                        out, lse, num_seqs, total_q, min_q_len, max_q_len, max_kv_len, num_q_heads, kv_split_tokens,
                         workspace, workspace_bytes_given, false, stream);
 }
 
@@ -436,10 +441,10 @@ int nk_ragged_paged_attention_noalloc(const void *q, int32_t q_dtype, const int3
                                       const int32_t *kv_lens, const nk_paged_kv_t *cache,
                                       float softmax_scale, int32_t window_left, int32_t window_right,
                                       int32_t sink_keys, void *out, float *lse, int32_t num_seqs,
-                                      int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                                      int32_t total_q, int32_t min_q_len, int32_t max_q_len, int32_t max_kv_len,
                                       int32_t num_q_heads, int32_t kv_split_tokens, void *stream) {
   return attention_call(q, q_dtype, q_offsets, kv_lens, cache, softmax_scale, window_left, window_right, sink_keys,
-                        out, lse, num_seqs, total_q, max_q_len, max_kv_len, num_q_heads, kv_split_tokens,
+                        out, lse, num_seqs, total_q, min_q_len, max_q_len, max_kv_len, num_q_heads, kv_split_tokens,
                         nullptr, 0, true, stream);
 }
 

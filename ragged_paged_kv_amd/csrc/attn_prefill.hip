@@ -602,7 +602,10 @@ NK_DEVICE int segment_of_item(const int32_t *segoff, int num_seqs, int i) {
 // Builds the prefill work list: every (segment, q-block) of the segments
 // with more than one row, ordered by the key tiles it visits, most first
 // (a counting sort; equal classes in any order), and zeroes the queue
-// counters.  One work-group.
+// counters.  q-blocks whose rows see no key at all (rows placed before a
+// segment's first key, or a segment without keys) sort last; this kernel
+// writes their zeros and -inf itself and leaves them out of the item count
+// the attention kernels read.  One work-group.
 __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, int BM) {
   __shared__ int hist[kPlanBins];
   __shared__ int part[kPlanThreads / 64];
@@ -627,7 +630,7 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
     base += tot;
   }
   const int n_items = min(base, a.sched_items_max);
-  if (tid == 0) { segoff[a.num_seqs] = base; sc[kSchedCount] = n_items; }
+  if (tid == 0) segoff[a.num_seqs] = base;
   __syncthreads();
 
   for (int i = tid; i < n_items; i += kPlanThreads) {
@@ -658,6 +661,21 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
     const int q0 = a.q_offsets[s];
     items[2 * pos] = int4{s, qb, q0, a.q_offsets[s + 1] - q0};
     items[2 * pos + 1] = int4{a.kv_lens[s], 0, 0, 0};
+  }
+  // the items without keys are the last ones (bin kPlanBins - 1 ends the
+  // order); after the loop above hist[kPlanBins - 1] is the end of that bin
+  __syncthreads();
+  const int n_keyed = n_items - (hist[kPlanBins - 1] - (kPlanBins > 1 ? hist[kPlanBins - 2] : 0));
+  if (tid == 0) sc[kSchedCount] = n_keyed;
+  const int D = a.cache.head_dim;
+  for (int i = n_keyed; i < n_items; ++i) {
+    const int4 rec = items[2 * i];                // {s, qb, q0, q_len}: every row of the block, every head
+    const int r0 = rec.y * BM, rows = min(BM, rec.w - r0);
+    const long long n = (long long)rows * a.hq * D;
+    bf16_t *o = (bf16_t *)a.out + ((size_t)(rec.z + r0) * a.hq) * D;
+    for (long long e = tid; e < n; e += kPlanThreads) o[e] = (bf16_t)0.f;
+    if (a.lse)
+      for (int e = tid; e < rows * a.hq; e += kPlanThreads) a.lse[(size_t)(rec.z + r0) * a.hq + e] = -INFINITY;
   }
 }
 

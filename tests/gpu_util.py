@@ -81,7 +81,8 @@ def run_hip(w, d, split=None, out_lse=True):
     out, lse = nk.ragged_paged_attention(q_out, d["q_offsets"], d["kv_lens"], d["cache"], w.softmax_scale,
                                          w.max_q_len, w.max_kv_len, w.window_left, lse=lse,
                                          window_right=w.window_right, sink_keys=w.sink_keys,
-                                         kv_split_tokens=w.split_tokens if split is None else split)
+                                         kv_split_tokens=w.split_tokens if split is None else split,
+                                         min_q_len=int(w.q_lens.min()) if w.num_seqs else 0)
     return q_out, out, lse
 
 

@@ -104,12 +104,13 @@ def test_attention_validation(L):
 
 def attn_band(L, cache, window_right, **kw):
     a = dict(q=1, q_dtype=nk.NK_BF16, q_offsets=1, kv_lens=1, scale=0.1, window=-1, out=1, lse=None, num_seqs=1,
-             total=4, max_q=4, max_kv=64, hq=4, split=0, ws=None, ws_bytes=0, sinks=0)
+             total=4, min_q=0, max_q=4, max_kv=64, hq=4, split=0, ws=None, ws_bytes=0, sinks=0)
     a.update(kw)
     return L.nk_ragged_paged_attention_band(a["q"], a["q_dtype"], a["q_offsets"], a["kv_lens"],
                                             None if cache is None else ctypes.byref(cache), a["scale"], a["window"],
-                                            window_right, a["sinks"], a["out"], a["lse"], a["num_seqs"], a["total"], a["max_q"],
-                                            a["max_kv"], a["hq"], a["split"], a["ws"], a["ws_bytes"], None)
+                                            window_right, a["sinks"], a["out"], a["lse"], a["num_seqs"], a["total"],
+                                            a["min_q"], a["max_q"], a["max_kv"], a["hq"], a["split"], a["ws"],
+                                            a["ws_bytes"], None)
 
 
 def test_band_validation(L):
@@ -121,6 +122,8 @@ def test_band_validation(L):
     assert attn_band(L, c, -1, total=0) == nk.NK_OK                   # empty batch: nothing launched
     assert attn_band(L, c, 0, window=8, sinks=-1) == nk.NK_ERR_INVALID_ARG
     assert attn_band(L, c, 0, window=8, sinks=4, total=0) == nk.NK_OK
+    assert attn_band(L, c, 0, min_q=-1) == nk.NK_ERR_INVALID_ARG
+    assert attn_band(L, c, 0, min_q=5, max_q=4) == nk.NK_ERR_INVALID_ARG   # above the upper bound
 
 
 def test_workspace_and_split_queries(L):
@@ -235,13 +238,13 @@ def test_backward_validation(L):
 
 def attn_noalloc(L, cache, **kw):
     a = dict(q=1, q_dtype=nk.NK_BF16, q_offsets=1, kv_lens=1, scale=0.1, window=-1, right=0, sinks=0, out=1,
-             lse=None, num_seqs=1, total=4, max_q=4, max_kv=64, hq=16, split=0)
+             lse=None, num_seqs=1, total=4, min_q=0, max_q=4, max_kv=64, hq=16, split=0)
     a.update(kw)
     return L.nk_ragged_paged_attention_noalloc(a["q"], a["q_dtype"], a["q_offsets"], a["kv_lens"],
                                                None if cache is None else ctypes.byref(cache), a["scale"],
                                                a["window"], a["right"], a["sinks"], a["out"], a["lse"],
-                                               a["num_seqs"], a["total"], a["max_q"], a["max_kv"], a["hq"],
-                                               a["split"], None)
+                                               a["num_seqs"], a["total"], a["min_q"], a["max_q"], a["max_kv"],
+                                               a["hq"], a["split"], None)
 
 
 def test_noalloc_validation(L):

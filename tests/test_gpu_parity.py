@@ -88,6 +88,40 @@ def test_decode_split_sizes(split):
     _run_and_compare(w, split=split)
 
 
+def test_split_rows_reuse_workspace():
+    """One workspace serves several split-KV calls in a row, including a call
+    with fewer sequences and then one with the first call's shape again:
+    every call's out and lse are bit-identical to a call on a fresh
+    workspace (the workspace needs no initialisation between calls)."""
+    big = synth.custom(q_lens=[1, 1, 1, 40, 1], kv_lens=[3000, 129, 4100, 40, 777], num_q_heads=32,
+                       num_kv_heads=4, head_dim=128, split_tokens=64, name="reuse_big")
+    small = synth.custom(q_lens=[1, 1], kv_lens=[2500, 65], num_q_heads=32, num_kv_heads=4, head_dim=128,
+                         split_tokens=64, name="reuse_small")
+    gu.say("split rows: workspace reuse")
+    ws = None
+    for w in (big, small, big, big):
+        d = gu.to_device(w)
+        q_out = nk.rope_qk_write_paged(d["q"], d["k"], d["v"], d["q_offsets"], d["kv_lens"], d["freqs"],
+                                       d["cache"], w.rotary_dim, w.rope_layout, position_ids=d["position_ids"])
+        need = nk.workspace_size(q_out.dtype, d["cache"], w.num_seqs, w.total_q, w.max_q_len, w.max_kv_len,
+                                 w.num_q_heads, w.window_left, w.split_tokens)
+        if ws is None:
+            ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+        assert ws.numel() >= need
+        args = (q_out, d["q_offsets"], d["kv_lens"], d["cache"], w.softmax_scale, w.max_q_len, w.max_kv_len,
+                w.window_left)
+        lse_a = torch.empty(w.total_q, w.num_q_heads, dtype=torch.float32, device="cuda")
+        out_a, _ = nk.ragged_paged_attention(*args, lse=lse_a, kv_split_tokens=w.split_tokens, workspace=ws)
+        lse_b = torch.empty_like(lse_a)
+        out_b, _ = nk.ragged_paged_attention(*args, lse=lse_b, kv_split_tokens=w.split_tokens)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+        assert np.array_equal(lse_a.cpu().numpy(), lse_b.cpu().numpy())
+        _, _, out_o, lse_o = gu.oracle_run(w, d["raw_cache"])
+        gu.check_close(gu.host_values(out_a, "bf16"), out_o, 2e-2, "out")
+        gu.check_close(lse_a.cpu().numpy(), lse_o, 2e-2, "lse")
+
+
 def test_deterministic_and_page_placement_invariant():
     base = dict(q_lens=[1, 1, 200], kv_lens=[900, 33, 260], num_q_heads=8, num_kv_heads=2, head_dim=128)
     w1 = synth.custom(**base, seed=1)

@@ -74,3 +74,34 @@ def test_profile_counts_and_outputs(kind):
     # timed and untimed runs write the same bits
     assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
     assert np.array_equal(lse0.cpu().numpy(), lse1.cpu().numpy())
+
+
+def test_prefill_only_batch_launches_no_decode_kernel():
+    """With min_q_len >= 2 (a batch without single-token rows) the call
+    launches no decode or merge kernel, and its outputs are bit-identical to
+    the call that does not state the bound."""
+    w = synth.custom(q_lens=[70, 130, 33], kv_lens=[70, 200, 90], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                     name="prefill_only")
+    gu.say("prefill-only batch: launches")
+    d = gu.to_device(w)
+    d["q_out"] = torch.empty_like(d["q"])
+    c = d["cache"]
+    nk.rope_qk_write_paged(d["q"], d["k"], d["v"], d["q_offsets"], d["kv_lens"], d["freqs"], c, w.rotary_dim,
+                           w.rope_layout, position_ids=d["position_ids"], q_out=d["q_out"])
+    outs = []
+    try:
+        for min_q in (0, int(w.q_lens.min())):
+            nk.profile_reset()
+            nk.profile_enable(True)
+            out = torch.empty_like(d["q"])
+            lse = torch.empty(w.total_q, w.num_q_heads, dtype=torch.float32, device="cuda")
+            nk.ragged_paged_attention(d["q_out"], d["q_offsets"], d["kv_lens"], c, w.softmax_scale, w.max_q_len,
+                                      w.max_kv_len, w.window_left, out=out, lse=lse, min_q_len=min_q)
+            torch.cuda.synchronize()
+            outs.append((out, lse, nk.profile_read("attn_decode")[1], nk.profile_read("attn_prefill")[1]))
+    finally:
+        nk.profile_enable(False)
+    assert outs[0][2] == 1 and outs[1][2] == 0          # the decode launch only without the bound
+    assert outs[0][3] == 1 and outs[1][3] == 1
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert np.array_equal(outs[0][1].cpu().numpy(), outs[1][1].cpu().numpy())
