@@ -411,44 +411,154 @@ def run_workload(name, steps, warmup, flush):
 
 
 # ------------------------------------------------------------------ CPU baseline
-CPU_BASELINE_SECONDS = 10.0     # the oracle is repeated until this much host time has passed
+CPU_BASELINE_SECONDS = 12.0     # host time budget of the headline workload's oracle sample
+CPU_WORKLOAD_SECONDS = 4.0      # the same for every other workload
+CPU_MAX_WORKERS = 16            # host cores a GPU's share of the machine holds
+
+_ORACLE_WORKLOADS = {}
+# workloads whose oracle task is not the forward pass of their own batch
+_ORACLE_SOURCE = {"pack_bf16": "decode_bf16", "prefill_backward_bf16": "prefill_bf16"}
 
 
-def cpu_baseline(name):
-    """The oracle as it stands, on the host: RoPE + append + attention over
-    the whole workload (decode) or over its five shortest segments (prefill),
-    repeated until CPU_BASELINE_SECONDS have passed (at most 30 runs); the
-    rate is that of the mean run."""
+def _oracle_inputs(w):
+    """Rotated queries and the cache after the append, by the oracle (the
+    forward's inputs; not timed)."""
+    import numpy as np
+
+    import synth
+    from oracle import formats
+
+    raw = synth.build_cache(w, threads=1)
+    nt = synth.new_tokens(w)
+    conv = (lambda x: x.astype(np.float64)) if w.in_dtype == "f32" else formats.bf16_value
+    q, k, v = conv(nt["q"]), conv(nt["k"]), conv(nt["v"])
+    return raw, q, k, v
+
+
+def _oracle_segment(name, s, r0, r1):
+    """Rows r0..r1-1 of segment s of a workload through the oracle, in a
+    worker process with one BLAS thread; returns the kind of work, its
+    algorithmic amount and the oracle's seconds.  Inputs are generated before
+    the clock starts.  A block of a segment's rows is run as a segment of its
+    own over the keys those rows can reach (the prefix up to the block's last
+    position), so its rows sit at their original positions; values other
+    than the block's own tokens come from the segment's prior-row stream
+    (the same shapes and work, other numbers).
+      forward workloads: RoPE + append, then attention (decode bytes or
+        prefill flops of the segment);
+      pack_bf16: slot s of the pack (kv_len kept rows of kv_len + 64), bytes;
+      prefill_backward_bf16: the gradients of segment s, 10 D flops per
+        (row, head, visible key)."""
+    from dataclasses import replace
+
     import numpy as np
     import threadpoolctl
 
     import synth
+    from oracle import attention as o_attn
+    from oracle import pack as o_pack
+    from oracle import rope as o_rope
+    from oracle.paged import PagedCache
     from synth import work
-    from tests import gpu_util as gu
 
-    w = synth.make(name)
-    sample = "whole batch"
-    if name == "prefill_bf16":
-        w = w.subset(np.arange(5))
-        sample = "segments 128..1024 (2688 of 8192 tokens)"
-    raw = synth.build_cache(w)
-    runs = 0
+    src = _ORACLE_SOURCE.get(name, name)
+    if src not in _ORACLE_WORKLOADS:
+        _ORACLE_WORKLOADS[src] = synth.make(src)
+    w = _ORACLE_WORKLOADS[src].subset([s])
+    q_len, kv_len = int(w.q_lens[0]), int(w.kv_lens[0])
+    if (r0, r1) != (0, q_len):
+        w = replace(w, q_lens=np.array([r1 - r0], np.int32), kv_lens=np.array([kv_len - q_len + r1], np.int32),
+                    token_ids=w.token_ids[r0:r1].copy())
+    with threadpoolctl.threadpool_limits(1):
+        if name == "pack_bf16":
+            kept = int(w.kv_lens[0])
+            rng = np.random.default_rng(s)
+            k = rng.standard_normal((kept + 64, w.num_kv_heads, w.head_dim))
+            v = rng.standard_normal((kept + 64, w.num_kv_heads, w.head_dim))
+            t0 = time.perf_counter()
+            o_pack.attention_pack(k, v, np.array([0, kept + 64]), np.array([kept]), "bf16", 16)
+            dt = time.perf_counter() - t0
+            nbytes = 2 * kept * w.num_kv_heads * w.head_dim * 2 * 2 + 16 + (-(-kept // 16)) * 4
+            return "pack", nbytes, dt
+        raw, q, k, v = _oracle_inputs(w)
+        freqs = synth.freqs_table(w)
+        t0 = time.perf_counter()
+        cache = PagedCache.from_storage(w.cache_dtype, raw["k_pages"], raw["v_pages"], raw["k_scales"],
+                                        raw["v_scales"])
+        q_out, cache2 = o_rope.rope_qk_write_paged(q, k, v, w.in_dtype, w.q_offsets, w.kv_lens, w.position_ids,
+                                                   freqs, w.rotary_dim, w.rope_layout, cache, w.page_table)
+        if name == "prefill_backward_bf16":
+            dout = np.random.default_rng(s).standard_normal(q_out.shape)
+            t0 = time.perf_counter()
+            o_attn.ragged_paged_attention_backward(q_out, w.q_offsets, w.kv_lens, cache2, w.page_table,
+                                                   w.softmax_scale, dout, w.window_left,
+                                                   window_right=w.window_right, sink_keys=w.sink_keys)
+            dt = time.perf_counter() - t0
+            return "backward", 10 * w.head_dim * w.num_q_heads * work.prefill_pairs(w), dt
+        o_attn.ragged_paged_attention(q_out, w.q_offsets, w.kv_lens, cache2, w.page_table, w.softmax_scale,
+                                      w.window_left, window_right=w.window_right, sink_keys=w.sink_keys)
+        dt = time.perf_counter() - t0
+    if int(w.q_lens[0]) == 1:
+        return "decode", work.decode_bytes(w), dt
+    return "prefill", work.prefill_flops(w), dt
+
+
+_KIND_UNIT = {"decode": ("GB/s", 1e9), "prefill": ("TFLOP/s", 1e12), "pack": ("GB/s", 1e9),
+              "backward": ("TFLOP/s", 1e12)}
+
+
+def cpu_baseline(name, seconds, pool, cores):
+    """The oracle as it stands, on the host's cores: a pool of `cores`
+    processes, one BLAS thread each, takes the workload's segments one at a
+    time (blocks of at most 256 rows, 64 for the gradients; a seeded
+    shuffle of their order, at most four passes) until
+    `seconds` of wall time have passed, then lets the segments in flight
+    finish.  The rate of each kind of work is its amount over its oracle
+    seconds summed over the segment runs, times the number of processes:
+    the processes run side by side, so that is the pool's aggregate rate.
+    Returns {kind: {value, unit, cores, kind, sample}}."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import synth
+
+    w = synth.make(_ORACLE_SOURCE.get(name, name))
+    n_seg = w.num_seqs
+    block = 64 if name == "prefill_backward_bf16" else 256
+    tasks = [(s, r0, min(r0 + block, int(w.q_lens[s]))) for s in range(n_seg)
+             for r0 in range(0, max(int(w.q_lens[s]), 1), block)]
+    order = np.random.default_rng(1234).permutation(len(tasks))
+    done = {}
     t0 = time.perf_counter()
+    pending, i = set(), 0
     while True:
-        gu.oracle_run(w, raw)
-        runs += 1
-        total = time.perf_counter() - t0
-        if total >= CPU_BASELINE_SECONDS or runs >= 30:
+        while len(pending) < cores and time.perf_counter() - t0 < seconds and i < 4 * len(tasks):
+            pending.add(pool.submit(_oracle_segment, name, *tasks[order[i % len(tasks)]]))
+            i += 1
+        if not pending:
             break
-    dt = total / runs
-    sample = f"{sample}, {runs} runs in {total:.1f} s"
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    if name == "prefill_bf16":
-        return {"value": work.prefill_flops(w) / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                "sample": sample, "seconds": dt}
-    return {"value": work.decode_bytes(w) / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds": dt}
+        fin, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+        for f in fin:
+            kind, amount, dt = f.result()
+            rec = done.setdefault(kind, [0, 0.0, 0])
+            rec[0] += amount
+            rec[1] += dt
+            rec[2] += 1
+    wall = time.perf_counter() - t0
+    res = {}
+    for kind, (amount, secs, n) in done.items():
+        unit, scale = _KIND_UNIT[kind]
+        res[kind] = {"value": amount / secs * cores / scale, "unit": unit, "cores": cores, "kind": "oracle",
+                     "sample": f"{n} runs of row blocks ({kind} work; {len(tasks)} blocks in {n_seg} segments), "
+                               f"{cores} processes x 1 BLAS thread, {wall:.1f} s wall; oracle {secs:.1f} s summed "
+                               f"over the runs"}
+    return res
+
+
+def cpu_cores():
+    """Host cores this process may run on, capped at one GPU's share."""
+    return max(1, min(len(os.sched_getaffinity(0)), CPU_MAX_WORKERS))
 
 
 # ------------------------------------------------------------------ counters
@@ -578,7 +688,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="decode_bf16,prefill_bf16,decode_fp8,mixed_window_bf16,prefill_bidir_bf16")
+    ap.add_argument("--only", default="decode_bf16,prefill_bf16,decode_fp8,mixed_window_bf16,prefill_bidir_bf16,"
+                    "mixed_sinks_bf16,prefill_mrope_bf16,prefill_prope_bf16,pack_bf16,prefill_backward_bf16")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
@@ -663,11 +774,19 @@ def main():
         log(json.dumps(results[n]))
 
     head = results.get("decode_bf16") or next(iter(results.values()))
-    cpu = None
-    if not args.no_cpu and head["workload"] in ("decode_bf16", "prefill_bf16"):
-        log("timing the oracle on the host")
-        cpu = cpu_baseline(head["workload"])
-        log(json.dumps(cpu))
+    cpu, cpu_all = None, {}
+    if not args.no_cpu:
+        import concurrent.futures as cf
+        import multiprocessing as mp
+        cores = cpu_cores()
+        log(f"timing the oracle on the host ({cores} processes)")
+        with cf.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn")) as pool:
+            for n in names:
+                budget = CPU_BASELINE_SECONDS if n == head["workload"] else CPU_WORKLOAD_SECONDS
+                cpu_all[n] = cpu_baseline(n, budget, pool, cores)
+                log(n, json.dumps(cpu_all[n]))
+        hk = cpu_all.get(head["workload"], {})
+        cpu = hk.get("decode") or next(iter(hk.values()), None)
 
     dec_k = head.get("kernels", {}).get("attn_decode")
     roof = None
@@ -712,6 +831,8 @@ def main():
             if t_attn > 0:
                 ideal = r["decode_bytes"] / (HBM_PEAK_GBS * 1e9) + r["prefill_flops"] / (BF16_PEAK_TFLOPS * 1e12)
                 e["combined_roofline_frac"] = ideal / t_attn
+        if n in cpu_all:
+            e["cpu_baseline"] = cpu_all[n]
         extra[n] = e
     line["workloads"] = extra
     print(json.dumps(line), flush=True)

@@ -101,3 +101,19 @@ def test_mfma_summary(tmp_path):
     assert rec["executed_over_algorithmic"] == pytest.approx(2.0)
     assert rec["active_cycles"] == pytest.approx(10.0)                       # one XCD's share
     assert rec["mfma_busy_frac"] == pytest.approx(1024.0 / (10.0 * 64))
+
+
+def test_cpu_baseline_pool_reports_each_kind():
+    """The host baseline runs the oracle in a process pool over row blocks
+    and reports one rate per kind of work, with the pool's process count as
+    its cores."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    assert 1 <= bench.cpu_cores() <= bench.CPU_MAX_WORKERS
+    with cf.ProcessPoolExecutor(2, mp_context=mp.get_context("spawn")) as pool:
+        res = bench.cpu_baseline("tiny_prefill_f32", 0.5, pool, 2)
+    assert set(res) == {"prefill"}
+    r = res["prefill"]
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert "2 processes" in r["sample"]
