@@ -13,7 +13,8 @@
 // softmax's Jacobian applied row by row (the running-state identities of the
 // Algenta page's flash-attention walkthrough give the same P from lse).
 //
-// Design (float32 VALU, correctness first): two kernels.
+// Design of the float32 path (and of bf16 at head dims other than 64 and
+// 128; the MFMA path below takes bf16 at 64 and 128): two VALU kernels.
 //   * dQ: one wave per (query row, up to 4 query heads of one KV head); lanes
 //     take 64 visible keys at a time, each lane loading its key's K and V once
 //     and computing q.k and dO.v for every head, then lanes over head
@@ -291,6 +292,486 @@ __global__ void __launch_bounds__(64) attn_dkv_kernel(BackwardArgs a, int blocks
   }
 }
 
+// ---------------------------------------------------------------- MFMA path
+// bf16 queries and cache, head_dim 64 or 128: the same gradients on
+// v_mfma_f32_32x32x16_bf16 (32 x 32 tiles, k = 16), P and dS rounded to bf16
+// for their products, float32 accumulation.
+//
+// Two kernels, each recomputing the scores and dP = dO V^T of its tiles:
+//   * dK/dV: a work-group of 4 waves owns 128 keys of one KV head (32 per
+//     wave, K and V held as MFMA operands) and walks the 32-row query tiles
+//     of every query head of the group that can see them.  Per tile the
+//     waves stage Q and dO row-major in LDS with the rows' log-sum-exp and
+//     dO.O; the score products read rows of these tiles, dV = P^T dO and
+//     dK = dS^T Q (contraction over rows) read down their columns with
+//     transposing LDS reads;
+//   * dQ: a work-group of 4 waves owns 32-row query tiles of up to 4 query
+//     heads of one KV head (Q and dO held as operands) and walks the 32-key
+//     tiles the rows see, staging K and V row-major (dQ = dS K reads down
+//     K's columns).
+// Both pipelines prefetch the next tile's global data into registers while
+// the current one is computed, into a second LDS buffer.
+// Row (dK/dV) or key (dQ) order inside a tile is permuted (bits 2 and 3 of
+// the index swapped) for the score products, which makes their output lane
+// layout the A operand layout of the next product: P and dS never move
+// between lanes.  In a 32 x 32 output lane l holds column l % 32 and rows
+// 8 (v / 4) + 4 (l / 32) + v % 4 (v < 16); under the permutation entry v is
+// row 16 (v / 8) + 8 (l / 32) + v % 8, i.e. entries 8 s .. 8 s + 7 are the
+// eight consecutive rows of k-step s.
+
+NK_DEVICE constexpr int bperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+NK_DEVICE uint32_t pack2_bf16(float lo, float hi) {
+  bf16x2_t v = {(bf16_t)lo, (bf16_t)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+NK_DEVICE bf16x8_t pack8(const float *x) {
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]),
+                                              pack2_bf16(x[4], x[5]), pack2_bf16(x[6], x[7])});
+}
+
+// Does the row at position p see key k (band and sink keys as the forward)?
+NK_DEVICE bool sees(const BackwardArgs &a, int p, int L, int k) {
+  const int hi = band_hi(p, L, a.window_right), lo = band_lo(p, a.window_left);
+  const int sinks = a.window_left < 0 ? 0 : a.sink_keys;
+  return k <= hi && (k >= lo || (k < sinks && k < lo && k <= hi));
+}
+
+// Four 16-bit values down a column of a row-major LDS tile: within each
+// 16-lane group, ds_read_b64_tr_b16 hands lane 4a + b element b of the 8
+// bytes addressed by lane 4e + a, as its element e (measured on gfx950).  So
+// if lane j of the group addresses row k0 + j / 4, columns c0 + 4 (j % 4)
+// .. + 3, lane i receives rows k0 .. k0 + 3 of column c0 + i.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+NK_DEVICE bf16x8_t lds_col8(const uint8_t *p, int row_bytes) {
+  typedef __attribute__((address_space(3))) i16x4_t *lds_ptr;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)p);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p + 4 * row_bytes));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int D>
+struct BwdTile {
+  // bytes per row-major row in LDS: 2D + 48 puts 16 consecutive rows on
+  // distinct banks for 16-byte row reads and 4 rows x 32 bytes apart for the
+  // column reads above
+  static constexpr int RM = 2 * D + 48;
+  static constexpr int KD = D / 16;         // k-steps over head dims
+  static constexpr int DC = D / 32;         // 32-dim output tiles
+  static constexpr int CH = 32 * D / 8;     // 16-byte chunks of a 32 x D tile
+  static constexpr int PER = CH / 256;      // of them per thread (4 waves)
+  static_assert(CH % 256 == 0, "tile chunks must divide over the work-group");
+};
+
+// ---- dK / dV
+template <int D>
+struct DkvLds {
+  using B = BwdTile<D>;
+  static constexpr int Q = 0, DO = 32 * B::RM, LSE = 64 * B::RM, DI = LSE + 128, SIZE = DI + 128;
+  static constexpr int TOTAL = 2 * SIZE;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int tiles_per_seq) {
+  using B = BwdTile<D>;
+  using LY = DkvLds<D>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];      // two buffers of LY::SIZE
+  // KV head fastest (consecutive work-groups go to different XCDs, so each
+  // XCD's L2 holds the rows of its own heads), then segment, then key tile:
+  // a causal segment's first key tiles carry the most rows, so every
+  // segment's heaviest work-groups are dispatched first
+  const int nh = a.cache.num_kv_heads;
+  const int g = blockIdx.x % nh, rest = blockIdx.x / nh;
+  const int s = rest % a.num_seqs, kt0 = (rest / a.num_seqs) * 128;
+  const int L = a.kv_lens[s];
+  if (kt0 >= L) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int hkv = a.cache.num_kv_heads, G = a.hq / hkv, P = a.cache.page_size;
+  const int q0 = a.q_offsets[s];
+  const int q_len = a.q_offsets[s + 1] - q0;
+  const int shift = L - q_len;
+  const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
+
+  // this wave's 32 keys as operands: K (B of S = Q K^T: lane = key l32,
+  // dims 16 kk + 8 h ..) and V (B of dP = dO V^T); keys past the segment are
+  // zeros
+  const int k0 = kt0 + 32 * w;
+  const int key = k0 + l32;
+  bf16x8_t kop[B::KD], vop[B::KD];
+  {
+    const bool kv = key < L;
+    const size_t blk = ((size_t)pt[min(key, L - 1) / P] * hkv + g) * P * D;
+    const bf16_t *kp = (const bf16_t *)a.cache.k_pages + blk;
+    const bf16_t *vp = (const bf16_t *)a.cache.v_pages + blk;
+    const int t = min(key, L - 1) % P;
+#pragma unroll
+    for (int kk = 0; kk < B::KD; ++kk) {
+      const int d0 = 16 * kk + 8 * h;
+      bf16x8_t x = *(const bf16x8_t *)(kp + k_elem<bf16_t>(d0, t, P));
+      bf16x8_t y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = vp[v_elem<bf16_t>(d0 + e, t, D)];
+      if (!kv) { x = bf16x8_t{}; y = bf16x8_t{}; }
+      kop[kk] = x;
+      vop[kk] = y;
+    }
+  }
+
+  // query rows that may see one of the work-group's keys (each (row, key)
+  // checked exactly when a tile straddles the band)
+  const int kmax = min(kt0 + 128, L) - 1;
+  const int i_min = a.window_right < 0 ? 0 : (int)max(0LL, (long long)kt0 - a.window_right - shift);
+  const bool sink = a.window_left >= 0 && kt0 < a.sink_keys;
+  const int i_max = (a.window_left < 0 || sink) ? q_len - 1
+                                                 : (int)min((long long)q_len - 1, (long long)kmax + a.window_left - shift);
+  const int rt0 = i_min / 32, rt1 = i_max < i_min ? rt0 - 1 : i_max / 32;
+  const int n_pairs = (rt1 - rt0 + 1) * G;
+
+  f32x16_t dk[B::DC], dv[B::DC];
+#pragma unroll
+  for (int c = 0; c < B::DC; ++c) { dk[c] = f32x16_t{}; dv[c] = f32x16_t{}; }
+  const float c2 = a.softmax_scale * kLog2e;
+
+  // software pipeline over the (row tile, head) pairs: the global loads of
+  // pair pr + 1 are in flight while pair pr is computed; LDS is double
+  // buffered, so one barrier per pair separates a buffer's writes from its
+  // reads (a buffer is rewritten two pairs later, after the next barrier)
+  bf16x8_t gq[B::PER], gd[B::PER], go[B::PER];
+  float glse[B::PER];
+  auto fetch = [&](int pr) {
+    const int r0 = (rt0 + pr / G) * 32, head = g * G + pr % G;
+#pragma unroll
+    for (int i = 0; i < B::PER; ++i) {
+      const int c = tid + 256 * i;
+      // rows past the segment read its last row (in bounds; their P is zero)
+      const int row = min(r0 + c / (D / 8), q_len - 1), d0 = 8 * (c % (D / 8));
+      const size_t rh = (size_t)(q0 + row) * a.hq + head;
+      gq[i] = *(const bf16x8_t *)((const bf16_t *)a.q + rh * D + d0);
+      gd[i] = *(const bf16x8_t *)((const bf16_t *)a.dout + rh * D + d0);
+      go[i] = *(const bf16x8_t *)((const bf16_t *)a.out + rh * D + d0);
+      glse[i] = a.lse[rh];
+    }
+  };
+  auto stage = [&](int pr, uint8_t *buf) {
+    const int r0 = (rt0 + pr / G) * 32;
+#pragma unroll
+    for (int i = 0; i < B::PER; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / (D / 8), d0 = 8 * (c % (D / 8));
+      const int row = r0 + r;
+      *(bf16x8_t *)(buf + LY::Q + r * B::RM + 2 * d0) = gq[i];
+      *(bf16x8_t *)(buf + LY::DO + r * B::RM + 2 * d0) = gd[i];
+      float di = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) di = fmaf((float)gd[i][e], (float)go[i][e], di);
+      // the D/8 chunks of a row sit in consecutive threads
+#pragma unroll
+      for (int m = 1; m < D / 8; m <<= 1) di += shfl_xor_f32(di, m);
+      if (c % (D / 8) == 0) {
+        ((float *)(buf + LY::DI))[r] = di;
+        // log2-domain lse; rows past the segment get +inf (P = 0)
+        ((float *)(buf + LY::LSE))[r] = row < q_len ? glse[i] * kLog2e : INFINITY;
+      }
+    }
+  };
+
+  if (n_pairs > 0) fetch(0);
+  for (int pr = 0; pr < n_pairs; ++pr) {
+    const int r0 = (rt0 + pr / G) * 32;
+    uint8_t *buf = lds + (pr & 1) * LY::SIZE;
+    stage(pr, buf);
+    __syncthreads();
+    if (pr + 1 < n_pairs) fetch(pr + 1);
+
+    // ---- S = Q K^T and dP = dO V^T (rows permuted)
+    f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+    {
+      const uint8_t *qa = buf + LY::Q + bperm(l32) * B::RM + 16 * h;
+      const uint8_t *da = buf + LY::DO + bperm(l32) * B::RM + 16 * h;
+#pragma unroll
+      for (int kk = 0; kk < B::KD; ++kk) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(qa + 32 * kk), kop[kk], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(da + 32 * kk), vop[kk], dp, 0, 0, 0);
+      }
+    }
+    // ---- P and dS: entry v is row 16 (v/8) + 8 h + v % 8 of the tile, key `key`
+    float pv[16], dsv[16];
+    {
+      const float *lse2 = (const float *)(buf + LY::LSE);
+      const float *dis = (const float *)(buf + LY::DI);
+      // whole tile inside the band (every row valid, every key seen)?
+      const int p_first = r0 + shift, p_last = r0 + 31 + shift;
+      const bool full = r0 + 31 < q_len && k0 + 31 < L && k0 + 31 <= band_hi(p_first, L, a.window_right) &&
+                        k0 >= band_lo(p_last, a.window_left);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 16 * (v >> 3) + 8 * h + (v & 7);
+        const bool ok = full || (r0 + r < q_len && key < L && sees(a, r0 + r + shift, L, key));
+        const float pe = ok ? fast_exp2(fmaf(sc[v], c2, -lse2[r])) : 0.f;
+        pv[v] = pe;
+        dsv[v] = pe * (dp[v] - dis[r]);
+      }
+    }
+    // ---- dV += P^T dO and dK += dS^T Q (contraction over the tile's rows)
+    {
+      const bf16x8_t pa0 = pack8(pv), pa1 = pack8(pv + 8);
+      const bf16x8_t sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
+      // B operands (rows 16 s + 8 h .. + 7 of dim 32 c + l32) read down the
+      // columns of the row-major dO and Q tiles
+      const int i16 = lane & 15;
+      const int cb = (8 * h + (i16 >> 2)) * B::RM + 32 * ((lane >> 4) & 1) + 8 * (i16 & 3);
+      const uint8_t *dob = buf + LY::DO + cb;
+      const uint8_t *qbb = buf + LY::Q + cb;
+#pragma unroll
+      for (int c = 0; c < B::DC; ++c) {
+        dv[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0, lds_col8(dob + 64 * c, B::RM), dv[c], 0, 0, 0);
+        dv[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1, lds_col8(dob + 64 * c + 16 * B::RM, B::RM), dv[c], 0, 0, 0);
+        dk[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa0, lds_col8(qbb + 64 * c, B::RM), dk[c], 0, 0, 0);
+        dk[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa1, lds_col8(qbb + 64 * c + 16 * B::RM, B::RM), dk[c], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- write: output entry v of tile c is key k0 + 8 (v/4) + 4 h + v % 4, dim 32 c + l32
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int kk = k0 + 8 * (v >> 2) + 4 * h + (v & 3);
+    if (kk >= L) continue;
+    const size_t orow = ((size_t)a.key_offsets[s] + kk) * hkv + g;
+#pragma unroll
+    for (int c = 0; c < B::DC; ++c) {
+      a.dk[orow * D + 32 * c + l32] = a.softmax_scale * dk[c][v];
+      a.dv[orow * D + 32 * c + l32] = dv[c][v];
+    }
+  }
+}
+
+// ---- dQ
+template <int D>
+struct DqLds {
+  using B = BwdTile<D>;
+  static constexpr int K = 0, V = 32 * B::RM, SIZE = 64 * B::RM;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int blocks_per_seq, int GW) {
+  using B = BwdTile<D>;
+  using LY = DqLds<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * LY::SIZE];   // two buffers
+  const int TB = 4 / GW;
+  const int hkv = a.cache.num_kv_heads, G = a.hq / hkv, P = a.cache.page_size;
+  // head block fastest (XCD-local rows and keys), then segment, then row
+  // block, last row blocks first: under a causal band they see the most keys
+  const int nhb = hkv * (G / GW);
+  const int hy = blockIdx.x % nhb, rest = blockIdx.x / nhb;
+  const int s = rest % a.num_seqs, rb = blocks_per_seq - 1 - rest / a.num_seqs;
+  const int g = hy / (G / GW), hblk = hy % (G / GW);
+  const int q0 = a.q_offsets[s];
+  const int q_len = a.q_offsets[s + 1] - q0;
+  const int L = a.kv_lens[s];
+  const int R0 = rb * 32 * TB;
+  if (R0 >= q_len) return;
+  const int shift = L - q_len;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int head = g * G + hblk * GW + w % GW;
+  const int r0 = R0 + 32 * (w / GW);
+  const int row = r0 + l32;                       // this lane's row (column of S^T)
+  const bool rvalid = row < q_len;
+  const int32_t *pt = a.cache.page_table + (size_t)s * a.cache.page_table_stride;
+
+  // Q and dO of the lane's row as B operands (dims 16 kk + 8 h ..), dO.O and lse
+  bf16x8_t qb[B::KD], db[B::KD];
+  float di = 0.f, lse2 = INFINITY;
+  {
+    const size_t off = ((size_t)(q0 + min(row, q_len - 1)) * a.hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < B::KD; ++kk) {
+      const int d0 = 16 * kk + 8 * h;
+      bf16x8_t qx = *(const bf16x8_t *)((const bf16_t *)a.q + off + d0);
+      bf16x8_t dx = *(const bf16x8_t *)((const bf16_t *)a.dout + off + d0);
+      const bf16x8_t ox = *(const bf16x8_t *)((const bf16_t *)a.out + off + d0);
+      if (!rvalid) { qx = bf16x8_t{}; dx = bf16x8_t{}; }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) di = fmaf((float)dx[e], (float)ox[e], di);
+      qb[kk] = qx;
+      db[kk] = dx;
+    }
+    di += shfl_xor_f32(di, 32);
+    if (rvalid) lse2 = a.lse[(size_t)(q0 + row) * a.hq + head] * kLog2e;
+  }
+
+  // keys the work-group's rows may see: the band of its first and last rows,
+  // plus the sink keys
+  const int p_lo = R0 + shift, p_hi = min(R0 + 32 * TB, q_len) - 1 + shift;
+  const int kh = band_hi(p_hi, L, a.window_right), kl = band_lo(p_lo, a.window_left);
+  const int sinks = a.window_left < 0 ? 0 : min(a.sink_keys, L);
+  // wave's own range (for skipping tiles it cannot see)
+  const int w_hi = band_hi(min(r0 + 31, q_len - 1) + shift, L, a.window_right);
+  const int w_lo = band_lo(r0 + shift, a.window_left);
+  const bool w_active = r0 < q_len;
+  // tiles: the sink tiles below the band's first tile, then the band's
+  const int tb0 = kl / 32, tb1 = kh < kl ? tb0 - 1 : kh / 32;
+  const int ns = sinks > 0 ? min((sinks + 31) / 32, max(tb0, 0)) : 0;
+  const int n_tiles = ns + max(0, tb1 - tb0 + 1);
+
+  f32x16_t dq[B::DC];
+#pragma unroll
+  for (int c = 0; c < B::DC; ++c) dq[c] = f32x16_t{};
+  const float c2 = a.softmax_scale * kLog2e;
+
+  // software pipeline over the key tiles: the global loads of tile it + 1
+  // are in flight while tile it is computed; LDS double buffered (one
+  // barrier per tile, as in the dK/dV kernel)
+  bf16x8_t gk[B::PER], gv[B::PER];
+  auto tile_base = [&](int it) { return 32 * (it < ns ? it : tb0 + (it - ns)); };
+  constexpr int RUNS = D / 32 * 64;               // V runs per 16-key block (bf16: 2 dim groups per run)
+  // this thread's K chunk is key c % 32 (the same key for every i, since
+  // 256 is a multiple of 32); its V chunks are runs of the 16-key block i
+  const int k_key = tid % 32;
+  auto v_key = [&](int i) { const int rr = (tid + 256 * i) % RUNS; return 16 * ((tid + 256 * i) / RUNS) + 4 * ((rr % 64) / 16); };
+  // page ids of a tile's chunks, read one tile ahead of its data
+  int pk_page = 0, pv_page[B::PER];
+  auto fetch_pages = [&](int it) {
+    const int kb = tile_base(it);
+    pk_page = pt[min(kb + k_key, L - 1) / P];
+#pragma unroll
+    for (int i = 0; i < B::PER; ++i) pv_page[i] = pt[min(kb + v_key(i), L - 1) / P];
+  };
+  auto fetch = [&](int it) {
+    const int kb = tile_base(it);
+#pragma unroll
+    for (int i = 0; i < B::PER; ++i) {
+      const int c = tid + 256 * i;
+      {
+        // keys past the segment read its last key (in bounds) and are zeroed when staged
+        const int k = min(kb + k_key, L - 1), d0 = 8 * (c / 32);
+        const size_t blk = ((size_t)pk_page * hkv + g) * P * D;
+        gk[i] = *(const bf16x8_t *)((const bf16_t *)a.cache.k_pages + blk + k_elem<bf16_t>(d0, k % P, P));
+      }
+      {
+        const int rr = c % RUNS, cg = rr / 64, l = rr % 16;
+        const int k = min(kb + v_key(i), L - 1);   // the run's 4 keys share a page
+        const size_t blk = ((size_t)pv_page[i] * hkv + g) * P * D;
+        gv[i] = *(const bf16x8_t *)((const bf16_t *)a.cache.v_pages + blk + v_elem<bf16_t>(32 * cg + l, (k % P) & ~3, D));
+      }
+    }
+  };
+  auto stage = [&](int it, uint8_t *buf) {
+    const int kb = tile_base(it);
+#pragma unroll
+    for (int i = 0; i < B::PER; ++i) {
+      const int c = tid + 256 * i;
+      {
+        const int kr = c % 32, d0 = 8 * (c / 32);
+        *(bf16x8_t *)(buf + LY::K + kr * B::RM + 2 * d0) = kb + kr < L ? gk[i] : bf16x8_t{};
+      }
+      {
+        const int sb = c / RUNS, rr = c % RUNS, cg = rr / 64, Ln = rr % 64, gq = Ln / 16, l = Ln % 16;
+        const int kr0 = 16 * sb + 4 * gq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = kb + kr0 + e < L;
+          *(bf16_t *)(buf + LY::V + (kr0 + e) * B::RM + 2 * (32 * cg + l)) = ok ? gv[i][e] : (bf16_t)0.f;
+          *(bf16_t *)(buf + LY::V + (kr0 + e) * B::RM + 2 * (32 * cg + 16 + l)) = ok ? gv[i][4 + e] : (bf16_t)0.f;
+        }
+      }
+    }
+  };
+
+  if (n_tiles > 0) {
+    fetch_pages(0);
+    fetch(0);
+    if (n_tiles > 1) fetch_pages(1);
+  }
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kb = tile_base(it);
+    uint8_t *buf = lds + (it & 1) * LY::SIZE;
+    stage(it, buf);
+    __syncthreads();
+    if (it + 1 < n_tiles) {
+      fetch(it + 1);
+      if (it + 2 < n_tiles) fetch_pages(it + 2);
+    }
+
+    const bool act = w_active && kb <= w_hi && (kb + 31 >= w_lo || kb < sinks);
+    if (act) {
+      // ---- S^T = K Q^T and dP^T = V dO^T (keys permuted)
+      f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+      const uint8_t *ka = buf + LY::K + bperm(l32) * B::RM + 16 * h;
+      const uint8_t *va = buf + LY::V + bperm(l32) * B::RM + 16 * h;
+#pragma unroll
+      for (int kk = 0; kk < B::KD; ++kk) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(ka + 32 * kk), qb[kk], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(va + 32 * kk), db[kk], dp, 0, 0, 0);
+      }
+      // entry v: key kb + 16 (v/8) + 8 h + v % 8 of row `row`
+      const int pos = row + shift;
+      const bool full = r0 + 31 < q_len && kb + 31 < L && kb + 31 <= band_hi(r0 + shift, L, a.window_right) &&
+                        kb >= band_lo(r0 + 31 + shift, a.window_left);
+      float dsv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int k = kb + 16 * (v >> 3) + 8 * h + (v & 7);
+        const bool ok = full || (rvalid && k < L && sees(a, pos, L, k));
+        const float pe = ok ? fast_exp2(fmaf(sc[v], c2, -lse2)) : 0.f;
+        dsv[v] = pe * (dp[v] - di);
+      }
+      // ---- dQ += dS K: A = dS (row l32, keys of k-step s), B = keys
+      // 16 s + 8 h .. + 7 of dim 32 c + l32, read down the K tile's columns
+      const bf16x8_t sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
+      const int i16 = lane & 15;
+      const uint8_t *kb_ = buf + LY::K + (8 * h + (i16 >> 2)) * B::RM + 32 * ((lane >> 4) & 1) + 8 * (i16 & 3);
+#pragma unroll
+      for (int c = 0; c < B::DC; ++c) {
+        dq[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa0, lds_col8(kb_ + 64 * c, B::RM), dq[c], 0, 0, 0);
+        dq[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa1, lds_col8(kb_ + 64 * c + 16 * B::RM, B::RM), dq[c], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- write: entry v of tile c is row r0 + 8 (v/4) + 4 h + v % 4, dim 32 c + l32
+  if (!w_active) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = r0 + 8 * (v >> 2) + 4 * h + (v & 3);
+    if (r >= q_len) continue;
+    float *drow = a.dq + ((size_t)(q0 + r) * a.hq + head) * D;
+#pragma unroll
+    for (int c = 0; c < B::DC; ++c) drow[32 * c + l32] = a.softmax_scale * dq[c][v];
+  }
+}
+
+template <int D>
+hipError_t launch_mfma(const BackwardArgs &a, int max_q_len, hipStream_t stream) {
+  const int hkv = a.cache.num_kv_heads, G = a.hq / hkv;
+  int GW = 1;                                      // heads per dQ work-group: power of 2 dividing G, at most 4
+  while (GW * 2 <= 4 && G % (GW * 2) == 0) GW *= 2;
+  const int rows_per_block = 32 * (4 / GW);
+  hipError_t e = hipSuccess;
+  if (a.total_q > 0 && max_q_len > 0) {
+    const int per_seq = (max_q_len + rows_per_block - 1) / rows_per_block;
+    const long long blocks = (long long)a.num_seqs * per_seq * hkv * (G / GW);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    e = launch(attn_dq_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, a, per_seq, GW);
+  }
+  if (e != hipSuccess || a.max_kv_len == 0) return e;
+  const int per_seq = (a.max_kv_len + 127) / 128;
+  const long long blocks = (long long)a.num_seqs * per_seq * hkv;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  static bool attr_set[64];                     // per device; idempotent, a race only repeats the call
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (!attr_set[dev & 63]) {
+    e = hipFuncSetAttribute((const void *)attn_dkv_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            DkvLds<D>::TOTAL);
+    if (e != hipSuccess) return e;
+    attr_set[dev & 63] = true;
+  }
+  return launch(attn_dkv_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), DkvLds<D>::TOTAL, stream, a, per_seq);
+}
+
 template <typename T>
 hipError_t launch_t(const BackwardArgs &a, hipStream_t stream) {
   hipError_t e = hipSuccess;
@@ -316,6 +797,11 @@ hipError_t launch_attn_backward(const BackwardArgs &a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   ProfileScope prof("attn_backward", stream);
   if (a.q_dtype == NK_F32) return launch_t<float>(a, stream);
+  // bf16 on MFMA for head dims 64 and 128 (the row-tile grid is bounded by
+  // total_q, the longest a segment can be)
+  const int D = a.cache.head_dim;
+  if (D == 128) return launch_mfma<128>(a, a.total_q, stream);
+  if (D == 64) return launch_mfma<64>(a, a.total_q, stream);
   return launch_t<bf16_t>(a, stream);
 }
 

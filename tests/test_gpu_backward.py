@@ -3,7 +3,9 @@ page, attention_packed_gradients): the GPU forward's out and lse, an output
 gradient, then dq, dk, dv on the GPU against the oracle's gradients computed
 from the plain definition in float64.  The GPU gradients read the forward's
 stored (bf16) output and its float32 lse, so the bound is relative to the
-gradients' scale: 2e-2 for bf16 inputs, 1e-4 for float32."""
+gradients' scale: 2e-2 for bf16 inputs, 1e-4 for float32.  bf16 at head
+dims 64 and 128 runs the MFMA kernels (P and dS rounded to bf16 for their
+products), other head dims the float32 VALU kernels."""
 
 import numpy as np
 import pytest
@@ -30,6 +32,15 @@ CASES = {
                                  head_dim=64),
     "causal_f32_d64": dict(q_lens=[9, 30, 1], kv_lens=[9, 45, 12], num_q_heads=4, num_kv_heads=2, head_dim=64,
                            in_dtype="f32", cache_dtype="f32"),
+    # MFMA path: several 128-key and 32-row tiles per segment, ragged tails,
+    # 1, 2 and 4 query heads per KV head
+    "long_causal_bf16_d128_g4": dict(q_lens=[300, 520, 1], kv_lens=[300, 600, 77], num_q_heads=16, num_kv_heads=4,
+                                     head_dim=128),
+    "window100_after7_bf16_d64_p32_g2": dict(q_lens=[260, 3, 190], kv_lens=[400, 3, 190], num_q_heads=4,
+                                             num_kv_heads=2, head_dim=64, page_size=32, window_left=100,
+                                             window_right=7),
+    "window60_sinks8_bf16_d128_mha": dict(q_lens=[150, 150], kv_lens=[150, 300], num_q_heads=2, num_kv_heads=2,
+                                          head_dim=128, window_left=60, sink_keys=8),
 }
 
 
