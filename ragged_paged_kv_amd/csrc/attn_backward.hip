@@ -331,18 +331,12 @@ NK_DEVICE bf16x8_t pack8(const float *x) {
                                               pack2_bf16(x[4], x[5]), pack2_bf16(x[6], x[7])});
 }
 
-// Does the row at position p see key k (band and sink keys as the forward)?
-NK_DEVICE bool sees(const BackwardArgs &a, int p, int L, int k) {
-  const int hi = band_hi(p, L, a.window_right), lo = band_lo(p, a.window_left);
-  const int sinks = a.window_left < 0 ? 0 : a.sink_keys;
-  return k <= hi && (k >= lo || (k < sinks && k < lo && k <= hi));
-}
-
 // Four 16-bit values down a column of a row-major LDS tile: within each
 // 16-lane group, ds_read_b64_tr_b16 hands lane 4a + b element b of the 8
 // bytes addressed by lane 4e + a, as its element e (measured on gfx950).  So
 // if lane j of the group addresses row k0 + j / 4, columns c0 + 4 (j % 4)
-// .. + 3, lane i receives rows k0 .. k0 + 3 of column c0 + i.
+// .. + 3, lane i receives rows k0 .. k0 + 3 of column c0 + i; lds_col8 reads
+// rows k0 .. k0 + 7 (the second half `row_bytes` x 4 further on).
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 NK_DEVICE bf16x8_t lds_col8(const uint8_t *p, int row_bytes) {
   typedef __attribute__((address_space(3))) i16x4_t *lds_ptr;
@@ -432,14 +426,24 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
 #pragma unroll
   for (int c = 0; c < B::DC; ++c) { dk[c] = f32x16_t{}; dv[c] = f32x16_t{}; }
   const float c2 = a.softmax_scale * kLog2e;
+  // positions p of the rows that see this lane's key: p >= key - window_right
+  // (a row sees keys up to p + window_right), p <= key + window_left (its
+  // band starts at p - window_left) unless the key is a sink key, which
+  // every row whose band reaches past it sees; none for keys past the segment
+  const int sinks = a.window_left < 0 ? 0 : a.sink_keys;
+  const int p_min = key >= L ? 1 << 30 : (a.window_right < 0 ? -(1 << 30) : key - a.window_right);
+  const int p_max = (a.window_left < 0 || key < sinks) ? (1 << 30) : key + a.window_left;
 
   // software pipeline over the (row tile, head) pairs: the global loads of
   // pair pr + 1 are in flight while pair pr is computed; LDS is double
   // buffered, so one barrier per pair separates a buffer's writes from its
   // reads (a buffer is rewritten two pairs later, after the next barrier)
-  bf16x8_t gq[B::PER], gd[B::PER], go[B::PER];
-  float glse[B::PER];
-  auto fetch = [&](int pr) {
+  // two pairs of loads in flight: each register set takes turns
+  struct Regs { bf16x8_t q[B::PER], d[B::PER], o[B::PER]; float lse[B::PER]; };
+  Regs R0, R1;
+  auto fetch = [&](int pr, Regs &R) {
+    bf16x8_t *gq = R.q, *gd = R.d, *go = R.o;
+    float *glse = R.lse;
     const int r0 = (rt0 + pr / G) * 32, head = g * G + pr % G;
 #pragma unroll
     for (int i = 0; i < B::PER; ++i) {
@@ -453,7 +457,9 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
       glse[i] = a.lse[rh];
     }
   };
-  auto stage = [&](int pr, uint8_t *buf) {
+  auto stage = [&](int pr, uint8_t *buf, const Regs &R) {
+    const bf16x8_t *gq = R.q, *gd = R.d, *go = R.o;
+    const float *glse = R.lse;
     const int r0 = (rt0 + pr / G) * 32;
 #pragma unroll
     for (int i = 0; i < B::PER; ++i) {
@@ -476,13 +482,12 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
     }
   };
 
-  if (n_pairs > 0) fetch(0);
-  for (int pr = 0; pr < n_pairs; ++pr) {
+  auto step = [&](int pr, Regs &R) {
     const int r0 = (rt0 + pr / G) * 32;
     uint8_t *buf = lds + (pr & 1) * LY::SIZE;
-    stage(pr, buf);
+    stage(pr, buf, R);
     __syncthreads();
-    if (pr + 1 < n_pairs) fetch(pr + 1);
+    if (pr + 2 < n_pairs) fetch(pr + 2, R);
 
     // ---- S = Q K^T and dP = dO V^T (rows permuted)
     f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
@@ -500,14 +505,14 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
     {
       const float *lse2 = (const float *)(buf + LY::LSE);
       const float *dis = (const float *)(buf + LY::DI);
-      // whole tile inside the band (every row valid, every key seen)?
-      const int p_first = r0 + shift, p_last = r0 + 31 + shift;
-      const bool full = r0 + 31 < q_len && k0 + 31 < L && k0 + 31 <= band_hi(p_first, L, a.window_right) &&
-                        k0 >= band_lo(p_last, a.window_left);
+      // tile rows (relative to 8 h) that see the key: [lo_r, hi_r]
+      const int base = r0 + shift + 8 * h;
+      const int lo_r = p_min - base, hi_r = min(p_max - base, q_len - 1 - r0 - 8 * h);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 16 * (v >> 3) + 8 * h + (v & 7);
-        const bool ok = full || (r0 + r < q_len && key < L && sees(a, r0 + r + shift, L, key));
+        const int rv = 16 * (v >> 3) + (v & 7);
+        const bool ok = rv >= lo_r && rv <= hi_r;
         const float pe = ok ? fast_exp2(fmaf(sc[v], c2, -lse2[r])) : 0.f;
         pv[v] = pe;
         dsv[v] = pe * (dp[v] - dis[r]);
@@ -531,6 +536,12 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
         dk[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa1, lds_col8(qbb + 64 * c + 16 * B::RM, B::RM), dk[c], 0, 0, 0);
       }
     }
+  };
+  if (n_pairs > 0) fetch(0, R0);
+  if (n_pairs > 1) fetch(1, R1);
+  for (int pr = 0; pr < n_pairs; pr += 2) {
+    step(pr, R0);
+    if (pr + 1 < n_pairs) step(pr + 1, R1);
   }
 
   // ---- write: output entry v of tile c is key k0 + 8 (v/4) + 4 h + v % 4, dim 32 c + l32
@@ -551,7 +562,12 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
 template <int D>
 struct DqLds {
   using B = BwdTile<D>;
-  static constexpr int K = 0, V = 32 * B::RM, SIZE = 64 * B::RM;
+  // V is staged as the cache stores it, 16-byte runs (4 keys x dims l and
+  // l + 16), with 64 bytes of padding after every 16 runs so that the
+  // transposing reads of one 16-lane group hit distinct banks
+  static constexpr int RUNS = D / 32 * 64;             // runs per 16-key block
+  static NK_DEVICE constexpr int run_at(int run) { return 16 * run + 64 * (run / 16); }
+  static constexpr int K = 0, V = 32 * B::RM, SIZE = V + run_at(2 * RUNS);
 };
 
 template <int D>
@@ -619,26 +635,43 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
 #pragma unroll
   for (int c = 0; c < B::DC; ++c) dq[c] = f32x16_t{};
   const float c2 = a.softmax_scale * kLog2e;
+  // transposing-read source of this lane for the V operand (see the score
+  // loop): key group 4 (lane/16 % 2) + swap(lane % 4), dim 8 h + lane/4 % 4
+  // of a k-step; the second read of an operand (dims + 4) is 4 runs on, 64
+  // bytes (lds_col8's step of 4 rows of 16 bytes)
+  const int va_off = [&] {
+    const int j = lane & 15, a2 = j & 3;
+    const int kg = 4 * ((lane >> 4) & 1) + (((a2 & 1) << 1) | (a2 >> 1));
+    const int sb = kg / 4, gq = kg % 4, l = 8 * h + (j >> 2);
+    return LY::run_at(sb * LY::RUNS + 16 * gq + l);
+  }();
+  // keys the lane's row sees (none for rows past the segment)
+  const int pos = row + shift;
+  const int k_lo = band_lo(pos, a.window_left);
+  const int k_hi = rvalid ? band_hi(pos, L, a.window_right) : -1;
+  const int n_sink = rvalid ? max(0, min(sinks, min(k_lo, k_hi + 1))) : 0;
 
   // software pipeline over the key tiles: the global loads of tile it + 1
   // are in flight while tile it is computed; LDS double buffered (one
   // barrier per tile, as in the dK/dV kernel)
-  bf16x8_t gk[B::PER], gv[B::PER];
   auto tile_base = [&](int it) { return 32 * (it < ns ? it : tb0 + (it - ns)); };
-  constexpr int RUNS = D / 32 * 64;               // V runs per 16-key block (bf16: 2 dim groups per run)
+  constexpr int RUNS = LY::RUNS;
   // this thread's K chunk is key c % 32 (the same key for every i, since
   // 256 is a multiple of 32); its V chunks are runs of the 16-key block i
   const int k_key = tid % 32;
   auto v_key = [&](int i) { const int rr = (tid + 256 * i) % RUNS; return 16 * ((tid + 256 * i) / RUNS) + 4 * ((rr % 64) / 16); };
-  // page ids of a tile's chunks, read one tile ahead of its data
-  int pk_page = 0, pv_page[B::PER];
-  auto fetch_pages = [&](int it) {
+  // two register sets take turns: a set holds the data of tile t (loaded
+  // two tiles ahead of its use) and the page ids of tile t + 2 (read two
+  // tiles ahead of the data that needs them)
+  struct Regs { bf16x8_t k[B::PER], v[B::PER]; int pk, pv[B::PER]; };
+  Regs RA, RB;
+  auto fetch_pages = [&](int it, Regs &R) {
     const int kb = tile_base(it);
-    pk_page = pt[min(kb + k_key, L - 1) / P];
+    R.pk = pt[min(kb + k_key, L - 1) / P];
 #pragma unroll
-    for (int i = 0; i < B::PER; ++i) pv_page[i] = pt[min(kb + v_key(i), L - 1) / P];
+    for (int i = 0; i < B::PER; ++i) R.pv[i] = pt[min(kb + v_key(i), L - 1) / P];
   };
-  auto fetch = [&](int it) {
+  auto fetch = [&](int it, Regs &R) {
     const int kb = tile_base(it);
 #pragma unroll
     for (int i = 0; i < B::PER; ++i) {
@@ -646,18 +679,19 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
       {
         // keys past the segment read its last key (in bounds) and are zeroed when staged
         const int k = min(kb + k_key, L - 1), d0 = 8 * (c / 32);
-        const size_t blk = ((size_t)pk_page * hkv + g) * P * D;
-        gk[i] = *(const bf16x8_t *)((const bf16_t *)a.cache.k_pages + blk + k_elem<bf16_t>(d0, k % P, P));
+        const size_t blk = ((size_t)R.pk * hkv + g) * P * D;
+        R.k[i] = *(const bf16x8_t *)((const bf16_t *)a.cache.k_pages + blk + k_elem<bf16_t>(d0, k % P, P));
       }
       {
         const int rr = c % RUNS, cg = rr / 64, l = rr % 16;
         const int k = min(kb + v_key(i), L - 1);   // the run's 4 keys share a page
-        const size_t blk = ((size_t)pv_page[i] * hkv + g) * P * D;
-        gv[i] = *(const bf16x8_t *)((const bf16_t *)a.cache.v_pages + blk + v_elem<bf16_t>(32 * cg + l, (k % P) & ~3, D));
+        const size_t blk = ((size_t)R.pv[i] * hkv + g) * P * D;
+        R.v[i] = *(const bf16x8_t *)((const bf16_t *)a.cache.v_pages + blk + v_elem<bf16_t>(32 * cg + l, (k % P) & ~3, D));
       }
     }
   };
-  auto stage = [&](int it, uint8_t *buf) {
+  auto stage = [&](int it, uint8_t *buf, const Regs &R) {
+    const bf16x8_t *gk = R.k, *gv = R.v;
     const int kb = tile_base(it);
 #pragma unroll
     for (int i = 0; i < B::PER; ++i) {
@@ -667,53 +701,58 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
         *(bf16x8_t *)(buf + LY::K + kr * B::RM + 2 * d0) = kb + kr < L ? gk[i] : bf16x8_t{};
       }
       {
-        const int sb = c / RUNS, rr = c % RUNS, cg = rr / 64, Ln = rr % 64, gq = Ln / 16, l = Ln % 16;
-        const int kr0 = 16 * sb + 4 * gq;
+        // run c of the tile (its two 16-key blocks in page order); keys past
+        // the segment become zeros
+        const int lim = L - (kb + v_key(i));
+        u32x4_t x = __builtin_bit_cast(u32x4_t, gv[i]);
+        if (lim < 4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = kb + kr0 + e < L;
-          *(bf16_t *)(buf + LY::V + (kr0 + e) * B::RM + 2 * (32 * cg + l)) = ok ? gv[i][e] : (bf16_t)0.f;
-          *(bf16_t *)(buf + LY::V + (kr0 + e) * B::RM + 2 * (32 * cg + 16 + l)) = ok ? gv[i][4 + e] : (bf16_t)0.f;
+          for (int w2 = 0; w2 < 4; ++w2) {
+            const int k = 2 * (w2 & 1);                     // words 0, 1: dim l keys 0-3; 2, 3: dim l + 16
+            x[w2] &= (k < lim ? 0xffffu : 0u) | (k + 1 < lim ? 0xffff0000u : 0u);
+          }
         }
+        *(u32x4_t *)(buf + LY::V + LY::run_at(c)) = x;
       }
     }
   };
 
-  if (n_tiles > 0) {
-    fetch_pages(0);
-    fetch(0);
-    if (n_tiles > 1) fetch_pages(1);
-  }
-  for (int it = 0; it < n_tiles; ++it) {
+  auto step = [&](int it, Regs &R) {
     const int kb = tile_base(it);
     uint8_t *buf = lds + (it & 1) * LY::SIZE;
-    stage(it, buf);
+    stage(it, buf, R);
     __syncthreads();
-    if (it + 1 < n_tiles) {
-      fetch(it + 1);
-      if (it + 2 < n_tiles) fetch_pages(it + 2);
+    if (it + 2 < n_tiles) {
+      fetch(it + 2, R);
+      if (it + 4 < n_tiles) fetch_pages(it + 4, R);
     }
 
     const bool act = w_active && kb <= w_hi && (kb + 31 >= w_lo || kb < sinks);
     if (act) {
+      const uint8_t *va = buf + LY::V + va_off;
       // ---- S^T = K Q^T and dP^T = V dO^T (keys permuted)
       f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
       const uint8_t *ka = buf + LY::K + bperm(l32) * B::RM + 16 * h;
-      const uint8_t *va = buf + LY::V + bperm(l32) * B::RM + 16 * h;
 #pragma unroll
       for (int kk = 0; kk < B::KD; ++kk) {
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(ka + 32 * kk), qb[kk], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(va + 32 * kk), db[kk], dp, 0, 0, 0);
+        // A = V rows of keys bperm(l32), dims 16 kk + 8 h ..: transposing
+        // reads of the runs (lane 4 e + a of a group addresses the run of
+        // dim 16 kk + 8 h + e for the key group that output lanes 4 a ..
+        // 4 a + 3 need)
+        const int off = 1280 * (kk / 2) + 8 * (kk % 2);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_col8(va + off, 16), db[kk], dp, 0, 0, 0);
       }
       // entry v: key kb + 16 (v/8) + 8 h + v % 8 of row `row`
-      const int pos = row + shift;
-      const bool full = r0 + 31 < q_len && kb + 31 < L && kb + 31 <= band_hi(r0 + shift, L, a.window_right) &&
-                        kb >= band_lo(r0 + 31 + shift, a.window_left);
+      // the lane's row sees keys [k_lo, k_hi] and the sink keys below n_sink;
+      // relative to kb + 8 h
+      const int base = kb + 8 * h;
+      const int lo_k = k_lo - base, hi_k = k_hi - base, sk_k = n_sink - base;
       float dsv[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int k = kb + 16 * (v >> 3) + 8 * h + (v & 7);
-        const bool ok = full || (rvalid && k < L && sees(a, pos, L, k));
+        const int kv = 16 * (v >> 3) + (v & 7);
+        const bool ok = (kv >= lo_k && kv <= hi_k) || kv < sk_k;
         const float pe = ok ? fast_exp2(fmaf(sc[v], c2, -lse2)) : 0.f;
         dsv[v] = pe * (dp[v] - di);
       }
@@ -728,6 +767,16 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
         dq[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa1, lds_col8(kb_ + 64 * c + 16 * B::RM, B::RM), dq[c], 0, 0, 0);
       }
     }
+  };
+  if (n_tiles > 0) fetch_pages(0, RA);
+  if (n_tiles > 1) fetch_pages(1, RB);
+  if (n_tiles > 0) fetch(0, RA);
+  if (n_tiles > 1) fetch(1, RB);
+  if (n_tiles > 2) fetch_pages(2, RA);
+  if (n_tiles > 3) fetch_pages(3, RB);
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(it, RA);
+    if (it + 1 < n_tiles) step(it + 1, RB);
   }
 
   // ---- write: entry v of tile c is row r0 + 8 (v/4) + 4 h + v % 4, dim 32 c + l32
