@@ -40,7 +40,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
-FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s
 FLUSH_BYTES = 1 << 30
 HIP_EVENT_NO_SYSTEM_FENCE = 0x20000000     # hipEventDisableSystemFence
 
@@ -77,7 +76,10 @@ FAMILY_SOURCES = {
     "attn_decode": ["attn_decode.hip", "common.h", "internal.h"],
     "attn_prefill": ["attn_prefill.hip", "common.h", "internal.h"],
     "rope_write": ["rope_write.hip", "common.h", "internal.h"],
+    "pack_kernel": ["rope_write.hip", "common.h", "internal.h"],
+    "_mfma_kernel": ["attn_backward.hip", "common.h", "internal.h"],
 }
+KERNEL_SOURCES = KERNEL_SOURCES + ["attn_backward.hip"]
 
 
 def family_sources(kernel_name):
@@ -562,6 +564,11 @@ def cpu_cores():
 
 
 # ------------------------------------------------------------------ counters
+# the counter summary (profiles/traffic_KEY.json) of each workload's HBM-bound kernel
+TRAFFIC_KEYS = {"decode_bf16": "decode_bf16", "decode_fp8": "decode_fp8", "mixed_window_bf16": "decode_d256",
+                "prefill_bf16": "rope_prefill", "pack_bf16": "pack"}
+
+
 def load_traffic(kernel_key):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
     were taken on the current kernel sources."""
@@ -720,8 +727,12 @@ def main():
         import synth
         from synth import work
         db, out = args.rocpd_mfma
-        rec = rocpd_mfma(db, args.pmc_kernel, args.simds, args.gui_instances,
-                         work.prefill_flops(synth.make(args.mfma_workload)))
+        if args.mfma_workload == "prefill_backward_bf16":
+            # gradients: 10 D per visible (row, head, key) against the forward's 4 D
+            flops = work.prefill_flops(synth.make("prefill_bf16")) * 10 // 4
+        else:
+            flops = work.prefill_flops(synth.make(args.mfma_workload))
+        rec = rocpd_mfma(db, args.pmc_kernel, args.simds, args.gui_instances, flops)
         with open(out, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec, indent=1))
@@ -810,7 +821,7 @@ def main():
         e = {"ms_per_step": r["ms_per_step"], "kernels": r["kernels"], "split_tokens": r.get("split_tokens")}
         if r.get("backward_TFLOPs_kernel"):
             e["backward_TFLOPs_kernel"] = r["backward_TFLOPs_kernel"]
-            e["backward_fp32_valu_frac"] = r["backward_TFLOPs_kernel"] / FP32_VALU_PEAK_TFLOPS
+            e["backward_mfma_frac"] = r["backward_TFLOPs_kernel"] / BF16_PEAK_TFLOPS
         if r.get("pack_GBps_kernel"):
             e["pack_GBps_kernel"] = r["pack_GBps_kernel"]
             e["pack_hbm_frac"] = r["pack_GBps_kernel"] / HBM_PEAK_GBS
@@ -831,6 +842,16 @@ def main():
             if t_attn > 0:
                 ideal = r["decode_bytes"] / (HBM_PEAK_GBS * 1e9) + r["prefill_flops"] / (BF16_PEAK_TFLOPS * 1e12)
                 e["combined_roofline_frac"] = ideal / t_attn
+        key = TRAFFIC_KEYS.get(n)
+        traffic = load_traffic(key) if key else None
+        if traffic:
+            # HBM bytes per launch of the workload's HBM-bound kernel, from the
+            # committed counter summary, over its algorithmic bytes
+            alg = {"decode_bf16": r.get("decode_bytes"), "decode_fp8": r.get("decode_bytes"),
+                   "mixed_window_bf16": r.get("decode_bytes"), "prefill_bf16": r.get("rope_bytes"),
+                   "pack_bf16": r.get("pack_bytes")}.get(n)
+            e["traffic"] = {"kernel_key": key, "bytes_per_launch": traffic,
+                            "over_algorithmic": traffic / alg if alg else None}
         if n in cpu_all:
             e["cpu_baseline"] = cpu_all[n]
         extra[n] = e

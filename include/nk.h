@@ -400,8 +400,11 @@ int nk_attention_pack(const void *k, const void *v, int32_t in_dtype, const int3
  * The pages call these bf16 gradients yet take a float32 query-gradient
  * buffer; all three are float32 here (a bf16 copy is one rounding away).
  * Types: q_dtype NK_F32 with an NK_F32 cache, NK_BF16 with NK_BF16;
- * e4m3 caches return NK_ERR_UNSUPPORTED.  Two kernels on `stream`, no
- * workspace, no allocation.  Errors as nk_ragged_paged_attention_band.
+ * e4m3 caches return NK_ERR_UNSUPPORTED.  bf16 at head_dim 64 and 128 runs
+ * on bf16 MFMA (the probabilities and dS rounded to bf16 for their products,
+ * float32 accumulation); other cases in float32 throughout.  Two kernels on
+ * `stream`, no workspace, no allocation.  Errors as
+ * nk_ragged_paged_attention_band.
  */
 int nk_ragged_paged_attention_backward(const void *q, int32_t q_dtype, const int32_t *q_offsets,
                                        const int32_t *kv_lens, const nk_paged_kv_t *cache, float softmax_scale,

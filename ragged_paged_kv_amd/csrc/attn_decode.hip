@@ -158,8 +158,10 @@ NK_DEVICE void load_page(Page<D, FP8> &pg, const nk_paged_kv_t &c, int page, int
   if constexpr (FP8) {
     const uint8_t *sk = (const uint8_t *)(c.k_scales + ph * P + sb);
     const uint8_t *sv = (const uint8_t *)(c.v_scales + ph * P + sb);
-    pg.ks = stream_load<NK_DECODE_NT_FP8>((const f32x4_t *)(sk + lo.sc));
-    pg.vs = stream_load<NK_DECODE_NT_FP8>((const f32x4_t *)(sv + lo.sc));
+    // the scales of a page's heads share cache lines read by the waves of
+    // the other heads: ordinary loads let those reads hit (measured +2 %)
+    pg.ks = stream_load<false>((const f32x4_t *)(sk + lo.sc));
+    pg.vs = stream_load<false>((const f32x4_t *)(sv + lo.sc));
   }
 }
 
