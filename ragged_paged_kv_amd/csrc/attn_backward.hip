@@ -309,8 +309,8 @@ __global__ void __launch_bounds__(64) attn_dkv_kernel(BackwardArgs a, int blocks
 //     heads of one KV head (Q and dO held as operands) and walks the 32-key
 //     tiles the rows see, staging K and V row-major (dQ = dS K reads down
 //     K's columns).
-// Both pipelines prefetch the next tile's global data into registers while
-// the current one is computed, into a second LDS buffer.
+// Both pipelines load the next tile's global data into registers while the
+// current one is computed (LDS double buffered, one barrier per tile).
 // Row (dK/dV) or key (dQ) order inside a tile is permuted (bits 2 and 3 of
 // the index swapped) for the score products, which makes their output lane
 // layout the A operand layout of the next product: P and dS never move
@@ -367,16 +367,19 @@ struct DkvLds {
 };
 
 template <int D>
-__global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int tiles_per_seq) {
+__global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int tiles_per_seq, int HC) {
   using B = BwdTile<D>;
   using LY = DkvLds<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];      // two buffers of LY::SIZE
   // KV head fastest (consecutive work-groups go to different XCDs, so each
-  // XCD's L2 holds the rows of its own heads), then segment, then key tile:
-  // a causal segment's first key tiles carry the most rows, so every
-  // segment's heaviest work-groups are dispatched first
+  // XCD's L2 holds the rows of its own heads), then head chunk, segment and
+  // key tile: a causal segment's first key tiles carry the most rows, so
+  // every segment's heaviest work-groups are dispatched first.  With HC > 1
+  // the G query heads of a KV head are split into HC chunks on separate
+  // work-groups, which add their dK/dV into the (zeroed) outputs.
   const int nh = a.cache.num_kv_heads;
-  const int g = blockIdx.x % nh, rest = blockIdx.x / nh;
+  const int g = blockIdx.x % nh, rest0 = blockIdx.x / nh;
+  const int hc = rest0 % HC, rest = rest0 / HC;
   const int s = rest % a.num_seqs, kt0 = (rest / a.num_seqs) * 128;
   const int L = a.kv_lens[s];
   if (kt0 >= L) return;
@@ -420,7 +423,8 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
   const int i_max = (a.window_left < 0 || sink) ? q_len - 1
                                                  : (int)min((long long)q_len - 1, (long long)kmax + a.window_left - shift);
   const int rt0 = i_min / 32, rt1 = i_max < i_min ? rt0 - 1 : i_max / 32;
-  const int n_pairs = (rt1 - rt0 + 1) * G;
+  const int Gc = G / HC;                        // query heads of this work-group: g G + hc Gc ..
+  const int n_pairs = (rt1 - rt0 + 1) * Gc;
 
   f32x16_t dk[B::DC], dv[B::DC];
 #pragma unroll
@@ -438,13 +442,13 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
   // pair pr + 1 are in flight while pair pr is computed; LDS is double
   // buffered, so one barrier per pair separates a buffer's writes from its
   // reads (a buffer is rewritten two pairs later, after the next barrier)
-  // two pairs of loads in flight: each register set takes turns
+  // the loads of pair pr + 1 are in flight while pair pr is computed
   struct Regs { bf16x8_t q[B::PER], d[B::PER], o[B::PER]; float lse[B::PER]; };
-  Regs R0, R1;
+  Regs R0;
   auto fetch = [&](int pr, Regs &R) {
     bf16x8_t *gq = R.q, *gd = R.d, *go = R.o;
     float *glse = R.lse;
-    const int r0 = (rt0 + pr / G) * 32, head = g * G + pr % G;
+    const int r0 = (rt0 + pr / Gc) * 32, head = g * G + hc * Gc + pr % Gc;
 #pragma unroll
     for (int i = 0; i < B::PER; ++i) {
       const int c = tid + 256 * i;
@@ -460,7 +464,7 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
   auto stage = [&](int pr, uint8_t *buf, const Regs &R) {
     const bf16x8_t *gq = R.q, *gd = R.d, *go = R.o;
     const float *glse = R.lse;
-    const int r0 = (rt0 + pr / G) * 32;
+    const int r0 = (rt0 + pr / Gc) * 32;
 #pragma unroll
     for (int i = 0; i < B::PER; ++i) {
       const int c = tid + 256 * i;
@@ -483,11 +487,11 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
   };
 
   auto step = [&](int pr, Regs &R) {
-    const int r0 = (rt0 + pr / G) * 32;
+    const int r0 = (rt0 + pr / Gc) * 32;
     uint8_t *buf = lds + (pr & 1) * LY::SIZE;
     stage(pr, buf, R);
     __syncthreads();
-    if (pr + 2 < n_pairs) fetch(pr + 2, R);
+    if (pr + 1 < n_pairs) fetch(pr + 1, R);
 
     // ---- S = Q K^T and dP = dO V^T (rows permuted)
     f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
@@ -503,19 +507,32 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
     // ---- P and dS: entry v is row 16 (v/8) + 8 h + v % 8 of the tile, key `key`
     float pv[16], dsv[16];
     {
-      const float *lse2 = (const float *)(buf + LY::LSE);
-      const float *dis = (const float *)(buf + LY::DI);
+      // the log-sum-exp and dO.O of rows 8 h + rl (rl = 0..7, 16..23) as
+      // 16-byte reads
+      float lse2[24], dis[24];
+      {
+        const f32x4_t *l4 = (const f32x4_t *)(buf + LY::LSE), *d4 = (const f32x4_t *)(buf + LY::DI);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int rl0 = 16 * (q4 >> 1) + 4 * (q4 & 1);
+          const f32x4_t lv = l4[(rl0 >> 2) + 2 * h], dv4 = d4[(rl0 >> 2) + 2 * h];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { lse2[rl0 + e] = lv[e]; dis[rl0 + e] = dv4[e]; }
+        }
+      }
       // tile rows (relative to 8 h) that see the key: [lo_r, hi_r]
       const int base = r0 + shift + 8 * h;
       const int lo_r = p_min - base, hi_r = min(p_max - base, q_len - 1 - r0 - 8 * h);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = 16 * (v >> 3) + 8 * h + (v & 7);
-        const int rv = 16 * (v >> 3) + (v & 7);
-        const bool ok = rv >= lo_r && rv <= hi_r;
-        const float pe = ok ? fast_exp2(fmaf(sc[v], c2, -lse2[r])) : 0.f;
+        const int rl = 16 * (v >> 3) + (v & 7);
+        const bool ok = rl >= lo_r && rl <= hi_r;
+        // exp of every entry, then a select: no branch per entry (the scores of
+        // entries not seen are finite, and rows past the segment have lse +inf)
+        const float ex = fast_exp2(fmaf(sc[v], c2, -lse2[rl]));
+        const float pe = ok ? ex : 0.f;
         pv[v] = pe;
-        dsv[v] = pe * (dp[v] - dis[r]);
+        dsv[v] = pe * (dp[v] - dis[rl]);
       }
     }
     // ---- dV += P^T dO and dK += dS^T Q (contraction over the tile's rows)
@@ -538,11 +555,7 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
     }
   };
   if (n_pairs > 0) fetch(0, R0);
-  if (n_pairs > 1) fetch(1, R1);
-  for (int pr = 0; pr < n_pairs; pr += 2) {
-    step(pr, R0);
-    if (pr + 1 < n_pairs) step(pr + 1, R1);
-  }
+  for (int pr = 0; pr < n_pairs; ++pr) step(pr, R0);
 
   // ---- write: output entry v of tile c is key k0 + 8 (v/4) + 4 h + v % 4, dim 32 c + l32
 #pragma unroll
@@ -552,8 +565,13 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
     const size_t orow = ((size_t)a.key_offsets[s] + kk) * hkv + g;
 #pragma unroll
     for (int c = 0; c < B::DC; ++c) {
-      a.dk[orow * D + 32 * c + l32] = a.softmax_scale * dk[c][v];
-      a.dv[orow * D + 32 * c + l32] = dv[c][v];
+      if (HC == 1) {
+        a.dk[orow * D + 32 * c + l32] = a.softmax_scale * dk[c][v];
+        a.dv[orow * D + 32 * c + l32] = dv[c][v];
+      } else {
+        unsafeAtomicAdd(a.dk + orow * D + 32 * c + l32, a.softmax_scale * dk[c][v]);
+        unsafeAtomicAdd(a.dv + orow * D + 32 * c + l32, dv[c][v]);
+      }
     }
   }
 }
@@ -571,7 +589,7 @@ struct DqLds {
 };
 
 template <int D>
-__global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int blocks_per_seq, int GW) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) attn_dq_mfma_kernel(BackwardArgs a, int blocks_per_seq, int GW) {
   using B = BwdTile<D>;
   using LY = DqLds<D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * LY::SIZE];   // two buffers
@@ -660,11 +678,11 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
   // 256 is a multiple of 32); its V chunks are runs of the 16-key block i
   const int k_key = tid % 32;
   auto v_key = [&](int i) { const int rr = (tid + 256 * i) % RUNS; return 16 * ((tid + 256 * i) / RUNS) + 4 * ((rr % 64) / 16); };
-  // two register sets take turns: a set holds the data of tile t (loaded
-  // two tiles ahead of its use) and the page ids of tile t + 2 (read two
-  // tiles ahead of the data that needs them)
+  // the registers hold the data of tile t (loaded one tile ahead of its
+  // use) and the page ids of tile t + 1 (read one tile ahead of the data
+  // that needs them)
   struct Regs { bf16x8_t k[B::PER], v[B::PER]; int pk, pv[B::PER]; };
-  Regs RA, RB;
+  Regs RA;
   auto fetch_pages = [&](int it, Regs &R) {
     const int kb = tile_base(it);
     R.pk = pt[min(kb + k_key, L - 1) / P];
@@ -722,9 +740,9 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
     uint8_t *buf = lds + (it & 1) * LY::SIZE;
     stage(it, buf, R);
     __syncthreads();
-    if (it + 2 < n_tiles) {
-      fetch(it + 2, R);
-      if (it + 4 < n_tiles) fetch_pages(it + 4, R);
+    if (it + 1 < n_tiles) {
+      fetch(it + 1, R);
+      if (it + 2 < n_tiles) fetch_pages(it + 2, R);
     }
 
     const bool act = w_active && kb <= w_hi && (kb + 31 >= w_lo || kb < sinks);
@@ -753,7 +771,8 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
       for (int v = 0; v < 16; ++v) {
         const int kv = 16 * (v >> 3) + (v & 7);
         const bool ok = (kv >= lo_k && kv <= hi_k) || kv < sk_k;
-        const float pe = ok ? fast_exp2(fmaf(sc[v], c2, -lse2)) : 0.f;
+        const float ex = fast_exp2(fmaf(sc[v], c2, -lse2));
+        const float pe = ok ? ex : 0.f;
         dsv[v] = pe * (dp[v] - di);
       }
       // ---- dQ += dS K: A = dS (row l32, keys of k-step s), B = keys
@@ -768,16 +787,12 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
       }
     }
   };
-  if (n_tiles > 0) fetch_pages(0, RA);
-  if (n_tiles > 1) fetch_pages(1, RB);
-  if (n_tiles > 0) fetch(0, RA);
-  if (n_tiles > 1) fetch(1, RB);
-  if (n_tiles > 2) fetch_pages(2, RA);
-  if (n_tiles > 3) fetch_pages(3, RB);
-  for (int it = 0; it < n_tiles; it += 2) {
-    step(it, RA);
-    if (it + 1 < n_tiles) step(it + 1, RB);
+  if (n_tiles > 0) {
+    fetch_pages(0, RA);
+    fetch(0, RA);
+    if (n_tiles > 1) fetch_pages(1, RA);
   }
+  for (int it = 0; it < n_tiles; ++it) step(it, RA);
 
   // ---- write: entry v of tile c is row r0 + 8 (v/4) + 4 h + v % 4, dim 32 c + l32
   if (!w_active) return;
@@ -788,6 +803,22 @@ __global__ void __launch_bounds__(256) attn_dq_mfma_kernel(BackwardArgs a, int b
     float *drow = a.dq + ((size_t)(q0 + r) * a.hq + head) * D;
 #pragma unroll
     for (int c = 0; c < B::DC; ++c) drow[32 * c + l32] = a.softmax_scale * dq[c][v];
+  }
+}
+
+// Zeros of the dK/dV rows of every segment's keys (rows key_offsets[s] ..
+// key_offsets[s] + kv_lens[s] - 1), before work-groups add into them: one
+// work-group per (segment, 16 keys).
+__global__ void __launch_bounds__(256) bwd_zero_kernel(BackwardArgs a, int per_seq) {
+  const int s = blockIdx.x / per_seq, k0 = (blockIdx.x % per_seq) * 16;
+  const int L = a.kv_lens[s];
+  if (k0 >= L) return;
+  const int width = a.cache.num_kv_heads * a.cache.head_dim;      // floats per key row, a multiple of 4
+  const size_t first = ((size_t)a.key_offsets[s] + k0) * width;
+  const int n4 = min(16, L - k0) * width / 4;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    ((f32x4_t *)(a.dk + first))[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    ((f32x4_t *)(a.dv + first))[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -805,8 +836,19 @@ hipError_t launch_mfma(const BackwardArgs &a, int max_q_len, hipStream_t stream)
     e = launch(attn_dq_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, a, per_seq, GW);
   }
   if (e != hipSuccess || a.max_kv_len == 0) return e;
+  // query heads of a KV head split over HC work-groups (a power of two
+  // dividing G, at most 4): shorter work-groups, added into zeroed outputs
+  int HC = 1;
+  while (HC * 2 <= 4 && G % (HC * 2) == 0) HC *= 2;
+  if (HC > 1) {
+    const int zper = (a.max_kv_len + 15) / 16;
+    const long long zblocks = (long long)a.num_seqs * zper;
+    if (zblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    e = launch(bwd_zero_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, a, zper);
+    if (e != hipSuccess) return e;
+  }
   const int per_seq = (a.max_kv_len + 127) / 128;
-  const long long blocks = (long long)a.num_seqs * per_seq * hkv;
+  const long long blocks = (long long)a.num_seqs * per_seq * hkv * HC;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   static bool attr_set[64];                     // per device; idempotent, a race only repeats the call
   int dev = 0;
@@ -818,7 +860,7 @@ hipError_t launch_mfma(const BackwardArgs &a, int max_q_len, hipStream_t stream)
     if (e != hipSuccess) return e;
     attr_set[dev & 63] = true;
   }
-  return launch(attn_dkv_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), DkvLds<D>::TOTAL, stream, a, per_seq);
+  return launch(attn_dkv_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), DkvLds<D>::TOTAL, stream, a, per_seq, HC);
 }
 
 template <typename T>
