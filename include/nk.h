@@ -402,7 +402,10 @@ int nk_attention_pack(const void *k, const void *v, int32_t in_dtype, const int3
  * Types: q_dtype NK_F32 with an NK_F32 cache, NK_BF16 with NK_BF16;
  * e4m3 caches return NK_ERR_UNSUPPORTED.  bf16 at head_dim 64 and 128 runs
  * on bf16 MFMA (the probabilities and dS rounded to bf16 for their products,
- * float32 accumulation); other cases in float32 throughout.  Two kernels on
+ * float32 accumulation); there, with two or more query heads per KV head,
+ * the dk/dv rows are zeroed and then summed over head groups with float
+ * atomic adds, so their last bits can differ from call to call.  Other cases
+ * run in float32 throughout and are deterministic.  Up to three kernels on
  * `stream`, no workspace, no allocation.  Errors as
  * nk_ragged_paged_attention_band.
  */
