@@ -41,6 +41,8 @@ CASES = {
                                              window_right=7),
     "window60_sinks8_bf16_d128_mha": dict(q_lens=[150, 150], kv_lens=[150, 300], num_q_heads=2, num_kv_heads=2,
                                           head_dim=128, window_left=60, sink_keys=8),
+    # one query head per KV head at head_dim 64 (dK/dV written directly)
+    "mha_bf16_d64_p16": dict(q_lens=[100, 64], kv_lens=[100, 130], num_q_heads=2, num_kv_heads=2, head_dim=64),
     # 16 query heads per KV head: 4 head chunks of 4 adding into dK/dV
     "causal_bf16_d64_g16": dict(q_lens=[200, 45], kv_lens=[260, 45], num_q_heads=32, num_kv_heads=2, head_dim=64,
                                 page_size=32),
