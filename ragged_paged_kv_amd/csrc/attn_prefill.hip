@@ -16,9 +16,9 @@
 //
 // Design (MFMA-bound):
 //   * a work-group owns BM query rows of one segment and GW query heads of one
-//     KV head (each wave owns 32 rows of one head; at head_dim 256 two waves
-//     share a row block, each computing the full scores and holding half of
-//     the output dims), so every K/V tile staged in LDS serves all GW heads;
+//     KV head (each wave owns 32 rows of one head; at head_dim 256 each wave
+//     owns 16 rows, whose scores and full 256-dim output fit its registers),
+//     so every K/V tile staged in LDS serves all GW heads;
 //   * KV tiles of 64 keys (four 16-token or two 32-token pages).  Each page's
 //     K or V block of one head is contiguous in the cache, so a wave's load
 //     instruction reads one contiguous 1 KiB (bf16) piece of one page, at a
@@ -32,7 +32,9 @@
 //     K rows sit in LDS in a permuted key order (bits 2 and 3 of the key
 //     swapped) that makes the score tile's lane layout the P^T operand layout
 //     of the second product O^T += V^T P^T (32 dims x 32 rows), so the
-//     probabilities never leave their lanes;
+//     probabilities never leave their lanes.  16-row waves use
+//     v_mfma_f32_16x16x32_bf16 (16 keys x 16 rows; 16 dims x 16 rows) with K
+//     in key order and the V^T columns permuted instead;
 //   * software pipeline: K runs one tile ahead of V; K and V tiles are
 //     double-buffered and the global loads of tiles t+3 (K) and t+2 (V) are
 //     in flight during iteration t.  Where two waves share a SIMD (8 waves
@@ -73,6 +75,14 @@
 // work-group; 2 = 8 waves, two per SIMD, each holding half of O)
 #ifndef NK_PREFILL_D256_SPLIT
 #define NK_PREFILL_D256_SPLIT 2
+#endif
+// Query rows per wave: 32 (v_mfma_f32_32x32x16_bf16 tiles) or 16
+// (v_mfma_f32_16x16x32_bf16 tiles), for head dims up to 128 and for 256
+#ifndef NK_PREFILL_RW
+#define NK_PREFILL_RW 32
+#endif
+#ifndef NK_PREFILL_D256_RW
+#define NK_PREFILL_D256_RW 16
 #endif
 // LDS operand reads in flight ahead of the MFMA that consumes them (head
 // dims up to 128; 256 has no registers to spare)
@@ -137,6 +147,38 @@ NK_DEVICE float halves_sum(float v) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// the same over the four 16-lane rows (l, l ^ 16, l ^ 32, l ^ 48):
+// v_permlane16_swap first exchanges rows 0/1 and 2/3
+NK_DEVICE float quarters_max(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return halves_max(fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])));
+}
+
+NK_DEVICE float quarters_sum(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return halves_sum(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+// One MFMA tile: 32 x 32 (k 16) or 16 x 16 (k 32), chosen by the accumulator
+NK_DEVICE f32x16_t mma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+NK_DEVICE f32x4_t mma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS column of V^T that holds key k of a tile, 16-row waves: within each
+// 32 keys, key 16h + 4q + i goes to column 8q + 4h + i, so that the 8
+// columns a lane reads for the P.V product's k-step hold the keys of its
+// score entries (keys 4q.. of both 16-key subtiles).  32-row waves keep
+// V^T in key order and permute the K rows instead.
+template <int RW>
+NK_DEVICE constexpr int v_column(int k) {
+  return RW == 32 ? k : (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
+
 NK_DEVICE float dot2_ones(uint32_t pk, float acc) {
   const bf16x2_t ones = {(bf16_t)1.0f, (bf16_t)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, acc, false);
@@ -149,26 +191,37 @@ NK_DEVICE int sink_tiles(int sink_keys, int tb0, int bn) {
   return sink_keys > 0 ? min((sink_keys + bn - 1) / bn, tb0) : 0;
 }
 
+// Output dims split over the waves of a row block (32-row waves at head_dim
+// 256 only)
+template <int D, int RW>
+constexpr int out_split() { return D == 256 && RW == 32 ? NK_PREFILL_D256_SPLIT : 1; }
+
 // One work item: BM query rows (q-block qb) of segment s for the GW query
 // heads of head block hy (KV head hy / HB).  Every thread of the work-group
-// calls it with the same arguments.
-template <int D, int P, bool FP8, int NW, bool SINKS>
+// calls it with the same arguments.  A wave owns RW rows of one head.
+template <int D, int P, bool FP8, int NW, int RW, bool SINKS>
 NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, int q_len, int L, int hy,
                             uint8_t *lds) {
   using C = Cfg<D, P, FP8, NW>;
+  using Acc = typename std::conditional<RW == 32, f32x16_t, f32x4_t>::type;
   constexpr int NT = C::NT;
-  constexpr int KD = D / 16;      // k-steps of the score MFMA (16 dims each)
-  constexpr int DH = D == 256 ? NK_PREFILL_D256_SPLIT : 1;   // waves sharing a row block's output dims
-  constexpr int DT = D / 32 / DH; // 32-dim tiles of the output MFMA held by a wave
+  constexpr int KW = 512 / RW;    // dims (score product) or keys (P.V) per MFMA k-step: 16 or 32
+  constexpr int KD = D / KW;      // k-steps of the score MFMA
+  constexpr int NSB = BN / RW;    // score subtiles (RW keys each) per tile
+  constexpr int NA = RW * RW / 64; // accumulator entries per lane per subtile (16 or 4)
+  constexpr int DH = out_split<D, RW>();   // waves sharing a row block's output dims
+  constexpr int DT = D / RW / DH; // RW-dim tiles of the output MFMA held by a wave
   constexpr int PER = C::PER;
   constexpr int NPG = C::NPG;
+  static_assert(sizeof(Acc) == NA * sizeof(float), "accumulator entries per lane");
+  static_assert(RW * DT * DH == D, "output tiles cover the head dims");
   using Raw = typename std::conditional<FP8, u32x2_t, bf16x8_t>::type;
 
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
   const int HB = G / GW;                      // head blocks per KV head
-  const int TB = NW / (GW * DH);              // 32-row blocks per work-group
-  const int BM = 32 * TB;
+  const int TB = NW / (GW * DH);              // RW-row blocks per work-group
+  const int BM = RW * TB;
   const int g = hy / HB;
   const int hblk = hy % HB;
 
@@ -195,9 +248,9 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const int dh = (wv / GW) % DH;              // which part of the output dims
   const int tb = wv / (GW * DH);
   const int head = g * G + hblk * GW + hl;
-  const int rw = r0 + 32 * tb;                // wave's first row
-  const int qcol = lane & 31;                 // this lane's query row (column of S^T)
-  const int half = lane >> 5;
+  const int rw = r0 + RW * tb;                // wave's first row
+  const int qcol = lane % RW;                 // this lane's query row (column of S^T)
+  const int half = lane / RW;                 // which 8 elements of a k-step the lane holds
   const int my_row = rw + qcol;
   const bool row_valid = my_row < q_len;
   const int my_pos = my_row + shift;
@@ -205,11 +258,11 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   const int my_hi = band_hi(my_pos, L, a.window_right);
   // the wave's key range (over its valid rows)
   const bool wave_active = rw < q_len;
-  const int w_rows_last = min(rw + 31, q_len - 1);
+  const int w_rows_last = min(rw + RW - 1, q_len - 1);
   const int wk_hi = band_hi(w_rows_last + shift, L, a.window_right);
   const int wk_lo = band_lo(rw + shift, a.window_left);
 
-  // ---- Q operand (B of the score product): lane holds Q[row][16kk + 8*half .. +8].
+  // ---- Q operand (B of the score product): lane holds Q[row][KW kk + 8 half .. +8].
   // A negative scale is folded into Q's sign (exact), a zero scale into a
   // zero Q, so that the exp2-domain factor c2 is positive.
   float c2 = a.softmax_scale * kLog2e;
@@ -222,7 +275,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     const bf16_t *qrow = (const bf16_t *)a.q + ((size_t)(q0 + (row_valid ? my_row : 0)) * a.hq + head) * D;
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
-      u32x4_t v = *(const u32x4_t *)(qrow + 16 * kk + 8 * half);
+      u32x4_t v = *(const u32x4_t *)(qrow + KW * kk + 8 * half);
       v ^= qxor;
       if (qzero) v = u32x4_t{};
       qop[kk] = __builtin_bit_cast(bf16x8_t, v);
@@ -258,7 +311,8 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     // [dim/(32 NK)][token][run (4)][half (NK)][8], NK 2 for e4m3, else 1
     constexpr int NK = FP8 ? 2 : 1;
     const int kslot = w % P, e8 = (w / P) & 3, blk = w / (4 * P);
-    kg[i] = (uint32_t)((((blk / NK) * P + perm_key(kslot)) * 32 * NK + e8 * NK * 8 + (blk % NK) * 8) * C::ESZ);
+    const int ksrc = RW == 32 ? perm_key(kslot) : kslot;
+    kg[i] = (uint32_t)((((blk / NK) * P + ksrc) * 32 * NK + e8 * NK * 8 + (blk % NK) * 8) * C::ESZ);
     kl[i] = (uint32_t)((pit[i] * P + kslot) * C::KROW + (blk * 32 + e8 * 8) * 2);
     // V: the page block is 16-token blocks of 16-byte runs in MFMA operand
     // order; a chunk (8 elements) is 4 tokens of 2 dims 16 apart: run
@@ -270,7 +324,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     const int dim0 = 16 * (cg * NV + jq) + l;              // and dim0 + 16
     vg[i] = (uint32_t)(e0 * C::ESZ);
     vkey[i] = (uint32_t)(pit[i] * P + 16 * sb + 4 * gq);
-    vl[i] = (uint32_t)(dim0 * C::VROW + vkey[i] * 2);
+    vl[i] = (uint32_t)(dim0 * C::VROW + v_column<RW>(vkey[i]) * 2);
   }
 
   Raw kst[PER], vst[PER];
@@ -291,7 +345,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
 #pragma unroll
     for (int i = 0; i < PER; ++i) dst[i] = *(const Raw *)(kb + pgk[i] * page_bytes + kg[i]);
     if (FP8 && tid < BN) {
-      const int key = tile * BN + 32 * (tid >> 5) + perm_key(tid & 31);
+      const int key = tile * BN + (RW == 32 ? 32 * (tid >> 5) + perm_key(tid & 31) : tid);
       const int page = pt[min(key / P, last_page)];
       dss = a.cache.k_scales[((size_t)page * hkv + g) * P + key % P];
     }
@@ -345,16 +399,17 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
 
   // ---- MFMA operand bases: per-lane base plus immediates
   const uint8_t *klane = lds + qcol * C::KROW + 16 * half;
-  const uint8_t *vlane = lds + C::V_OFF + (dh * DT * 32 + qcol) * C::VROW + 16 * half;
+  const uint8_t *vlane = lds + C::V_OFF + (dh * DT * RW + qcol) * C::VROW + 16 * half;
 
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16_t o[DT];
+  Acc o[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
-  f32x16_t sc[2];          // scores S^T of the next tile (two 32-key subtiles)
-  uint32_t pk[16];         // probabilities of the current tile, bf16 pairs
+  for (int dt = 0; dt < DT; ++dt) o[dt] = Acc{};
+  Acc sc[NSB];             // scores S^T of the next tile (NSB subtiles of RW keys)
+  constexpr int NPK = NSB * NA / 2;
+  uint32_t pk[NPK];        // probabilities of the current tile, bf16 pairs
 #pragma unroll
-  for (int j = 0; j < 16; ++j) pk[j] = 0u;
+  for (int j = 0; j < NPK; ++j) pk[j] = 0u;
 
   auto active = [&](int t) {
     const int b = phys(t) * BN;
@@ -369,9 +424,10 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   auto mfma_step = [&](int t) {
     const uint8_t *kt = klane + ((t + 1) & 1) * C::KBUF;
     const uint8_t *vt = vlane + (t & 1) * C::VBUF;
-    auto kop = [&](int i) { return *(const bf16x8_t *)(kt + (i / KD) * 32 * C::KROW + 32 * (i % KD)); };
-    auto vop = [&](int i) { return *(const bf16x8_t *)(vt + (i % DT) * 32 * C::VROW + 32 * (i / DT)); };
-    constexpr int NS = 2 * KD, NP = 4 * DT, AH = D == 256 ? NK_PREFILL_LDS_AHEAD_D256 : NK_PREFILL_LDS_AHEAD;
+    auto kop = [&](int i) { return *(const bf16x8_t *)(kt + (i / KD) * RW * C::KROW + 2 * KW * (i % KD)); };
+    auto vop = [&](int i) { return *(const bf16x8_t *)(vt + (i % DT) * RW * C::VROW + 2 * KW * (i / DT)); };
+    constexpr int NS = NSB * KD, NP = (BN / KW) * DT;
+    constexpr int AH = D == 256 && RW == 32 ? NK_PREFILL_LDS_AHEAD_D256 : NK_PREFILL_LDS_AHEAD;
     bf16x8_t ring[AH];
 #pragma unroll
     for (int i = 0; i < AH; ++i) ring[i] = i < NS ? kop(i) : vop(i - NS);
@@ -381,11 +437,14 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
       if (i + AH < NS + NP) ring[i % AH] = i + AH < NS ? kop(i + AH) : vop(i + AH - NS);
       if (i < NS) {
         const int st = i / KD, kk = i % KD;
-        sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, qop[kk], kk == 0 ? f32x16_t{} : sc[st], 0, 0, 0);
+        sc[st] = mma(opnd, qop[kk], kk == 0 ? Acc{} : sc[st]);
       } else {
-        const int c = (i - NS) / DT, dt = (i - NS) % DT, b = 8 * (c >> 1) + 4 * (c & 1);
+        // k-step c of P^T: 32-row waves take the pairs 8(c/2) + 4(c%2) ..
+        // (the permuted K rows), 16-row waves the pairs 4c .. (entries 0..3
+        // of subtiles 2c and 2c + 1, matching the permuted V^T columns)
+        const int c = (i - NS) / DT, dt = (i - NS) % DT, b = RW == 32 ? 8 * (c >> 1) + 4 * (c & 1) : 4 * c;
         const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[b], pk[b + 1], pk[b + 2], pk[b + 3]});
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, pop, o[dt], 0, 0, 0);
+        o[dt] = mma(opnd, pop, o[dt]);
       }
     }
 #pragma unroll
@@ -400,24 +459,27 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   };
 
   // V(t): softmax of S(t+1) into P(t+1), with the running maximum and sum
-  // (element v of subtile st holds key 32st + 16(v>>3) + 8half + (v&7) of
-  // the tile) -- VALU work only.  S is dead afterwards and is overwritten in
-  // place.
+  // -- VALU work only.  Entry v of subtile st holds key
+  // 32st + 16(v>>3) + 8half + (v&7) of the tile (32-row waves: C row
+  // 8(v>>2) + 4half + (v&3), through the K row permutation) or
+  // 16st + 4half + v (16-row waves: C row 4half + v, K rows in key order).
+  // S is dead afterwards and is overwritten in place.
   auto softmax_step = [&](int t) {
     const int tn = t + 1;
     if (tn > t1 || !active(tn)) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pk[j] = 0u;
+      for (int j = 0; j < NPK; ++j) pk[j] = 0u;
       return;
     }
     const int tile_base = phys(tn) * BN;
     if constexpr (FP8) {
+      // K scales are stored per LDS row: C rows 4 apart, 4 at a time
       const float *ks = (const float *)(lds + C::KS_OFF + (tn & 1) * C::SBUF);
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < NSB; ++st)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4_t k4 = *(const f32x4_t *)(ks + 32 * st + 8 * j + 4 * half);
+        for (int j = 0; j < NA / 4; ++j) {
+          const f32x4_t k4 = *(const f32x4_t *)(ks + RW * st + 8 * j + 4 * half);
 #pragma unroll
           for (int r = 0; r < 4; ++r) sc[st][4 * j + r] *= k4[r];
         }
@@ -425,21 +487,22 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     const bool mask = tile_base + BN - 1 > band_hi(rw + shift, L, a.window_right) ||
                       (a.window_left >= 0 && tile_base < band_lo(w_rows_last + shift, a.window_left));
     if (mask) {
-      const int rel_hi = row_valid ? my_hi - tile_base - 8 * half : -1000000;
-      const int rel_lo = my_lo - tile_base - 8 * half;
-      const int rel_sink = a.sink_keys - tile_base - 8 * half;    // keys below it are sinks
+      constexpr int KOFF = RW == 32 ? 8 : 4;                      // key offset per lane group
+      const int rel_hi = row_valid ? my_hi - tile_base - KOFF * half : -1000000;
+      const int rel_lo = my_lo - tile_base - KOFF * half;
+      const int rel_sink = a.sink_keys - tile_base - KOFF * half;    // keys below it are sinks
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < NSB; ++st)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kv = 32 * st + 16 * (v >> 3) + (v & 7);
+        for (int v = 0; v < NA; ++v) {
+          const int kv = RW == 32 ? 32 * st + 16 * (v >> 3) + (v & 7) : 16 * st + v;
           if (kv > rel_hi || (kv < rel_lo && (!SINKS || kv >= rel_sink))) sc[st][v] = -INFINITY;
         }
     }
     float tmax = sc[0][0];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) tmax = fmaxf(tmax, sc[i >> 4][i & 15]);
-    tmax = halves_max(tmax);
+    for (int i = 1; i < NSB * NA; ++i) tmax = fmaxf(tmax, sc[i / NA][i % NA]);
+    tmax = RW == 32 ? halves_max(tmax) : quarters_max(tmax);
     const float tm = tmax * c2;
     const bool grow = tm > m_run + 8.f;
     if (__any(grow)) {
@@ -453,8 +516,8 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     const float nm = m_run == -INFINITY ? 0.f : -m_run;
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int st = j >> 3, v = 2 * (j & 7);
+    for (int j = 0; j < NPK; ++j) {
+      const int st = 2 * j / NA, v = 2 * j % NA;
       pk[j] = pack_bf16(fast_exp2(fmaf(sc[st][v], c2, nm)), fast_exp2(fmaf(sc[st][v + 1], c2, nm)));
       if (j & 1) l1 = dot2_ones(pk[j], l1); else l0 = dot2_ones(pk[j], l0);
     }
@@ -506,12 +569,11 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   {
     const uint8_t *kt = klane + (t0 & 1) * C::KBUF;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      sc[st] = f32x16_t{};
+    for (int st = 0; st < NSB; ++st) {
+      sc[st] = Acc{};
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk)
-        sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t *)(kt + st * 32 * C::KROW + 32 * kk),
-                                                         qop[kk], sc[st], 0, 0, 0);
+        sc[st] = mma(*(const bf16x8_t *)(kt + st * RW * C::KROW + 2 * KW * kk), qop[kk], sc[st]);
     }
   }
   __syncthreads();
@@ -527,19 +589,19 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   }
 
   if (!wave_active) return;
-  l_run = halves_sum(l_run);
+  l_run = RW == 32 ? halves_sum(l_run) : quarters_sum(l_run);
   if (!row_valid) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   bf16_t *orow = (bf16_t *)a.out + ((size_t)(q0 + my_row) * a.hq + head) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // values v = 4j..4j+3 are dims 32dt + 8j + 4*half + 0..3
+    for (int j = 0; j < NA / 4; ++j) {
+      // values v = 4j..4j+3 are dims RW dt + 8j + 4 half + 0..3
       bf16x4_t ov;
 #pragma unroll
       for (int r = 0; r < 4; ++r) ov[r] = (bf16_t)(o[dt][4 * j + r] * inv);
-      *(bf16x4_t *)(orow + 32 * (dh * DT + dt) + 8 * j + 4 * half) = ov;
+      *(bf16x4_t *)(orow + RW * (dh * DT + dt) + 8 * j + 4 * half) = ov;
     }
   if (a.lse && half == 0 && dh == 0)
     a.lse[(size_t)(q0 + my_row) * a.hq + head] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
@@ -685,7 +747,7 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
 // one queue share that XCD's L2); a unit is (item, head block).  An item
 // record carries its segment's row offset, row count and key count, so a
 // unit starts after one read.
-template <int D, int P, bool FP8, int NW, bool SINKS>
+template <int D, int P, bool FP8, int NW, int RW, bool SINKS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 1 : 2)))
 attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -706,7 +768,7 @@ attn_prefill_kernel(AttnArgs a, int GW, int NQ) {
     if (threadIdx.x == 0) next = atomicAdd(ctr, 1);   // in flight while the item runs
     const int4 rec = items[2 * (u / NHq)];      // {segment, q-block, q0, q_len}
     const int kv = items[2 * (u / NHq) + 1].x;
-    prefill_item<D, P, FP8, NW, SINKS>(a, GW, rec.x, rec.y, rec.z, rec.w, kv, q + NQ * (u % NHq), lds);
+    prefill_item<D, P, FP8, NW, RW, SINKS>(a, GW, rec.x, rec.y, rec.z, rec.w, kv, q + NQ * (u % NHq), lds);
     if (threadIdx.x == 0) unit_slot = next;
     __syncthreads();
     u = unit_slot;
@@ -721,18 +783,20 @@ DeviceShape &device_shape(int dev) {
 
 template <int D, int P, bool FP8, bool SINKS>
 hipError_t launch_cfg(const AttnArgs &a, hipStream_t stream) {
-  constexpr int DH = D == 256 ? NK_PREFILL_D256_SPLIT : 1;
-  constexpr int NW = D == 256 ? 4 * DH : NK_PREFILL_NW;
+  constexpr int RW = D == 256 ? NK_PREFILL_D256_RW : NK_PREFILL_RW;
+  constexpr int DH = out_split<D, RW>();
+  constexpr int NW = D == 256 && RW == 32 ? 4 * DH : NK_PREFILL_NW;
   using C = Cfg<D, P, FP8, NW>;
   const int hkv = a.cache.num_kv_heads;
   const int G = a.hq / hkv;
   int GW = 1;                                  // heads per work-group: power of 2 dividing G
   while (GW * 2 * DH <= NW && G % (GW * 2) == 0) GW *= 2;
-  const int BM = 32 * (NW / (GW * DH));
+  const int BM = RW * (NW / (GW * DH));
+  static_assert(RW >= kMinPrefillBlock, "the work list is sized for q-blocks of kMinPrefillBlock rows or more");
   const int NH = hkv * (G / GW);
   const int NQ = NH % kSchedQueues == 0 ? kSchedQueues : 1;
   if (!a.sched) return hipErrorInvalidValue;
-  auto kern = attn_prefill_kernel<D, P, FP8, NW, SINKS>;
+  auto kern = attn_prefill_kernel<D, P, FP8, NW, RW, SINKS>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;

@@ -61,8 +61,14 @@ constexpr int kSchedItemInts = 8;             // {s, q-block, q0, q_len, kv_len,
 __host__ __device__ inline size_t sched_items_offset(int num_seqs) {                  // 32-byte items
   return ((size_t)kSchedSegOff + num_seqs + 1 + 63) / 64 * 64;
 }
-// q-blocks of a prefill batch: at most one per 32 rows plus one per segment
-__host__ __device__ inline int sched_items_max(int num_seqs, int total_q) { return total_q / 32 + num_seqs + 1; }
+// Smallest q-block of the prefill kernels (rows): 16-row waves, one row
+// block per work-group
+constexpr int kMinPrefillBlock = 16;
+// q-blocks of a prefill batch: at most one per kMinPrefillBlock rows plus one
+// per segment
+__host__ __device__ inline int sched_items_max(int num_seqs, int total_q) {
+  return total_q / kMinPrefillBlock + num_seqs + 1;
+}
 __host__ __device__ inline size_t sched_bytes(int num_seqs, int total_q) {
   return (sched_items_offset(num_seqs) + (size_t)kSchedItemInts * sched_items_max(num_seqs, total_q)) * 4;
 }

@@ -50,6 +50,9 @@ CASES = {
                                  head_dim=256),
     "prefill_d256_g8_fp8": dict(q_lens=[70, 5], kv_lens=[100, 5], num_q_heads=16, num_kv_heads=2,
                                 head_dim=256, page_size=32, cache_dtype="e4m3"),
+    # 8 query heads per work-group at head_dim 256: 16-row q-blocks, each segment ending in a partial one
+    "prefill_d256_g8_ragged": dict(q_lens=[70, 5, 33, 16], kv_lens=[100, 5, 33, 80], num_q_heads=16,
+                                   num_kv_heads=2, head_dim=256, page_size=32),
     # the largest query-head group a KV head may have (64): 4 blocks of 16 decode columns, 8 prefill heads
     # per work-group
     "max_group_g64_d128": dict(q_lens=[1, 40, 1], kv_lens=[700, 40, 33], num_q_heads=64, num_kv_heads=1,
