@@ -85,7 +85,10 @@
 #define NK_PREFILL_D256_RW 16
 #endif
 // LDS operand reads in flight ahead of the MFMA that consumes them (head
-// dims up to 128; 256 has no registers to spare)
+// dims up to 128; 256: measured, fewer reads in flight are faster there)
+#ifndef NK_PREFILL_VPAIR
+#define NK_PREFILL_VPAIR 1
+#endif
 #ifndef NK_PREFILL_LDS_AHEAD
 #define NK_PREFILL_LDS_AHEAD 4
 #endif
@@ -123,6 +126,10 @@ struct Cfg {
   static constexpr int PAGE_CH = D * P / 8;            // 8-element chunks per page block
   static constexpr int PER = BN * D / 8 / NT;          // chunks per thread per tile (K or V)
   static constexpr int NPG = BN / P;                   // pages per tile
+  // a 16-token block of one head's V is 16 D elements = 2 D chunks of 8:
+  // when that is one chunk per thread, a thread's chunks i and i + 1 (even i)
+  // cover the same dims for tokens 16 apart
+  static constexpr bool V_PAIRS = NK_PREFILL_VPAIR && 2 * D == NT && PER % 2 == 0;
   static_assert(PAGE_CH % 64 == 0, "a wave's chunk must lie in one page");
   static_assert((BN * D / 8) % NT == 0, "tile chunks must divide over the threads");
 };
@@ -375,9 +382,8 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   // slots may hold anything, and 0 * NaN is NaN)
   auto store_v = [&](int buf, int vtile) {
     const int base = phys(vtile) * BN;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      // elements 0..3: dim dim0, tokens vkey..+3; 4..7: dim dim0 + 16
+    // chunk i as bf16: elements 0..3 dim dim0, tokens vkey..+3; 4..7 dim dim0 + 16
+    auto chunk = [&](int i) {
       bf16x8_t x;
       if constexpr (FP8) {
         const bf16x8_t c = fp8x8_to_bf16x8(vst[i]);
@@ -391,9 +397,26 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
         for (int e = 0; e < 8; ++e)
           if (base + (int)vkey[i] + (e & 3) >= L) x[e] = (bf16_t)0.f;
       }
-      uint8_t *dst = lds + C::V_OFF + buf * C::VBUF + vl[i];
-      *(bf16x4_t *)dst = bf16x4_t{x[0], x[1], x[2], x[3]};
-      *(bf16x4_t *)(dst + 16 * C::VROW) = bf16x4_t{x[4], x[5], x[6], x[7]};
+      return x;
+    };
+    if constexpr (C::V_PAIRS && RW == 16) {
+      // chunks i and i + 1 hold the same dims for tokens 16 apart, which the
+      // 16-row column order places side by side: one 16-byte store per dim
+#pragma unroll
+      for (int i = 0; i < PER; i += 2) {
+        const bf16x8_t x0 = chunk(i), x1 = chunk(i + 1);
+        uint8_t *dst = lds + C::V_OFF + buf * C::VBUF + vl[i];
+        *(bf16x8_t *)dst = bf16x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        *(bf16x8_t *)(dst + 16 * C::VROW) = bf16x8_t{x0[4], x0[5], x0[6], x0[7], x1[4], x1[5], x1[6], x1[7]};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const bf16x8_t x = chunk(i);
+        uint8_t *dst = lds + C::V_OFF + buf * C::VBUF + vl[i];
+        *(bf16x4_t *)dst = bf16x4_t{x[0], x[1], x[2], x[3]};
+        *(bf16x4_t *)(dst + 16 * C::VROW) = bf16x4_t{x[4], x[5], x[6], x[7]};
+      }
     }
   };
 
@@ -427,7 +450,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     auto kop = [&](int i) { return *(const bf16x8_t *)(kt + (i / KD) * RW * C::KROW + 2 * KW * (i % KD)); };
     auto vop = [&](int i) { return *(const bf16x8_t *)(vt + (i % DT) * RW * C::VROW + 2 * KW * (i / DT)); };
     constexpr int NS = NSB * KD, NP = (BN / KW) * DT;
-    constexpr int AH = D == 256 && RW == 32 ? NK_PREFILL_LDS_AHEAD_D256 : NK_PREFILL_LDS_AHEAD;
+    constexpr int AH = D == 256 ? NK_PREFILL_LDS_AHEAD_D256 : NK_PREFILL_LDS_AHEAD;
     bf16x8_t ring[AH];
 #pragma unroll
     for (int i = 0; i < AH; ++i) ring[i] = i < NS ? kop(i) : vop(i - NS);

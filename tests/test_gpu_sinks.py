@@ -32,6 +32,9 @@ CASES = {
                                                  num_kv_heads=2, head_dim=256, page_size=32,
                                                  rope_layout="interleaved", rotary_dim=128, window_left=20,
                                                  window_right=9, sink_keys=8),
+    # e4m3 at head_dim 256 (16-row waves, 4 heads per work-group), page 16
+    "sinks4_window40_e4m3_d256_g4": dict(**RAGGED, num_q_heads=8, num_kv_heads=2, head_dim=256,
+                                         cache_dtype="e4m3", window_left=40, sink_keys=4),
     "sinks4_window64_gqa16_d64_p32": dict(q_lens=[1, 1, 200], kv_lens=[1000, 33, 260], num_q_heads=16,
                                           num_kv_heads=1, head_dim=64, page_size=32, window_left=64,
                                           sink_keys=4),
