@@ -53,17 +53,6 @@
 #include "common.h"
 #include "internal.h"
 
-// Scheduling hint for the block that interleaves the next tile's score MFMAs
-// with the exponentials (compile-time choice, measured).
-#ifndef NK_PREFILL_IGLP
-#define NK_PREFILL_IGLP -1
-#endif
-#if NK_PREFILL_IGLP >= 0
-#define NK_PREFILL_SCHED_HINT() __builtin_amdgcn_iglp_opt(NK_PREFILL_IGLP)
-#else
-#define NK_PREFILL_SCHED_HINT() ((void)0)
-#endif
-
 // Waves per work-group for head dims up to 128 (compile-time, measured):
 // 8 = one work-group per CU, 4 = two work-groups per CU whose barriers are
 // independent.
