@@ -405,8 +405,9 @@ int nk_attention_pack(const void *k, const void *v, int32_t in_dtype, const int3
  * float32 accumulation); there, with two or more query heads per KV head,
  * the dk/dv rows are zeroed and then summed over head groups with float
  * atomic adds, so their last bits can differ from call to call.  Other cases
- * run in float32 throughout and are deterministic.  Up to three kernels on
- * `stream`, no workspace, no allocation.  Errors as
+ * run in float32 throughout and are deterministic.  Up to four kernels on
+ * `stream` (the MFMA path first stores dO.O per row and head in dq, which it
+ * then overwrites with the gradient), no workspace, no allocation.  Errors as
  * nk_ragged_paged_attention_band.
  */
 int nk_ragged_paged_attention_backward(const void *q, int32_t q_dtype, const int32_t *q_offsets,

@@ -443,11 +443,14 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
   // buffered, so one barrier per pair separates a buffer's writes from its
   // reads (a buffer is rewritten two pairs later, after the next barrier)
   // the loads of pair pr + 1 are in flight while pair pr is computed
-  struct Regs { bf16x8_t q[B::PER], d[B::PER], o[B::PER]; float lse[B::PER]; };
+  // dO.O of each (row, head) comes precomputed in the dq buffer (rows x
+  // heads floats), which the dQ kernel overwrites only after this kernel
+  const float *rowdot = a.dq;
+  struct Regs { bf16x8_t q[B::PER], d[B::PER]; float lse[B::PER], di[B::PER]; };
   Regs R0;
   auto fetch = [&](int pr, Regs &R) {
-    bf16x8_t *gq = R.q, *gd = R.d, *go = R.o;
-    float *glse = R.lse;
+    bf16x8_t *gq = R.q, *gd = R.d;
+    float *glse = R.lse, *gdi = R.di;
     const int r0 = (rt0 + pr / Gc) * 32, head = g * G + hc * Gc + pr % Gc;
 #pragma unroll
     for (int i = 0; i < B::PER; ++i) {
@@ -457,13 +460,13 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
       const size_t rh = (size_t)(q0 + row) * a.hq + head;
       gq[i] = *(const bf16x8_t *)((const bf16_t *)a.q + rh * D + d0);
       gd[i] = *(const bf16x8_t *)((const bf16_t *)a.dout + rh * D + d0);
-      go[i] = *(const bf16x8_t *)((const bf16_t *)a.out + rh * D + d0);
       glse[i] = a.lse[rh];
+      gdi[i] = rowdot[rh];
     }
   };
   auto stage = [&](int pr, uint8_t *buf, const Regs &R) {
-    const bf16x8_t *gq = R.q, *gd = R.d, *go = R.o;
-    const float *glse = R.lse;
+    const bf16x8_t *gq = R.q, *gd = R.d;
+    const float *glse = R.lse, *gdi = R.di;
     const int r0 = (rt0 + pr / Gc) * 32;
 #pragma unroll
     for (int i = 0; i < B::PER; ++i) {
@@ -472,14 +475,8 @@ __global__ void __launch_bounds__(256) attn_dkv_mfma_kernel(BackwardArgs a, int 
       const int row = r0 + r;
       *(bf16x8_t *)(buf + LY::Q + r * B::RM + 2 * d0) = gq[i];
       *(bf16x8_t *)(buf + LY::DO + r * B::RM + 2 * d0) = gd[i];
-      float di = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) di = fmaf((float)gd[i][e], (float)go[i][e], di);
-      // the D/8 chunks of a row sit in consecutive threads
-#pragma unroll
-      for (int m = 1; m < D / 8; m <<= 1) di += shfl_xor_f32(di, m);
       if (c % (D / 8) == 0) {
-        ((float *)(buf + LY::DI))[r] = di;
+        ((float *)(buf + LY::DI))[r] = gdi[i];
         // log2-domain lse; rows past the segment get +inf (P = 0)
         ((float *)(buf + LY::LSE))[r] = row < q_len ? glse[i] * kLog2e : INFINITY;
       }
@@ -806,6 +803,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   }
 }
 
+// dO.O of every (row, query head), as float32, into the first total_q x hq
+// floats of the dq buffer, for the dK/dV kernel (the dQ kernel, launched
+// after it, computes its own and overwrites the buffer): D/8 consecutive
+// lanes per (row, head), 16-byte loads, a lane-group sum.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_rowdot_kernel(BackwardArgs a) {
+  constexpr int LG = D / 8;                       // lanes per (row, head)
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long rh = t / LG;
+  const bool live = rh < (long long)a.total_q * a.hq;
+  const int j = (int)(t % LG);
+  float x = 0.f;
+  if (live) {
+    const bf16x8_t d = *(const bf16x8_t *)((const bf16_t *)a.dout + rh * D + 8 * j);
+    const bf16x8_t o = *(const bf16x8_t *)((const bf16_t *)a.out + rh * D + 8 * j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x = fmaf((float)d[e], (float)o[e], x);
+  }
+#pragma unroll
+  for (int m = 1; m < LG; m <<= 1) x += shfl_xor_f32(x, m);
+  if (live && j == 0) a.dq[rh] = x;
+}
+
 // Zeros of the dK/dV rows of every segment's keys (rows key_offsets[s] ..
 // key_offsets[s] + kv_lens[s] - 1), before work-groups add into them: one
 // work-group per (segment, 16 keys).
@@ -829,13 +849,22 @@ hipError_t launch_mfma(const BackwardArgs &a, int max_q_len, hipStream_t stream)
   while (GW * 2 <= 4 && G % (GW * 2) == 0) GW *= 2;
   const int rows_per_block = 32 * (4 / GW);
   hipError_t e = hipSuccess;
-  if (a.total_q > 0 && max_q_len > 0) {
+  // dQ last: the dK/dV kernel reads dO.O from the dq buffer
+  auto launch_dq = [&]() -> hipError_t {
+    if (a.total_q <= 0 || max_q_len <= 0) return hipSuccess;
     const int per_seq = (max_q_len + rows_per_block - 1) / rows_per_block;
     const long long blocks = (long long)a.num_seqs * per_seq * hkv * (G / GW);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    e = launch(attn_dq_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, a, per_seq, GW);
+    return launch(attn_dq_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, a, per_seq, GW);
+  };
+  if (a.max_kv_len == 0 || a.total_q <= 0) return launch_dq();
+  {
+    const long long threads = (long long)a.total_q * a.hq * (D / 8);
+    const long long rblocks = (threads + 255) / 256;
+    if (rblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    e = launch(bwd_rowdot_kernel<D>, dim3((unsigned)rblocks), dim3(256), 0, stream, a);
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess || a.max_kv_len == 0) return e;
   // query heads of a KV head split over HC work-groups (a power of two
   // dividing G, at most 4): shorter work-groups, added into zeroed outputs
   int HC = 1;
@@ -860,7 +889,9 @@ hipError_t launch_mfma(const BackwardArgs &a, int max_q_len, hipStream_t stream)
     if (e != hipSuccess) return e;
     attr_set[dev & 63] = true;
   }
-  return launch(attn_dkv_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), DkvLds<D>::TOTAL, stream, a, per_seq, HC);
+  e = launch(attn_dkv_mfma_kernel<D>, dim3((unsigned)blocks), dim3(256), DkvLds<D>::TOTAL, stream, a, per_seq, HC);
+  if (e != hipSuccess) return e;
+  return launch_dq();
 }
 
 template <typename T>
