@@ -84,6 +84,13 @@
 #ifndef NK_PREFILL_LDS_AHEAD_D256
 #define NK_PREFILL_LDS_AHEAD_D256 2
 #endif
+// Page ids of the K tile a load step requests are read one load step
+// earlier (1), so that its global loads do not wait for scalar loads
+// (head_dim 256: 2 % faster on the sliding-window batch; at 128 within
+// noise, so left off there)
+#ifndef NK_PREFILL_EARLY_IDS
+#define NK_PREFILL_EARLY_IDS 1
+#endif
 
 namespace nk {
 namespace {
@@ -332,12 +339,26 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   // pages of the K tile last requested: the V tile requested one step later
   // is the same tile
   size_t pgk[PER];
-  // K of `tile` into the given staging registers
-  auto load_k_to = [&](int vtile, Raw (&dst)[PER], float &dss) {
+  constexpr bool EARLY_IDS = NK_PREFILL_EARLY_IDS && D == 256;
+  // page ids read ahead for the next load_k (EARLY_IDS)
+  int pid_next[PER];
+  auto fetch_ids = [&](int vtile) {
     const int tile = phys(vtile);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) pgk[i] = page_of(tile, pit[i]);
-    __builtin_amdgcn_sched_barrier(0);     // all page lookups in flight together
+    for (int i = 0; i < PER; ++i) pid_next[i] = ptc[min(tile * NPG + pit[i], last_page)];
+  };
+  // K of `tile` into the given staging registers; `early`: its page ids are
+  // the ones fetch_ids read
+  auto load_k_to = [&](int vtile, Raw (&dst)[PER], float &dss, bool early) {
+    const int tile = phys(vtile);
+    if (early) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) pgk[i] = (size_t)(uint32_t)pid_next[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) pgk[i] = page_of(tile, pit[i]);
+      __builtin_amdgcn_sched_barrier(0);     // all page lookups in flight together
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) dst[i] = *(const Raw *)(kb + pgk[i] * page_bytes + kg[i]);
     if (FP8 && tid < BN) {
@@ -346,7 +367,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
       dss = a.cache.k_scales[((size_t)page * hkv + g) * P + key % P];
     }
   };
-  auto load_k = [&](int tile) { load_k_to(tile, kst, kss); };
+  auto load_k = [&](int tile) { load_k_to(tile, kst, kss, false); };
   // V of `tile` through the given pages
   auto load_v = [&](const size_t (&pg)[PER]) {
 #pragma unroll
@@ -503,13 +524,24 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
       const int rel_hi = row_valid ? my_hi - tile_base - KOFF * half : -1000000;
       const int rel_lo = my_lo - tile_base - KOFF * half;
       const int rel_sink = a.sink_keys - tile_base - KOFF * half;    // keys below it are sinks
+      if (!SINKS && a.window_left < 0) {
+        // no left bound (plain causal): one compare per entry
 #pragma unroll
-      for (int st = 0; st < NSB; ++st)
+        for (int st = 0; st < NSB; ++st)
 #pragma unroll
-        for (int v = 0; v < NA; ++v) {
-          const int kv = RW == 32 ? 32 * st + 16 * (v >> 3) + (v & 7) : 16 * st + v;
-          if (kv > rel_hi || (kv < rel_lo && (!SINKS || kv >= rel_sink))) sc[st][v] = -INFINITY;
-        }
+          for (int v = 0; v < NA; ++v) {
+            const int kv = RW == 32 ? 32 * st + 16 * (v >> 3) + (v & 7) : 16 * st + v;
+            if (kv > rel_hi) sc[st][v] = -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < NSB; ++st)
+#pragma unroll
+          for (int v = 0; v < NA; ++v) {
+            const int kv = RW == 32 ? 32 * st + 16 * (v >> 3) + (v & 7) : 16 * st + v;
+            if (kv > rel_hi || (kv < rel_lo && (!SINKS || kv >= rel_sink))) sc[st][v] = -INFINITY;
+          }
+      }
     }
     float tmax = sc[0][0];
 #pragma unroll
@@ -544,7 +576,12 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
     size_t pgv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) pgv[i] = pgk[i];
-    if (t + 3 <= t1) load_k(t + 3);
+    if (EARLY_IDS) {
+      if (t + 3 <= t1) load_k_to(t + 3, kst, kss, true);
+      if (t + 4 <= t1) fetch_ids(t + 4);
+    } else {
+      if (t + 3 <= t1) load_k(t + 3);
+    }
     if (t + 2 <= t1) load_v(pgv);
   };
 
@@ -553,12 +590,14 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
   {
     Raw k0[PER];
     float ks0 = 0.f;
-    load_k_to(t0, k0, ks0);
+    load_k_to(t0, k0, ks0, false);
     size_t pgv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) pgv[i] = pgk[i];
     if (t0 + 1 <= t1) load_k(t0 + 1);
     load_v(pgv);
+    // the first load step requests K(t0 + 2)
+    if (EARLY_IDS && t0 + 2 <= t1) fetch_ids(t0 + 2);
     store_k_from(t0 & 1, k0, ks0);
   }
   __syncthreads();
@@ -621,10 +660,7 @@ NK_DEVICE void prefill_item(const AttnArgs &a, int GW, int s, int qb, int q0, in
 
 // Key tiles a work item visits (0 when none of its rows sees a key); the
 // same bounds as prefill_item.
-NK_DEVICE int item_tiles(const AttnArgs &a, int BM, int s, int qb) {
-  const int q0 = a.q_offsets[s];
-  const int q_len = a.q_offsets[s + 1] - q0;
-  const int L = a.kv_lens[s];
+NK_DEVICE int item_tiles(const AttnArgs &a, int BM, int q_len, int L, int qb) {
   const int shift = L - q_len;
   const int r0 = qb * BM;
   const int r_last = min(r0 + BM, q_len) - 1;
@@ -679,14 +715,24 @@ NK_DEVICE int segment_of_item(const int32_t *segoff, int num_seqs, int i) {
 // counters.  q-blocks whose rows see no key at all (rows placed before a
 // segment's first key, or a segment without keys) sort last; this kernel
 // writes their zeros and -inf itself and leaves them out of the item count
-// the attention kernels read.  One work-group.
+// the attention kernels read.  One work-group.  Batches of up to
+// kPlanLdsSegs segments keep the segments' item offsets, row offsets and
+// key counts in LDS, so the per-item segment search and band bounds make no
+// dependent global reads; larger batches search the offsets in the
+// workspace.
+constexpr int kPlanLdsSegs = 2048;
+
 __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, int BM) {
   __shared__ int hist[kPlanBins];
   __shared__ int part[kPlanThreads / 64];
+  __shared__ int l_segoff[kPlanLdsSegs + 1];
+  __shared__ int l_qoff[kPlanLdsSegs + 1];
+  __shared__ int l_kvl[kPlanLdsSegs];
   int32_t *sc = a.sched;
   int32_t *segoff = sc + kSchedSegOff;
   int4 *items = (int4 *)(sc + sched_items_offset(a.num_seqs));   // two int4 per item
   const int tid = threadIdx.x;
+  const bool small = a.num_seqs <= kPlanLdsSegs;
   for (int i = tid; i < kPlanBins; i += kPlanThreads) hist[i] = 0;
   if (tid < kSchedQueues) sc[tid * kSchedCounterStride] = 0;
 
@@ -695,21 +741,37 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
     const int s = c0 + tid;
     int n = 0;
     if (s < a.num_seqs) {
-      const int q_len = a.q_offsets[s + 1] - a.q_offsets[s];
+      const int q0 = a.q_offsets[s], q1 = a.q_offsets[s + 1];
+      const int q_len = q1 - q0;
       n = q_len > 1 ? (q_len + BM - 1) / BM : 0;
+      if (small) {
+        l_qoff[s] = q0;
+        l_kvl[s] = a.kv_lens[s];
+        if (s == a.num_seqs - 1) l_qoff[s + 1] = q1;
+      }
     }
     int tot;
     const int ex = block_exclusive_scan(n, part, &tot);
-    if (s < a.num_seqs) segoff[s] = base + ex;
+    if (s < a.num_seqs) {
+      segoff[s] = base + ex;
+      if (small) l_segoff[s] = base + ex;
+    }
     base += tot;
   }
   const int n_items = min(base, a.sched_items_max);
-  if (tid == 0) segoff[a.num_seqs] = base;
+  if (tid == 0) {
+    segoff[a.num_seqs] = base;
+    if (small) l_segoff[a.num_seqs] = base;
+  }
   __syncthreads();
+  // generic pointers: LDS copies for small batches, else global memory
+  const int32_t *so = small ? (const int32_t *)l_segoff : (const int32_t *)segoff;
+  const int32_t *qo = small ? (const int32_t *)l_qoff : a.q_offsets;
+  const int32_t *kl = small ? (const int32_t *)l_kvl : a.kv_lens;
 
   for (int i = tid; i < n_items; i += kPlanThreads) {
-    const int s = segment_of_item(segoff, a.num_seqs, i);
-    const int w = item_tiles(a, BM, s, i - segoff[s]);
+    const int s = segment_of_item(so, a.num_seqs, i);
+    const int w = item_tiles(a, BM, qo[s + 1] - qo[s], kl[s], i - so[s]);
     atomicAdd(&hist[kPlanBins - 1 - min(w, kPlanBins - 1)], 1);
   }
   __syncthreads();
@@ -728,13 +790,13 @@ __global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(AttnArgs a, 
   }
   __syncthreads();
   for (int i = tid; i < n_items; i += kPlanThreads) {
-    const int s = segment_of_item(segoff, a.num_seqs, i);
-    const int qb = i - segoff[s];
-    const int w = item_tiles(a, BM, s, qb);
+    const int s = segment_of_item(so, a.num_seqs, i);
+    const int qb = i - so[s];
+    const int q0 = qo[s], q_len = qo[s + 1] - q0, L = kl[s];
+    const int w = item_tiles(a, BM, q_len, L, qb);
     const int pos = atomicAdd(&hist[kPlanBins - 1 - min(w, kPlanBins - 1)], 1);
-    const int q0 = a.q_offsets[s];
-    items[2 * pos] = int4{s, qb, q0, a.q_offsets[s + 1] - q0};
-    items[2 * pos + 1] = int4{a.kv_lens[s], 0, 0, 0};
+    items[2 * pos] = int4{s, qb, q0, q_len};
+    items[2 * pos + 1] = int4{L, 0, 0, 0};
   }
   // the items without keys are the last ones (bin kPlanBins - 1 ends the
   // order); after the loop above hist[kPlanBins - 1] is the end of that bin
