@@ -4,9 +4,10 @@ INFRASTRUCTURE).
 Definitions followed:
 
 * NumKong matrix-kernels page, "Attention with a Pre-Packed KV-Cache" and
-  ``attention_packed``: segments are addressed by cumulative offsets; queries
-  align to the end of their segment's keys, so row r of q query rows over k
-  keys sits at position r + k - q and sees keys from that position minus
+  ``attention_packed``: segment s spans rows offsets[s] .. offsets[s+1]-1 of
+  the batch; queries align to the end of their segment's keys, so row r of q
+  query rows over k keys sits at position r + k - q and sees keys from that
+  position minus
   ``keys_before`` through that position plus ``keys_after``; ``keys_after=0``
   is causal; ``keys_before = w - 1`` is a window of w keys; a row without a
   visible key has an all-zero output; the forward also returns a
