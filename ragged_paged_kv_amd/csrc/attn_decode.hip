@@ -71,6 +71,14 @@
 #define NK_DECODE_NT_FP8 1
 #endif
 
+// e4m3 scales: 1 = the 16 lanes of a row each load the scales of a
+// different 16-key step (one load instruction covers 16 steps) and a step's
+// scales reach the lanes that use them by a DPP row broadcast; 0 = every
+// step loads its own (two load instructions of 64 bytes each per step)
+#ifndef NK_DECODE_SCALE_BCAST
+#define NK_DECODE_SCALE_BCAST 1
+#endif
+
 namespace nk {
 namespace {
 
@@ -155,7 +163,7 @@ NK_DEVICE void load_page(Page<D, FP8> &pg, const nk_paged_kv_t &c, int page, int
 #pragma unroll
   for (int r = 0; r < PG::DT / PG::NV; ++r)
     pg.v[r] = stream_load<FP8 ? NK_DECODE_NT_FP8 : NK_DECODE_NT_BF16>((const u32x4_t *)(vpage + lo.v + 1024 * r));
-  if constexpr (FP8) {
+  if constexpr (FP8 && !NK_DECODE_SCALE_BCAST) {
     const uint8_t *sk = (const uint8_t *)(c.k_scales + ph * P + sb);
     const uint8_t *sv = (const uint8_t *)(c.v_scales + ph * P + sb);
     // the scales of a page's heads share cache lines read by the waves of
@@ -185,6 +193,30 @@ NK_DEVICE float rows_sum(float v) {
   u = __builtin_bit_cast(uint32_t, v);
   r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Lane n of each 16-lane row, broadcast to its row (DPP row_newbcast).
+// With every row and bank enabled each lane takes the broadcast value and
+// `dep` is never selected; it only ties the move to the step whose value it
+// is (otherwise the compiler hoists every step's broadcasts to the start of
+// the unrolled sub-chunk and keeps them all live).
+template <int N>
+NK_DEVICE float row_bcast(float v, float dep) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, dep), __builtin_bit_cast(int, v),
+                                                               0x150 + N, 0xf, 0xf, false));
+}
+// the same for an index that is a constant once the caller is unrolled
+NK_DEVICE float row_bcast_n(float v, int n, float dep) {
+  switch (n & 15) {
+    case 0: return row_bcast<0>(v, dep);   case 1: return row_bcast<1>(v, dep);
+    case 2: return row_bcast<2>(v, dep);   case 3: return row_bcast<3>(v, dep);
+    case 4: return row_bcast<4>(v, dep);   case 5: return row_bcast<5>(v, dep);
+    case 6: return row_bcast<6>(v, dep);   case 7: return row_bcast<7>(v, dep);
+    case 8: return row_bcast<8>(v, dep);   case 9: return row_bcast<9>(v, dep);
+    case 10: return row_bcast<10>(v, dep); case 11: return row_bcast<11>(v, dep);
+    case 12: return row_bcast<12>(v, dep); case 13: return row_bcast<13>(v, dep);
+    case 14: return row_bcast<14>(v, dep); default: return row_bcast<15>(v, dep);
+  }
 }
 
 NK_DEVICE float dot2_ones(bf16x2_t p, float acc) {
@@ -271,13 +303,38 @@ attn_decode_kernel(AttnArgs a) {
     const int page = __builtin_amdgcn_readlane(step_page, j);
     load_page<D, P, FP8>(pg, a.cache, page, SUB == 1 ? 0 : (key0 % P), g, loff);
   };
+  // e4m3 scales of a sub-chunk (NK_DECODE_SCALE_BCAST): for its 16-step
+  // group gi, lane lr + 16 lg holds the K and V scales of keys 4 lg .. 4 lg + 3
+  // of step 16 gi + lr
+  constexpr bool SB = FP8 && NK_DECODE_SCALE_BCAST;
+  constexpr int NG = SB ? CH / 16 : 1;
+  f32x4_t ksg[NG], vsg[NG];
+  auto fetch_scales = [&](int base) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int key0 = cs + 16 * min(base + 16 * gi + n, nsteps - 1);
+      const size_t off = ((size_t)pt[key0 / P] * hkv + g) * P + key0 % P + 4 * lg;
+      ksg[gi] = *(const f32x4_t *)(a.cache.k_scales + off);
+      vsg[gi] = *(const f32x4_t *)(a.cache.v_scales + off);
+    }
+  };
+  // scales of this lane's 4 keys at step jl of the sub-chunk (jl a constant
+  // once the step loop is unrolled)
+  auto k_scale = [&](const PG &pg, int jl, int r, float dep) {
+    if constexpr (SB) return row_bcast_n(ksg[jl / 16][r], jl, dep);
+    else return pg.ks[r];
+  };
+  auto v_scale = [&](const PG &pg, int jl, int r, float dep) {
+    if constexpr (SB) return row_bcast_n(vsg[jl / 16][r], jl, dep);
+    else return pg.vs[r];
+  };
 
   // NS consecutive 16-key steps (pages pg[0..NS-1], steps i..i+NS-1) share
   // one update of the running maximum; the maximum is replaced only when a
   // score exceeds it by more than 2^8 (exact either way: each term is
   // exp2(x - m_used)), and the normaliser sums the probabilities as rounded
   // to bf16 for the P.V product
-  auto consume = [&](const PG *const *pg, int i) {
+  auto consume = [&](const PG *const *pg, int i, int jl) {
     float x[NS][4];
     bool edge = false;
 #pragma unroll
@@ -290,7 +347,8 @@ attn_decode_kernel(AttnArgs a) {
       }
       // lane holds keys kb + 4*lg + r of head column n
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[u][r] = FP8 ? sacc[r] * qk_scale * pg[u]->ks[r] : sacc[r] * qk_scale;
+      for (int r = 0; r < 4; ++r)
+        x[u][r] = FP8 ? sacc[r] * qk_scale * k_scale(*pg[u], jl + u, r, sacc[r]) : sacc[r] * qk_scale;
       edge |= kb < vlo || kb + 16 > ce || i + u >= nsteps;
     }
     if (edge) {
@@ -329,7 +387,7 @@ attn_decode_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) l_run += p[r];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pop[r] = (bf16_t)(p[r] * pg[u]->vs[r]);
+        for (int r = 0; r < 4; ++r) pop[r] = (bf16_t)(p[r] * v_scale(*pg[u], jl + u, r, p[r]));
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) pop[r] = (bf16_t)p[r];
@@ -368,6 +426,7 @@ attn_decode_kernel(AttnArgs a) {
   for (int sub = 0; sub * CH < nsteps; ++sub) {
     const int base = sub * CH;
     fetch_pages(base);
+    if constexpr (SB) fetch_scales(base);       // requested before the pages that need them
     PG ring[NPF];
 #pragma unroll
     for (int j = 0; j < NPF; ++j) issue(ring[j], base + j, j);
@@ -377,7 +436,7 @@ attn_decode_kernel(AttnArgs a) {
         const PG *pgs[NS];
 #pragma unroll
         for (int u = 0; u < NS; ++u) pgs[u] = &ring[(j + u) % NPF];
-        consume(pgs, base + j);
+        consume(pgs, base + j, j);
       }
 #pragma unroll
       for (int u = 0; u < NS; ++u)
