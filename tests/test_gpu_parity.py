@@ -57,6 +57,11 @@ CASES = {
     # per work-group
     "max_group_g64_d128": dict(q_lens=[1, 40, 1], kv_lens=[700, 40, 33], num_q_heads=64, num_kv_heads=1,
                                head_dim=128),
+    # 2100 short prefill segments, some over prior keys: more than the 2048 segments whose offsets the plan
+    # kernel keeps in LDS, so the work list is built from the offsets in global memory
+    "prefill_many_segments_d64": dict(q_lens=[2, 3, 5, 17] * 525,
+                                      kv_lens=[q + (i % 3) * 7 for i, q in enumerate([2, 3, 5, 17] * 525)],
+                                      num_q_heads=4, num_kv_heads=2, head_dim=64),
     # p-RoPE (a quarter of the pairs rotated) under a sliding window, decode rows included
     "proportional_rope_d256_window": dict(q_lens=[90, 1, 1], kv_lens=[90, 700, 40], num_q_heads=8,
                                           num_kv_heads=2, head_dim=256, page_size=32,
