@@ -100,6 +100,18 @@ def test_decode_split_sizes(split):
     _run_and_compare(w, split=split)
 
 
+@pytest.mark.parametrize("split", [96, 512, 1024])
+def test_decode_split_sizes_e4m3(split):
+    """e4m3 decode: chunks of 16-step sub-chunks (split below 512), of one
+    32-step sub-chunk, and of two (split 1024), each sub-chunk with its own
+    scale loads."""
+    w = synth.custom(q_lens=[1] * 5, kv_lens=[1, 100, 777, 2048, 3333], num_q_heads=16, num_kv_heads=4,
+                     head_dim=128, cache_dtype="e4m3", explicit_positions=False, name="split_e4m3")
+    gu.say(f"decode e4m3 split {split}")
+    e1, e2, _, _ = _run_and_compare(w, split=split)
+    gu.record_margin(f"parity decode_e4m3_split{split}", e1, e2, gu.tol_for(w))
+
+
 def test_split_rows_reuse_workspace():
     """One workspace serves several split-KV calls in a row, including a call
     with fewer sequences and then one with the first call's shape again:
