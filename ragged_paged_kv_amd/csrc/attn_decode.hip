@@ -83,7 +83,8 @@
 // first, so that the work-groups of chunks most rows do not have come first
 // and exit at once, and the long rows' last chunks do not wait behind them
 // for a slot (batched decode 52.6 -> 51.9 us; the e4m3 long-context batch,
-// many grids' worth of work-groups, ran 0.3 % slower that way)
+// many grids' worth of work-groups, ran 0.3 % slower that way, and calls
+// with sink keys, whose sink chunk is the last index, 3.7 %)
 #ifndef NK_DECODE_CHUNKS_REVERSED
 #define NK_DECODE_CHUNKS_REVERSED 1
 #endif
@@ -256,7 +257,7 @@ attn_decode_kernel(AttnArgs a) {
   const int g = blockIdx.x % hkv_;
   const int sc = blockIdx.x / hkv_;
   const int s = sc % B;
-  const int c = NK_DECODE_CHUNKS_REVERSED && !FP8 ? a.max_chunks - 1 - sc / B : sc / B;
+  const int c = NK_DECODE_CHUNKS_REVERSED && !FP8 && a.sink_keys == 0 ? a.max_chunks - 1 - sc / B : sc / B;
   const int hb = blockIdx.y;                  // block of 16 query heads
   const int lane = threadIdx.x;
   const int hkv = a.cache.num_kv_heads;
